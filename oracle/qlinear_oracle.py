@@ -1,0 +1,238 @@
+"""Plain, slow, obviously-correct CPU oracle for group-wise affine quantized linear.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py``; never by the library, and it imports
+nothing from the library.
+
+What it computes (sources are the pages' titles and sections):
+
+* Format. Each run of 64 consecutive weights along K in one output row shares
+  one f16 scale and one f16 bias; this overhead is what adds half a bit to each
+  nominal width (Ideogram-4-IQ4_M model card, aimarketly.com, opening section on
+  bits per weight). The grid is uniform affine (same card, section on what
+  "IQ4" means), and the packed Q4/Q8 tensors use group size 64
+  (SceneWorks/ideogram-4-mlx model card, huggingface.co, section "Versions").
+  Dequantized weight: W_hat[n, k] = s[n, g] * q[n, k] + b[n, g], g = k // 64.
+* Fit. Round-to-nearest from the group's min/max ("candidate 0", the card's
+  section on what "IQ4" means; the OrbitQuant W2A4 card's quantization manifest
+  names the same int4 RTN group-64 policy).
+* Packing. The pages say only "packed". Reading taken: codes are stored
+  little-endian along K in uint32 words, 32/bits codes per word, code k in bits
+  [bits*(k % (32/bits)), +bits) of word k // (32/bits).
+* Product. y = x @ W_hat^T, x given as bf16, accumulated in float64.
+
+Readings where the pages are silent (each also listed in the design notes):
+scale = (max - min) / (2**bits - 1) in fp32; both scale and bias rounded to f16
+with round-half-even; q computed from the *stored* f16 scale and bias in fp32
+(IEEE subtract and divide), rounded half-to-even, clamped to [0, 2**bits - 1];
+a group whose f16 scale is zero gets q = 0; non-finite weights, or a scale or
+bias that overflows f16, are rejected.
+
+Every function here is pinned by ``tests/test_oracle.py`` to facts other than
+itself (hand-worked examples, exact rational arithmetic, brute force, closed
+forms, special cases).
+"""
+from __future__ import annotations
+
+import math
+import time
+
+import numpy as np
+
+__all__ = [
+    "GROUP", "SUPPORTED_BITS", "codes_per_word", "bits_per_weight", "storage_bytes",
+    "f16_bits_to_f32", "f32_to_f16_bits", "bf16_bits_to_f64",
+    "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
+    "forward_rows", "error_metrics", "timed_forward",
+]
+
+GROUP = 64
+SUPPORTED_BITS = (2, 4, 8)
+
+
+def codes_per_word(bits: int) -> int:
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"bits must be one of {SUPPORTED_BITS}, got {bits}")
+    return 32 // bits
+
+
+def bits_per_weight(bits: int, group: int = GROUP) -> float:
+    """Nominal width plus one f16 scale and one f16 bias (32 bits) per group.
+
+    Ideogram-4-IQ4_M model card, opening section: the half bit above each
+    nominal width is the group overhead of an f16 scale and an f16 bias per 64.
+    """
+    return bits + 32.0 / group
+
+
+def storage_bytes(bits: int, n: int, k: int, group: int = GROUP) -> int:
+    """Bytes of packed codes + f16 scales + f16 biases for an [n, k] weight."""
+    words = n * k // codes_per_word(bits)
+    groups = n * (k // group)
+    return 4 * words + 2 * groups + 2 * groups
+
+
+# ---------------------------------------------------------------- float helpers
+
+def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """uint16 IEEE half bit patterns -> float32 (exact)."""
+    return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE half, round-half-to-even (NumPy's conversion), as uint16."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def bf16_bits_to_f64(xb: np.ndarray) -> np.ndarray:
+    """uint16 bfloat16 bit patterns -> float64 (exact: bf16 is the top half of fp32)."""
+    u = np.asarray(xb, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- the fit (RTN)
+
+def quantize_rtn(w: np.ndarray, bits: int, group: int = GROUP):
+    """Min/max round-to-nearest per (row, 64-wide K group).
+
+    Returns (q uint8 [N, K], s16 uint16 [N, G], b16 uint16 [N, G]) where s16, b16
+    are f16 bit patterns. Steps, all in fp32 with IEEE rounding:
+      mn, mx  = min, max of the group
+      s       = f16((mx - mn) / Q)        Q = 2**bits - 1
+      b       = f16(mn)
+      q       = clamp(rint_half_even((w - b) / s), 0, Q); q = 0 where s == 0
+    Ideogram-4-IQ4_M card, section on what "IQ4" means (min/max candidate,
+    round-to-nearest); rounding, tie and division rules are this oracle's
+    stated readings.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    if group != GROUP:
+        raise ValueError("only group size 64 is defined by the pages")
+    if k % group != 0:
+        raise ValueError("K must be a multiple of the group size")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    qmax = np.float32(2 ** bits - 1)
+    codes_per_word(bits)  # validates bits
+    g = k // group
+    wg = w.reshape(n, g, group)
+    mn = wg.min(axis=2)
+    mx = wg.max(axis=2)
+    s32 = (mx - mn) / qmax                       # fp32 subtract, fp32 divide
+    s16 = f32_to_f16_bits(s32)
+    b16 = f32_to_f16_bits(mn)
+    s_f = f16_bits_to_f32(s16)
+    b_f = f16_bits_to_f32(b16)
+    if not (np.all(np.isfinite(s_f)) and np.all(np.isfinite(b_f))):
+        raise ValueError("scale or bias overflows f16")
+    zero = s_f == 0
+    safe_s = np.where(zero, np.float32(1), s_f)
+    t = (wg - b_f[:, :, None]) / safe_s[:, :, None]   # fp32 subtract, fp32 divide
+    q = np.rint(t)                                     # half to even
+    q = np.clip(q, 0, qmax)
+    q = np.where(zero[:, :, None], np.float32(0), q)
+    return q.astype(np.uint8).reshape(n, k), s16, b16
+
+
+# ---------------------------------------------------------------- packing
+
+def pack(q: np.ndarray, bits: int) -> np.ndarray:
+    """q uint8 [N, K] (values < 2**bits) -> uint32 [N, K*bits/32].
+
+    Code k sits in bits [bits*(k % c), bits*(k % c) + bits) of word k // c,
+    c = 32 // bits (little-endian along K).
+    """
+    q = np.asarray(q)
+    c = codes_per_word(bits)
+    n, k = q.shape
+    if k % c:
+        raise ValueError("K must be a multiple of codes per word")
+    if q.size and int(q.max()) >= (1 << bits):
+        raise ValueError("code out of range")
+    q32 = q.astype(np.uint32).reshape(n, k // c, c)
+    words = np.zeros((n, k // c), dtype=np.uint32)
+    for j in range(c):
+        words |= q32[:, :, j] << np.uint32(bits * j)
+    return words
+
+
+def unpack(words: np.ndarray, bits: int, k: int) -> np.ndarray:
+    """Inverse of ``pack``: uint32 [N, K*bits/32] -> uint8 [N, K]."""
+    c = codes_per_word(bits)
+    words = np.asarray(words, dtype=np.uint32)
+    n = words.shape[0]
+    if words.shape[1] * c != k:
+        raise ValueError("word count does not match K")
+    mask = np.uint32((1 << bits) - 1)
+    out = np.empty((n, k // c, c), dtype=np.uint8)
+    for j in range(c):
+        out[:, :, j] = ((words >> np.uint32(bits * j)) & mask).astype(np.uint8)
+    return out.reshape(n, k)
+
+
+# ---------------------------------------------------------------- dequantize
+
+def dequantize(q: np.ndarray, s16: np.ndarray, b16: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W_hat = f32(s) * f32(q) + f32(b) in fp32, one group of 64 per (s, b).
+
+    s has at most 11 significant bits and q at most 8, so s*q is exact in fp32
+    and the only rounding is the final add: the result is unique.
+    """
+    q = np.asarray(q)
+    n, k = q.shape
+    g = k // group
+    s = f16_bits_to_f32(s16).reshape(n, g, 1)
+    b = f16_bits_to_f32(b16).reshape(n, g, 1)
+    qf = q.astype(np.float32).reshape(n, g, group)
+    return (s * qf + b).astype(np.float32).reshape(n, k)
+
+
+# ---------------------------------------------------------------- product
+
+def gemm_f64(x_bf16: np.ndarray, w_hat: np.ndarray) -> np.ndarray:
+    """y = f64(x) @ f64(W_hat)^T, float64 accumulation (BLAS dgemm)."""
+    x = bf16_bits_to_f64(x_bf16)
+    return x @ np.asarray(w_hat, dtype=np.float64).T
+
+
+def forward(x_bf16, packed, s16, b16, bits, k, group: int = GROUP) -> np.ndarray:
+    """Full path: unpack -> dequantize (fp32) -> fp64 GEMM. Returns float64 [M, N]."""
+    q = unpack(packed, bits, k)
+    w_hat = dequantize(q, s16, b16, group)
+    return gemm_f64(x_bf16, w_hat)
+
+
+def forward_rows(x_bf16, packed, s16, b16, bits, k, rows, cols=None, group: int = GROUP):
+    """The same result restricted to selected output rows (and columns)."""
+    x_sel = np.asarray(x_bf16)[np.asarray(rows)]
+    if cols is not None:
+        cols = np.asarray(cols)
+        packed, s16, b16 = packed[cols], s16[cols], b16[cols]
+    return forward(x_sel, packed, s16, b16, bits, k, group)
+
+
+def error_metrics(y: np.ndarray, y_ref: np.ndarray) -> dict:
+    """relF = ||y - ref||_F / ||ref||_F ; maxabs_over_rms = max|y - ref| / rms(ref)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    d = y - y_ref
+    nref = float(np.linalg.norm(y_ref))
+    rms = nref / math.sqrt(max(y_ref.size, 1))
+    relf = float(np.linalg.norm(d)) / nref if nref > 0 else float(np.linalg.norm(d))
+    mad = float(np.max(np.abs(d))) if d.size else 0.0
+    return {"relF": relf, "maxabs_over_rms": (mad / rms) if rms > 0 else mad, "max_abs": mad, "rms": rms}
+
+
+def timed_forward(x_bf16, packed, s16, b16, bits, k, group: int = GROUP):
+    """Oracle forward with the dequantize and GEMM legs timed separately (seconds)."""
+    t0 = time.perf_counter()
+    q = unpack(packed, bits, k)
+    w_hat = dequantize(q, s16, b16, group)
+    t1 = time.perf_counter()
+    y = gemm_f64(x_bf16, w_hat)
+    t2 = time.perf_counter()
+    return y, {"dequant_s": t1 - t0, "gemm_s": t2 - t1, "total_s": t2 - t0}

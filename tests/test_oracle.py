@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each test states what it checks against: a figure printed on the pages
+(tests/golden/page_figures.json), a hand-worked example (tests/golden/
+hand_example.json), exact rational arithmetic, brute force or a closed form.
+No expected value here comes from the HIP library.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- independent helpers
+
+def exact_f16_rne(v: Fraction) -> int:
+    """Round a rational to IEEE half, half-to-even, returning the bit pattern.
+
+    Written from the IEEE 754 binary16 definition (5 exponent bits, bias 15,
+    10 fraction bits, subnormals below 2**-14); shares nothing with NumPy.
+    """
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    if a == 0:
+        return sign
+    e = math.floor(math.log2(a)) if a.numerator and a.denominator else 0
+    # fix floor(log2) exactly
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -14)                      # subnormal range shares the 2**-14 exponent
+    ulp = Fraction(2) ** (e - 10)
+    m = a / ulp                          # significand in units of ulp
+    fl = math.floor(m)
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    if fl == 2048:                       # carried into the next binade
+        fl = 1024
+        e += 1
+    if e > 15:
+        return sign | 0x7C00             # overflow to inf
+    if fl < 1024:                        # subnormal
+        return sign | fl
+    return sign | ((e + 15) << 10) | (fl - 1024)
+
+
+def f16_value(bits: int) -> Fraction:
+    s = -1 if bits & 0x8000 else 1
+    e = (bits >> 10) & 0x1F
+    f = bits & 0x3FF
+    if e == 0:
+        return s * Fraction(f) * Fraction(2) ** -24
+    return s * (1 + Fraction(f, 1024)) * Fraction(2) ** (e - 15)
+
+
+# ----------------------------------------------------------------- bits per weight / sizes
+
+def test_bpw_closed_form_matches_page_overhead():
+    fig = _golden("page_figures.json")
+    over = fig["group_overhead_bits"]["value"]
+    assert fig["group_overhead_bits"]["group"] == oracle.GROUP == fig["group_size"]["value"]
+    for b in (2, 4, 8):
+        assert oracle.bits_per_weight(b) == b + over
+    for (n, k) in [(256, 512), (13824, 4608), (4608, 53248), (3, 64)]:
+        for b in (2, 4, 8):
+            assert oracle.storage_bytes(b, n, k) * 8 == n * k * (b + over)
+
+
+def test_page_sizes_follow_from_closed_form():
+    fig = _golden("page_figures.json")
+    p = fig["quantized_params"]["value"]
+    q4 = p * oracle.bits_per_weight(4) / 8 / 1e9
+    q8 = p * oracle.bits_per_weight(8) / 8 / 1e9
+    bf16 = p * 2 / 1e9
+    assert abs(q4 - fig["q4_on_disk_gb"]["value"]) < 0.5       # 14.2 vs ~14
+    assert abs(q8 - fig["q8_on_disk_gb"]["value"]) < 0.5       # 26.8 vs ~27
+    assert abs(bf16 - fig["bf16_snapshot_gb"]["value"]) < 0.5  # 50.4 vs ~50
+    assert abs(q4 / bf16 - fig["q4_download_fraction_vs_bf16"]["value"]) < 0.05
+
+
+# ----------------------------------------------------------------- packing
+
+def test_pack_hand_words():
+    hw = _golden("hand_example.json")["pack_words"]
+    for key, bits in (("bits4_codes_1_to_8", 4), ("bits2_codes", 2), ("bits8_codes", 8)):
+        codes = np.array([hw[key]["codes"]], dtype=np.uint8)
+        word = int(hw[key]["word_hex"], 16)
+        packed = oracle.pack(codes, bits)
+        assert packed.shape == (1, 1) and int(packed[0, 0]) == word
+        assert np.array_equal(oracle.unpack(packed, bits, codes.shape[1]), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_pack_unpack_round_trip(bits):
+    n, k = 7, 256
+    q = inputs.random_codes(n, k, bits, workload_id=99)
+    assert np.array_equal(oracle.unpack(oracle.pack(q, bits), bits, k), q)
+    qmax = (1 << bits) - 1
+    for pat in (np.zeros((n, k)), np.full((n, k), qmax), np.tile([0, qmax], (n, k // 2))):
+        pat = pat.astype(np.uint8)
+        assert np.array_equal(oracle.unpack(oracle.pack(pat, bits), bits, k), pat)
+    all_q = oracle.pack(np.full((1, 32 // bits), qmax, dtype=np.uint8), bits)
+    assert int(all_q[0, 0]) == 0xFFFFFFFF
+    words = np.random.default_rng(5).integers(0, 2**32, size=(n, k * bits // 32), dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(oracle.pack(oracle.unpack(words, bits, k), bits), words)
+
+
+def test_pack_rejects_out_of_range_code():
+    with pytest.raises(ValueError):
+        oracle.pack(np.array([[16] + [0] * 7], dtype=np.uint8), 4)
+
+
+# ----------------------------------------------------------------- f16 / bf16 conversions
+
+def test_f16_rounding_matches_exact_rne():
+    vals = [Fraction(1) + Fraction(1, 2048), Fraction(1) + Fraction(3, 2048), Fraction(65504),
+            Fraction(1, 2**24), Fraction(3, 2**26), Fraction(5, 2**26), Fraction(-1, 3),
+            Fraction(1, 10), Fraction(3, 2) / 15]
+    rng = np.random.default_rng(11)
+    vals += [Fraction(float(v)) for v in rng.normal(0, 0.05, 400).astype(np.float32)]
+    vals += [Fraction(float(v)) for v in rng.uniform(-7e-5, 7e-5, 200).astype(np.float32)]
+    for v in vals:
+        f32 = np.float32(float(v))
+        if Fraction(float(f32)) != v:
+            continue  # only values exactly representable in fp32 are fed to the conversion
+        got = int(oracle.f32_to_f16_bits(np.array([f32]))[0])
+        assert got == exact_f16_rne(v), (v, hex(got), hex(exact_f16_rne(v)))
+    # the two ties, by hand: 1 + 2^-11 -> 1.0 (even), 1 + 3*2^-11 -> 1 + 2^-9
+    assert int(oracle.f32_to_f16_bits(np.array([1 + 2**-11], np.float32))[0]) == 0x3C00
+    assert int(oracle.f32_to_f16_bits(np.array([1 + 3 * 2**-11], np.float32))[0]) == 0x3C02
+
+
+def test_bf16_decode_known_patterns():
+    got = oracle.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x4300, 0x0000, 0x8000, 0x0001], dtype=np.uint16))
+    assert list(got[:5]) == [1.0, -2.0, 128.0, 0.0, -0.0]
+    assert got[5] == 2.0 ** -133
+
+
+def test_input_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = inputs.activations_f32(33, 128, workload_id=7, structure="outlier")
+    mine = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+# ----------------------------------------------------------------- RTN fit
+
+def test_rtn_hand_example():
+    ex = _golden("hand_example.json")["rtn_4bit_group"]
+    k = np.arange(64)
+    w = (-1 + 0.125 * (k % 16)).astype(np.float32)[None, :]
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    assert int(s16[0, 0]) == int(ex["s16_hex"], 16)
+    assert int(b16[0, 0]) == int(ex["b16_hex"], 16)
+    assert np.array_equal(q[0], (k % 16).astype(np.uint8))
+    words = oracle.pack(q, 4)
+    assert [int(v) for v in words[0]] == [int(h, 16) for h in ex["words_hex"]]
+    w_hat = oracle.dequantize(q, s16, b16)
+    assert np.array_equal(w_hat, w)
+
+
+def test_rtn_tie_rounds_half_to_even():
+    ex = _golden("hand_example.json")["tie_4bit_group"]
+    s_f = float(np.float16(0.1))
+    assert np.float16(0.1).view(np.uint16) == int(ex["s16_hex"], 16)
+    w = np.zeros((1, 64), np.float32)
+    w[0, 1] = 1.5
+    w[0, 2] = 2.5 * s_f
+    w[0, 3] = 3.5 * s_f
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    assert int(s16[0, 0]) == int(ex["s16_hex"], 16) and int(b16[0, 0]) == int(ex["b16_hex"], 16)
+    assert list(q[0, :4]) == ex["q_first4"]
+    assert not q[0, 4:].any()
+
+
+def test_constant_group():
+    w = np.full((2, 128), 0.3, np.float32)
+    w[1, 64:] = -2.75
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    assert not s16.any()
+    assert not q.any()
+    assert int(b16[0, 0]) == exact_f16_rne(Fraction(float(np.float32(0.3))))
+    w_hat = oracle.dequantize(q, s16, b16)
+    assert np.array_equal(w_hat[0], np.full(128, float(np.float16(0.3)), np.float32))
+    assert np.array_equal(w_hat[1, 64:], np.full(64, -2.75, np.float32))
+
+
+def test_rtn_rejects_non_finite_and_overflow():
+    w = np.zeros((1, 64), np.float32)
+    w[0, 5] = np.nan
+    with pytest.raises(ValueError):
+        oracle.quantize_rtn(w, 4)
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0] = 1e6   # bias fine (0) but scale 1e6/15 overflows f16
+    with pytest.raises(ValueError):
+        oracle.quantize_rtn(w, 4)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rtn_scale_bias_are_rounded_min_max(bits):
+    """s and b equal exact-RNE f16 of (max-min)/Q (fp32 ops) and of min, group by group."""
+    w = inputs.weights(6, 256, workload_id=21)
+    q, s16, b16 = oracle.quantize_rtn(w, bits)
+    qmax = (1 << bits) - 1
+    for n in range(w.shape[0]):
+        for g in range(w.shape[1] // 64):
+            grp = w[n, 64 * g:64 * g + 64]
+            mn, mx = np.float32(grp.min()), np.float32(grp.max())
+            s32 = np.float32(np.float32(mx - mn) / np.float32(qmax))
+            assert int(s16[n, g]) == exact_f16_rne(Fraction(float(s32)))
+            assert int(b16[n, g]) == exact_f16_rne(Fraction(float(mn)))
+    assert q.max() <= qmax
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rtn_brute_force_nearest_code(bits):
+    """q is the nearest grid point among all 2**bits codes (exact fp64 distances)."""
+    w = inputs.weights(16, 512, workload_id=22)
+    q, s16, b16 = oracle.quantize_rtn(w, bits)
+    s = oracle.f16_bits_to_f32(s16).astype(np.float64).repeat(64, axis=1)
+    b = oracle.f16_bits_to_f32(b16).astype(np.float64).repeat(64, axis=1)
+    codes = np.arange(1 << bits, dtype=np.float64)
+    grid = s[:, :, None] * codes[None, None, :] + b[:, :, None]     # exact in fp64
+    d = np.abs(w.astype(np.float64)[:, :, None] - grid)              # exact in fp64
+    best = d.min(axis=2)
+    chosen = np.take_along_axis(d, q.astype(np.int64)[:, :, None], axis=2)[:, :, 0]
+    # the chosen code is optimal up to the fp32 rounding of (w - b) / s
+    assert np.all(chosen - best <= 2.0 ** -20 * s)
+    # and exactly the argmin wherever the best code is clearly separated
+    srt = np.sort(d, axis=2)
+    clear = (srt[:, :, 1] - srt[:, :, 0]) > 2.0 ** -18 * s
+    assert np.array_equal(q[clear], d.argmin(axis=2)[clear].astype(np.uint8))
+    # error bound of round-to-nearest on a uniform grid
+    w_hat = oracle.dequantize(q, s16, b16).astype(np.float64)
+    assert np.all(np.abs(w - w_hat) <= 0.5 * s + 4 * np.spacing(np.abs(w).astype(np.float32)).astype(np.float64) + 1e-12)
+
+
+# ----------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_dequant_equals_exact_then_round(bits):
+    """fp32 mul+add equals the exactly computed s*q + b rounded once to fp32."""
+    n, k = 32, 256
+    q = inputs.random_codes(n, k, bits, workload_id=23)
+    s16 = inputs.random_f16_bits(n, k // 64, 1e-4, 0.2, workload_id=23, role=inputs.ROLE_SCALE)
+    b16 = inputs.random_f16_bits(n, k // 64, -3.0, 3.0, workload_id=23, role=inputs.ROLE_BIAS)
+    got = oracle.dequantize(q, s16, b16)
+    s = np.asarray(s16).view(np.float16).astype(np.float64).repeat(64, axis=1)
+    b = np.asarray(b16).view(np.float16).astype(np.float64).repeat(64, axis=1)
+    exact = s * q.astype(np.float64) + b     # exact in fp64 for these magnitudes
+    assert np.array_equal(got, exact.astype(np.float32))
+    # spot-check a few against rational arithmetic
+    for (i, j) in [(0, 0), (3, 77), (31, 255)]:
+        v = f16_value(int(s16[i, j // 64])) * int(q[i, j]) + f16_value(int(b16[i, j // 64]))
+        assert Fraction(float(got[i, j])) == Fraction(float(np.float32(float(v))))
+
+
+# ----------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("shape", [(1, 64, 1), (3, 128, 5), (17, 192, 9), (8, 512, 16)])
+def test_gemm_brute_force_fsum(shape):
+    m, k, n = shape
+    x = inputs.activations_bf16(m, k, workload_id=31)
+    w = inputs.weights(n, k, workload_id=31)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    y = oracle.forward(x, oracle.pack(q, 4), s16, b16, 4, k)
+    xf = oracle.bf16_bits_to_f64(x)
+    w_hat = oracle.dequantize(q, s16, b16).astype(np.float64)
+    for i in range(m):
+        for j in range(n):
+            ref = math.fsum(float(xf[i, t]) * float(w_hat[j, t]) for t in range(k))  # products exact
+            assert abs(y[i, j] - ref) <= 1e-12 * max(1.0, math.fsum(abs(float(xf[i, t]) * float(w_hat[j, t])) for t in range(k)))
+
+
+def test_identity_x_gives_transposed_weights():
+    k, n = 128, 24   # M = K != N, so a transposed operand cannot pass
+    w = inputs.weights(n, k, workload_id=32)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    one = 0x3F80
+    x = np.zeros((k, k), np.uint16)
+    x[np.arange(k), np.arange(k)] = one
+    y = oracle.forward(x, oracle.pack(q, 4), s16, b16, 4, k)
+    assert y.shape == (k, n)
+    assert np.array_equal(y, oracle.dequantize(q, s16, b16).astype(np.float64).T)
+
+
+def test_zero_and_ones_rows():
+    k, n = 256, 10
+    w = inputs.weights(n, k, workload_id=33)
+    q, s16, b16 = oracle.quantize_rtn(w, 8)
+    x = np.zeros((2, k), np.uint16)
+    x[1, :] = 0x3F80
+    y = oracle.forward(x, oracle.pack(q, 8), s16, b16, 8, k)
+    assert not y[0].any()
+    w_hat = oracle.dequantize(q, s16, b16)
+    for j in range(n):
+        assert abs(y[1, j] - math.fsum(float(v) for v in w_hat[j])) <= 1e-12
+
+
+def test_linearity():
+    k, n, m = 256, 12, 5
+    w = inputs.weights(n, k, workload_id=34)
+    q, s16, b16 = oracle.quantize_rtn(w, 2)
+    p = oracle.pack(q, 2)
+    x1 = inputs.activations_bf16(m, k, workload_id=34)
+    x2 = inputs.activations_bf16(m, k, workload_id=35)
+    # x1 + x2 exactly representable? use 2*x1 instead (exact scaling in bf16)
+    x1f = oracle.bf16_bits_to_f64(x1)
+    two_x1 = inputs.f32_to_bf16_bits((2 * x1f).astype(np.float32))
+    y1 = oracle.forward(x1, p, s16, b16, 2, k)
+    assert np.allclose(oracle.forward(two_x1, p, s16, b16, 2, k), 2 * y1, rtol=0, atol=1e-12)
+    y2 = oracle.forward(x2, p, s16, b16, 2, k)
+    xx = np.concatenate([x1, x2])
+    assert np.allclose(oracle.forward(xx, p, s16, b16, 2, k), np.concatenate([y1, y2]), rtol=0, atol=1e-12)
+
+
+def test_error_metrics_closed_form():
+    ref = np.ones((4, 4))
+    y = ref.copy()
+    y[0, 0] += 0.5
+    e = oracle.error_metrics(y, ref)
+    assert abs(e["relF"] - 0.5 / 4.0) < 1e-15
+    assert abs(e["maxabs_over_rms"] - 0.5) < 1e-15
+
+
+def test_forward_rows_matches_full():
+    m, k, n = 9, 128, 11
+    x = inputs.activations_bf16(m, k, workload_id=36)
+    w = inputs.weights(n, k, workload_id=36)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    p = oracle.pack(q, 4)
+    full = oracle.forward(x, p, s16, b16, 4, k)
+    rows, cols = [0, 4, 8], [1, 10]
+    sub = oracle.forward_rows(x, p, s16, b16, 4, k, rows, cols)
+    assert np.array_equal(sub, full[np.ix_(rows, cols)])
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+def test_planted_bit_order_mistake_is_caught(monkeypatch):
+    """A big-endian nibble order in the oracle's unpack must fail the hand-word pin."""
+    real_unpack = oracle.qlinear_oracle.unpack
+
+    def wrong_unpack(words, bits, k):
+        q = real_unpack(words, bits, k)
+        c = 32 // bits
+        return q.reshape(q.shape[0], -1, c)[:, :, ::-1].reshape(q.shape)
+
+    hw = _golden("hand_example.json")["pack_words"]["bits4_codes_1_to_8"]
+    word = np.array([[int(hw["word_hex"], 16)]], dtype=np.uint32)
+    assert list(wrong_unpack(word, 4, 8)[0]) != hw["codes"]
+    assert list(real_unpack(word, 4, 8)[0]) == hw["codes"]
+
+
+def test_planted_dropped_bias_is_caught():
+    """Dequantizing without the bias term must fail the hand example."""
+    k = np.arange(64)
+    w = (-1 + 0.125 * (k % 16)).astype(np.float32)[None, :]
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    no_bias = oracle.dequantize(q, s16, np.zeros_like(b16))
+    assert not np.array_equal(no_bias, w)
+    assert np.array_equal(oracle.dequantize(q, s16, b16), w)
+
+
+# ----------------------------------------------------------------- generators
+
+def test_generators_are_deterministic():
+    a = inputs.workload_inputs("tiny")
+    b = inputs.workload_inputs("tiny")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert a[0].shape == (256, 512) and a[1].shape == (64, 512)
+    xo = inputs.activations_f32(4, 4608, workload_id=2, structure="outlier")
+    big = np.abs(xo).max(axis=0) > 0
+    assert big.all()
+    xs = inputs.activations_f32(64, 53248, workload_id=4, structure="slices")
+    stds = xs.reshape(64, 13, 4096).std(axis=(0, 2))
+    assert np.all((stds > 0.4) & (stds < 4.2))
