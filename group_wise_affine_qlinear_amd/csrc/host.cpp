@@ -1,0 +1,447 @@
+// C ABI of libqlinear: argument validation, dispatch, workspace, host packer
+// and host RTN quantizer. Kernels live in gemm.hip, skinny.hip and misc.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qlinear.h"
+#include "ql_kernels.h"
+
+#define QL_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kGroup = 64;
+constexpr int kMaxSkinnyM = 16;
+
+thread_local char g_last_path[160] = "none";
+
+void set_last_path(const char *s) {
+  std::snprintf(g_last_path, sizeof(g_last_path), "%s", s);
+}
+
+bool bits_ok(int bits) { return bits == 2 || bits == 4 || bits == 8; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// fp32 -> IEEE half bit pattern, round-half-to-even (overflow -> inf).
+uint16_t f32_to_f16(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return (uint16_t)(sign | 0x7C00u | (ax > 0x7F800000u ? 0x200u : 0u));
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // >= 65520 rounds to inf
+  if (ax < 0x38800000u) {                                    // below 2^-14: subnormal or zero
+    if (ax < 0x33000000u) return (uint16_t)sign;             // below 2^-25
+    const uint32_t e = ax >> 23;
+    const uint32_t m = (ax & 0x7FFFFFu) | 0x800000u;
+    const uint32_t shift = 126u - e;                         // value / 2^-24 = m >> shift
+    uint32_t q = m >> shift;
+    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1u);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    return (uint16_t)(sign | q);
+  }
+  const uint32_t e = (ax >> 23) - 112u;
+  const uint32_t m = ax & 0x7FFFFFu;
+  uint32_t q = (e << 10) | (m >> 13);
+  const uint32_t rem = m & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (q & 1u))) ++q;
+  return (uint16_t)(sign | q);
+}
+
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+  uint32_t x;
+  if (e == 0) {
+    if (m == 0) {
+      x = sign;
+    } else {  // subnormal: value = m * 2^-24, exact in fp32
+      float v = std::ldexp((float)m, -24);
+      std::memcpy(&x, &v, 4);
+      x |= sign;
+    }
+  } else if (e == 31) {
+    x = sign | 0x7F800000u | (m << 13);
+  } else {
+    x = sign | ((e + 112u) << 23) | (m << 13);
+  }
+  float f;
+  std::memcpy(&f, &x, 4);
+  return f;
+}
+
+// ---- library-owned workspace for qlinear_forward (one per device)
+struct Workspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+constexpr int kMaxDevices = 64;
+Workspace g_ws[kMaxDevices];
+std::mutex g_ws_mutex;
+
+int get_owned_workspace(size_t need, void **out) {
+  *out = nullptr;
+  if (need == 0) return QL_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QL_EHIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace &w = g_ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      // earlier launches may still read the old buffer
+      if (hipDeviceSynchronize() != hipSuccess) return QL_EHIP;
+      if (hipFree(w.ptr) != hipSuccess) return QL_EHIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t sz = (size_t)round_up((int64_t)need, 1 << 20);
+    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
+      w.ptr = nullptr;
+      return QL_EHIP;
+    }
+    w.bytes = sz;
+  }
+  *out = w.ptr;
+  return QL_OK;
+}
+
+// ---- dispatch
+struct Plan {
+  int path = QL_PATH_AUTO;
+  int tile = 0;
+  int splits = 1;
+  int groups_per_split = 0;
+  size_t ws_xsum = 0, ws_partial = 0;
+};
+
+int env_int(const char *name, int dflt) {
+  const char *v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+// Static tile table from sweeps on MI355X, with a heuristic default. Entries:
+// bits (0 = any), M range, N range, K range -> tile id and split count
+// (0 = heuristic split).
+struct TableEntry {
+  int bits;
+  int64_t m_lo, m_hi, n_lo, n_hi, k_lo, k_hi;
+  int tile, splits;
+};
+const TableEntry kTable[] = {
+    // placeholder defaults; refined by measurement
+    {0, 17, 1LL << 40, 1, 1LL << 40, 1, 1LL << 40, 1, 0},
+};
+
+int choose_splits(int64_t tiles, int G) {
+  // Fill ~2 waves of blocks on 256 CUs when the tile grid alone is small;
+  // keep at least 8 groups per split.
+  if (tiles >= 256 || G < 16) return 1;
+  int s = (int)((512 + tiles - 1) / tiles);
+  if (s > G / 8) s = G / 8;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : s;
+}
+
+int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int force_split,
+              int force_tile, Plan *p) {
+  const int G = (int)(K / kGroup);
+  int path = force_path;
+  if (path == QL_PATH_AUTO) {
+    const int envp = env_int("QLINEAR_FORCE_PATH", 0);
+    if (envp > 0) path = envp;
+  }
+  if (path == QL_PATH_AUTO) path = (M <= kMaxSkinnyM) ? QL_PATH_SKINNY : QL_PATH_GEMM;
+  if (path == QL_PATH_SKINNY) {
+    if (M > kMaxSkinnyM) return QL_EUNSUPPORTED;
+    p->path = QL_PATH_SKINNY;
+    return QL_OK;
+  }
+  if (path != QL_PATH_GEMM && path != QL_PATH_SPLITK) return QL_EUNSUPPORTED;
+  int tile = force_tile > 0 ? force_tile : env_int("QLINEAR_TILE", 0);
+  int splits = 0;
+  if (tile <= 0) {
+    for (const TableEntry &e : kTable) {
+      if ((e.bits == 0 || e.bits == bits) && M >= e.m_lo && M <= e.m_hi && N >= e.n_lo && N <= e.n_hi &&
+          K >= e.k_lo && K <= e.k_hi) {
+        tile = e.tile;
+        splits = e.splits;
+        break;
+      }
+    }
+    if (tile <= 0) tile = 1;
+  }
+  const ql::TileInfo *ti = ql::gemm_tile(tile);
+  if (!ti) return QL_EUNSUPPORTED;
+  const int64_t tiles = ((M + ti->bm - 1) / ti->bm) * ((N + ti->bn - 1) / ti->bn);
+  if (force_split > 0) splits = force_split;
+  if (splits <= 0) splits = choose_splits(tiles, G);
+  if (path == QL_PATH_GEMM && force_path == QL_PATH_GEMM) splits = force_split > 0 ? force_split : 1;
+  if (path == QL_PATH_SPLITK && splits < 2) splits = G >= 2 ? 2 : 1;
+  if (splits > G) splits = G > 0 ? G : 1;
+  const int gps = G > 0 ? (G + splits - 1) / splits : 0;
+  if (G > 0) splits = (G + gps - 1) / gps;  // no empty split
+  if (path == QL_PATH_SPLITK && splits < 2) return QL_EUNSUPPORTED;
+  p->path = splits > 1 ? QL_PATH_SPLITK : QL_PATH_GEMM;
+  p->tile = tile;
+  p->splits = splits;
+  p->groups_per_split = gps;
+  p->ws_xsum = (size_t)G * (size_t)round_up(M, 256) * 4u;
+  p->ws_partial = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4u : 0;
+  return QL_OK;
+}
+
+size_t plan_ws(const Plan &p) {
+  if (p.path == QL_PATH_SKINNY) return 0;
+  return (size_t)round_up((int64_t)p.ws_xsum, 256) + p.ws_partial;
+}
+
+int validate_forward(const ql_forward_args *a) {
+  if (!a) return QL_EINVAL;
+  if (!bits_ok(a->bits) || a->group != kGroup) return QL_EUNSUPPORTED;
+  if (a->M < 0 || a->N < 0 || a->K < 0 || a->K % kGroup) return QL_EINVAL;
+  if (a->M > (1LL << 31) - 1 || a->N > (1LL << 31) - 1 || a->K > (1LL << 30)) return QL_EINVAL;
+  if (a->out_dtype != QL_OUT_F32 && a->out_dtype != QL_OUT_BF16) return QL_EINVAL;
+  if (a->M == 0 || a->N == 0) return QL_OK;
+  if (!a->out) return QL_EINVAL;
+  if (!aligned16(a->out)) return QL_EALIGN;
+  if (a->K == 0) return QL_OK;
+  if (!a->x || !a->packed_q || !a->scales || !a->biases) return QL_EINVAL;
+  if (!aligned16(a->x) || !aligned16(a->packed_q)) return QL_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(a->scales) & 1u) || (reinterpret_cast<uintptr_t>(a->biases) & 1u))
+    return QL_EALIGN;
+  return QL_OK;
+}
+
+}  // namespace
+
+QL_API int qlinear_version(void) { return 100; }
+
+QL_API const char *qlinear_status_string(int status) {
+  switch (status) {
+    case QL_OK: return "ok";
+    case QL_EINVAL: return "invalid argument (size, null pointer or K not a multiple of 64)";
+    case QL_EALIGN: return "misaligned pointer (x, out and packed_q need 16-byte alignment)";
+    case QL_EUNSUPPORTED: return "unsupported (bits must be 2, 4 or 8; group 64; or forced path cannot serve shape)";
+    case QL_EWORKSPACE: return "workspace missing or too small";
+    case QL_EHIP: return "HIP runtime error";
+    case QL_ERANGE: return "non-finite weight or f16 overflow of scale/bias";
+    default: return "unknown status";
+  }
+}
+
+QL_API int qlinear_last_path(char *buf, size_t len) {
+  if (!buf || len == 0) return QL_EINVAL;
+  std::snprintf(buf, len, "%s", g_last_path);
+  return QL_OK;
+}
+
+QL_API size_t qlinear_packed_words(int bits, int64_t N, int64_t K) {
+  if (!bits_ok(bits) || N < 0 || K < 0) return 0;
+  return (size_t)N * (size_t)K * (size_t)bits / 32u;
+}
+
+QL_API size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K) {
+  if (!bits_ok(bits) || M <= 0 || N <= 0 || K <= 0 || K % kGroup) return 0;
+  Plan p;
+  if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, &p) != QL_OK) return 0;
+  return plan_ws(p);
+}
+
+QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
+  int st = validate_forward(a);
+  if (st != QL_OK) return st;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+  if (a->M == 0 || a->N == 0) {
+    set_last_path("noop");
+    return QL_OK;
+  }
+  if (a->K == 0) {
+    set_last_path("fill_zero");
+    return ql::launch_fill_zero(a->out, a->M * a->N, a->out_dtype == QL_OUT_BF16, stream) == hipSuccess ? QL_OK
+                                                                                                       : QL_EHIP;
+  }
+  Plan p;
+  st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, &p);
+  if (st != QL_OK) return st;
+  const int G = (int)(a->K / kGroup);
+  const int out_bf16 = a->out_dtype == QL_OUT_BF16;
+  char buf[160];
+  if (p.path == QL_PATH_SKINNY) {
+    ql::SkinnyArgs s{static_cast<const uint16_t *>(a->x), a->packed_q,
+                     static_cast<const uint16_t *>(a->scales), static_cast<const uint16_t *>(a->biases),
+                     a->out, a->M, a->N, a->K, G, out_bf16};
+    std::snprintf(buf, sizeof(buf), "skinny_b%d_m%s", a->bits, a->M <= 8 ? "8" : "16");
+    set_last_path(buf);
+    return ql::launch_skinny(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;
+  }
+  const size_t need = plan_ws(p);
+  void *ws = a->workspace;
+  if (ws) {
+    if (a->workspace_bytes < need) return QL_EWORKSPACE;
+    if (!aligned16(ws)) return QL_EALIGN;
+  } else {
+    st = get_owned_workspace(need, &ws);
+    if (st != QL_OK) return st;
+  }
+  const int64_t Mp = round_up(a->M, 256);
+  float *xsum = static_cast<float *>(ws);
+  float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up((int64_t)p.ws_xsum, 256));
+  if (ql::launch_xsum(static_cast<const uint16_t *>(a->x), xsum, a->M, a->K, Mp, stream) != hipSuccess)
+    return QL_EHIP;
+  ql::GemmArgs g{static_cast<const uint16_t *>(a->x),
+                 a->packed_q,
+                 static_cast<const uint16_t *>(a->scales),
+                 static_cast<const uint16_t *>(a->biases),
+                 xsum,
+                 a->out,
+                 partial,
+                 a->M, a->N, a->K, Mp,
+                 G,
+                 p.splits,
+                 p.groups_per_split,
+                 out_bf16};
+  const ql::TileInfo *ti = ql::gemm_tile(p.tile);
+  std::snprintf(buf, sizeof(buf), "%s_b%d_split%d", ti ? ti->name : "gemm", a->bits, p.splits);
+  set_last_path(buf);
+  if (ql::launch_gemm(a->bits, p.tile, g, stream) != hipSuccess) return QL_EHIP;
+  if (p.splits > 1) {
+    if (ql::launch_splitk_reduce(partial, p.splits, a->M, a->N, a->out, out_bf16, stream) != hipSuccess)
+      return QL_EHIP;
+  }
+  return QL_OK;
+}
+
+QL_API int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales, const void *biases,
+                           int bits, int group, int64_t M, int64_t N, int64_t K, float *out) {
+  ql_forward_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.packed_q = packed_q;
+  a.scales = scales;
+  a.biases = biases;
+  a.bits = bits;
+  a.group = group;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.out = out;
+  a.out_dtype = QL_OUT_F32;
+  return qlinear_forward_ex(&a, nullptr);
+}
+
+QL_API int qlinear_pack_host(const uint8_t *q, int bits, int64_t N, int64_t K, uint32_t *packed) {
+  if (!bits_ok(bits)) return QL_EUNSUPPORTED;
+  const int cpw = 32 / bits;
+  if (N < 0 || K < 0 || K % cpw) return QL_EINVAL;
+  if (N * K > 0 && (!q || !packed)) return QL_EINVAL;
+  const uint32_t lim = 1u << bits;
+  for (int64_t i = 0; i < N * K; ++i)
+    if (q[i] >= lim) return QL_ERANGE;
+  const int64_t wr = K / cpw;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t j = 0; j < wr; ++j) {
+      uint32_t word = 0;
+      const uint8_t *src = q + n * K + j * cpw;
+      for (int i = 0; i < cpw; ++i) word |= (uint32_t)src[i] << (bits * i);
+      packed[n * wr + j] = word;
+    }
+  }
+  return QL_OK;
+}
+
+QL_API int qlinear_unpack_host(const uint32_t *packed, int bits, int64_t N, int64_t K, uint8_t *q) {
+  if (!bits_ok(bits)) return QL_EUNSUPPORTED;
+  const int cpw = 32 / bits;
+  if (N < 0 || K < 0 || K % cpw) return QL_EINVAL;
+  if (N * K > 0 && (!q || !packed)) return QL_EINVAL;
+  const uint32_t mask = (1u << bits) - 1u;
+  const int64_t wr = K / cpw;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < wr; ++j) {
+      const uint32_t word = packed[n * wr + j];
+      for (int i = 0; i < cpw; ++i) q[n * K + j * cpw + i] = (uint8_t)((word >> (bits * i)) & mask);
+    }
+  return QL_OK;
+}
+
+QL_API int qlinear_quantize_rtn_host(const float *w, int bits, int group, int64_t N, int64_t K, uint8_t *q,
+                                     uint16_t *s16, uint16_t *b16) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (N * K > 0 && (!w || !q || !s16 || !b16)) return QL_EINVAL;
+  const int64_t G = K / kGroup;
+  const float qmax = (float)((1 << bits) - 1);
+  for (int64_t i = 0; i < N * K; ++i)
+    if (!std::isfinite(w[i])) return QL_ERANGE;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t g = 0; g < G; ++g) {
+      const float *wp = w + n * K + g * kGroup;
+      // min/max order -0 below +0 (IEEE 754-2019 minimum/maximum)
+      float mn = wp[0], mx = wp[0];
+      for (int k = 1; k < kGroup; ++k) {
+        const float v = wp[k];
+        if (v < mn || (v == mn && std::signbit(v) && !std::signbit(mn))) mn = v;
+        if (v > mx || (v == mx && !std::signbit(v) && std::signbit(mx))) mx = v;
+      }
+      volatile float diff = mx - mn;  // keep fp32 rounding of each step explicit
+      volatile float s32 = diff / qmax;
+      const uint16_t sh = f32_to_f16(s32), bh = f32_to_f16(mn);
+      if ((sh & 0x7C00u) == 0x7C00u || (bh & 0x7C00u) == 0x7C00u) return QL_ERANGE;
+      const float sf = f16_to_f32(sh), bf = f16_to_f32(bh);
+      for (int k = 0; k < kGroup; ++k) {
+        uint8_t code = 0;
+        if (sf != 0.f) {
+          volatile float d = wp[k] - bf;
+          volatile float t = d / sf;
+          float r = std::nearbyint((float)t);
+          if (r < 0.f) r = 0.f;
+          if (r > qmax) r = qmax;
+          code = (uint8_t)r;
+        }
+        q[n * K + g * kGroup + k] = code;
+      }
+      s16[n * G + g] = sh;
+      b16[n * G + g] = bh;
+    }
+  }
+  return QL_OK;
+}
+
+QL_API int qlinear_quantize_rtn(const float *w, int bits, int group, int64_t N, int64_t K, uint32_t *packed_q,
+                                uint16_t *scales, uint16_t *biases, int *status_dev, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!w || !packed_q || !scales || !biases) return QL_EINVAL;
+  if (!aligned16(w) || !aligned16(packed_q)) return QL_EALIGN;
+  set_last_path("quantize_rtn");
+  return ql::launch_quantize(bits, w, N, K, packed_q, scales, biases, status_dev,
+                             reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
+QL_API int qlinear_dequantize(const uint32_t *packed_q, const void *scales, const void *biases, int bits,
+                              int group, int64_t N, int64_t K, float *w_out, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!packed_q || !scales || !biases || !w_out) return QL_EINVAL;
+  if (!aligned16(packed_q) || !aligned16(w_out)) return QL_EALIGN;
+  set_last_path("dequantize");
+  return ql::launch_dequant(bits, packed_q, static_cast<const uint16_t *>(scales),
+                            static_cast<const uint16_t *>(biases), N, K, w_out,
+                            reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}

@@ -1,0 +1,60 @@
+// Internal launcher interface between the C ABI (host.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ql {
+
+struct GemmArgs {
+  const uint16_t *x;      // bf16 [M, K]
+  const uint32_t *w;      // packed codes [N, K*bits/32]
+  const uint16_t *s;      // f16 [N, G]
+  const uint16_t *b;      // f16 [N, G]
+  const float *xsum;      // [G, Mp] per-group row sums of x
+  void *out;              // [M, N] fp32 or bf16 (splits == 1)
+  float *partial;         // [splits, M, N] fp32 (splits > 1)
+  int64_t M, N, K, Mp;
+  int G;
+  int splits;
+  int groups_per_split;
+  int out_bf16;
+};
+
+struct TileInfo {
+  int id, bm, bn, warps_m, warps_n;
+  const char *name;
+};
+
+// GEMM tile configurations compiled into the library (id >= 1).
+const TileInfo *gemm_tile(int id);
+int gemm_tile_count();
+size_t gemm_lds_bytes(int bits, int id);
+
+hipError_t launch_xsum(const uint16_t *x, float *xsum, int64_t M, int64_t K, int64_t Mp,
+                       hipStream_t stream);
+hipError_t launch_gemm(int bits, int tile_id, const GemmArgs &a, hipStream_t stream);
+hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N,
+                                void *out, int out_bf16, hipStream_t stream);
+hipError_t launch_fill_zero(void *out, int64_t count, int out_bf16, hipStream_t stream);
+
+struct SkinnyArgs {
+  const uint16_t *x;
+  const uint32_t *w;
+  const uint16_t *s;
+  const uint16_t *b;
+  void *out;
+  int64_t M, N, K;
+  int G;
+  int out_bf16;
+};
+// M <= 16 only.
+hipError_t launch_skinny(int bits, const SkinnyArgs &a, hipStream_t stream);
+
+hipError_t launch_dequant(int bits, const uint32_t *w, const uint16_t *s, const uint16_t *b,
+                          int64_t N, int64_t K, float *out, hipStream_t stream);
+hipError_t launch_quantize(int bits, const float *w, int64_t N, int64_t K, uint32_t *packed,
+                           uint16_t *s, uint16_t *b, int *status, hipStream_t stream);
+
+}  // namespace ql

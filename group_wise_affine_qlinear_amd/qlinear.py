@@ -1,0 +1,263 @@
+"""ctypes binding over libqlinear's C ABI (``include/qlinear.h``).
+
+Argument marshalling only: every step of the product runs in the HIP library.
+Device arguments are torch CUDA tensors (PyTorch supplies device memory and the
+stream); host helpers take numpy arrays. Each function has the name of the C
+entry point it calls. A non-zero status raises ``QLinearError``. The library is
+loaded on first use; if it is not built the call fails loudly (there is no
+fallback of any kind).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlinear.so")
+
+QL_OK, QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP, QL_ERANGE = 0, -1, -2, -3, -4, -5, -6
+QL_OUT_F32, QL_OUT_BF16 = 0, 1
+QL_PATH_AUTO, QL_PATH_SKINNY, QL_PATH_GEMM, QL_PATH_SPLITK = 0, 1, 2, 3
+
+EXPORTED = (
+    "qlinear_forward", "qlinear_forward_ex", "qlinear_workspace_bytes", "qlinear_packed_words",
+    "qlinear_pack_host", "qlinear_unpack_host", "qlinear_quantize_rtn_host", "qlinear_quantize_rtn",
+    "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
+)
+
+
+class QLinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({qlinear_status_string(status)})")
+
+
+class ql_forward_args(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("packed_q", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("biases", ctypes.c_void_p),
+        ("bits", ctypes.c_int),
+        ("group", ctypes.c_int),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("out", ctypes.c_void_p),
+        ("out_dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("path", ctypes.c_int),
+        ("split_k", ctypes.c_int),
+        ("tile", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and return libqlinear with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libqlinear.so not found at {path}; build it with "
+            "`python -m group_wise_affine_qlinear_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "qlinear_forward": ([vp, vp, vp, vp, i32, i32, i64, i64, i64, vp], i32),
+        "qlinear_forward_ex": ([ctypes.POINTER(ql_forward_args), vp], i32),
+        "qlinear_workspace_bytes": ([i32, i64, i64, i64], sz),
+        "qlinear_packed_words": ([i32, i64, i64], sz),
+        "qlinear_pack_host": ([vp, i32, i64, i64, vp], i32),
+        "qlinear_unpack_host": ([vp, i32, i64, i64, vp], i32),
+        "qlinear_quantize_rtn_host": ([vp, i32, i32, i64, i64, vp, vp, vp], i32),
+        "qlinear_quantize_rtn": ([vp, i32, i32, i64, i64, vp, vp, vp, vp, vp], i32),
+        "qlinear_dequantize": ([vp, vp, vp, i32, i32, i64, i64, vp, vp], i32),
+        "qlinear_status_string": ([i32], ctypes.c_char_p),
+        "qlinear_last_path": ([ctypes.c_char_p, sz], i32),
+        "qlinear_version": ([], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != QL_OK:
+        raise QLinearError(status, where)
+
+
+# ------------------------------------------------------------------ torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _u16(torch):
+    return (torch.int16, torch.uint16, torch.float16, torch.bfloat16)
+
+
+# ------------------------------------------------------------------ device entry points
+
+def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
+    """C ``qlinear_forward``: out[M, N] fp32 = x[M, K] (bf16) @ W_hat^T, default stream."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    G = K // group if group else 0
+    st = lib.qlinear_forward(
+        _dev_ptr(x, "x", u16, (M, K)),
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, G)),
+        _dev_ptr(biases, "biases", u16, (N, G)),
+        bits, group, M, N, K,
+        _dev_ptr(out, "out", (torch.float32,), (M, N)))
+    _check(st, "qlinear_forward")
+    return out
+
+
+def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
+                       workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0):
+    """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype and forced path."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    G = K // group if group else 0
+    a = ql_forward_args()
+    a.x = _dev_ptr(x, "x", u16, (M, K))
+    a.packed_q = _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32))
+    a.scales = _dev_ptr(scales, "scales", u16, (N, G))
+    a.biases = _dev_ptr(biases, "biases", u16, (N, G))
+    a.bits, a.group, a.M, a.N, a.K = bits, group, M, N, K
+    if out.dtype == torch.float32:
+        a.out_dtype = QL_OUT_F32
+    elif out.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        a.out_dtype = QL_OUT_BF16
+    else:
+        raise TypeError("out must be float32 or bfloat16")
+    a.out = _dev_ptr(out, "out", (out.dtype,), (M, N))
+    if workspace is not None:
+        a.workspace = _dev_ptr(workspace, "workspace", (workspace.dtype,))
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.path, a.split_k, a.tile = path, split_k, tile
+    st = lib.qlinear_forward_ex(ctypes.byref(a), _stream_handle(stream))
+    _check(st, "qlinear_forward_ex")
+    return out
+
+
+def qlinear_quantize_rtn(w, bits, group, N, K, packed_q, scales, biases, status=None, stream=None):
+    """C ``qlinear_quantize_rtn``: device load-time RTN fit + pack."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    st = lib.qlinear_quantize_rtn(
+        _dev_ptr(w, "w", (torch.float32,), (N, K)), bits, group, N, K,
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)),
+        _dev_ptr(status, "status", (torch.int32,)) if status is not None else None,
+        _stream_handle(stream))
+    _check(st, "qlinear_quantize_rtn")
+
+
+def qlinear_dequantize(packed_q, scales, biases, bits, group, N, K, w_out, stream=None):
+    """C ``qlinear_dequantize``: W_hat fp32 [N, K]."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    st = lib.qlinear_dequantize(
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)),
+        bits, group, N, K,
+        _dev_ptr(w_out, "w_out", (torch.float32,), (N, K)),
+        _stream_handle(stream))
+    _check(st, "qlinear_dequantize")
+    return w_out
+
+
+# ------------------------------------------------------------------ host entry points
+
+def qlinear_packed_words(bits, N, K) -> int:
+    return int(load_library().qlinear_packed_words(bits, N, K))
+
+
+def qlinear_workspace_bytes(bits, M, N, K) -> int:
+    return int(load_library().qlinear_workspace_bytes(bits, M, N, K))
+
+
+def qlinear_pack_host(q: np.ndarray, bits: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    n, k = q.shape
+    out = np.empty((n, k * bits // 32), dtype=np.uint32)
+    _check(load_library().qlinear_pack_host(q.ctypes.data, bits, n, k, out.ctypes.data), "qlinear_pack_host")
+    return out
+
+
+def qlinear_unpack_host(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    n = packed.shape[0]
+    out = np.empty((n, K), dtype=np.uint8)
+    _check(load_library().qlinear_unpack_host(packed.ctypes.data, bits, n, K, out.ctypes.data),
+           "qlinear_unpack_host")
+    return out
+
+
+def qlinear_quantize_rtn_host(w: np.ndarray, bits: int, group: int = 64):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    q = np.empty((n, k), dtype=np.uint8)
+    g = k // group if group else 0
+    s = np.empty((n, g), dtype=np.uint16)
+    b = np.empty((n, g), dtype=np.uint16)
+    _check(load_library().qlinear_quantize_rtn_host(w.ctypes.data, bits, group, n, k, q.ctypes.data,
+                                                    s.ctypes.data, b.ctypes.data), "qlinear_quantize_rtn_host")
+    return q, s, b
+
+
+def qlinear_status_string(status: int) -> str:
+    return load_library().qlinear_status_string(status).decode()
+
+
+def qlinear_last_path() -> str:
+    buf = ctypes.create_string_buffer(160)
+    _check(load_library().qlinear_last_path(buf, 160), "qlinear_last_path")
+    return buf.value.decode()
+
+
+def qlinear_version() -> int:
+    return int(load_library().qlinear_version())

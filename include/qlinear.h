@@ -1,0 +1,163 @@
+/*
+ * qlinear.h -- C ABI of libqlinear, an MI355X (gfx950) group-wise affine
+ * quantized linear layer.
+ *
+ *   y[m, n] = sum_k x[m, k] * W_hat[n, k]
+ *   W_hat[n, k] = scale[n, g] * q[n, k] + bias[n, g],   g = k / 64
+ *
+ * The format -- unsigned codes q of 2, 4 or 8 bits, one f16 scale and one f16
+ * bias per 64 consecutive weights of a row, i.e. half a bit of overhead per
+ * weight -- is the one described by the Ideogram-4-IQ4_M model card
+ * (aimarketly.com; opening section and the section on what "IQ4" means) and
+ * the SceneWorks/ideogram-4-mlx model card (huggingface.co; section
+ * "Versions": group-wise affine Q4/Q8, group size 64, packed).
+ *
+ * Conventions for every entry point:
+ *  - Pointers whose name ends in _host are host memory; all others are device
+ *    memory (hipMalloc'ed or torch CUDA tensors). The caller owns every buffer;
+ *    the library never frees caller memory.
+ *  - Arrays are row-major and contiguous.
+ *      x        bf16 bit patterns, [M, K]
+ *      packed_q uint32, [N, K*bits/32]; code k of a row sits in bits
+ *               [bits*(k % (32/bits)), +bits) of word k / (32/bits)
+ *               (little-endian along K; the pages say only "packed", this is
+ *               the layout this library fixes)
+ *      scales   f16 bit patterns, [N, K/64]
+ *      biases   f16 bit patterns, [N, K/64]
+ *      out      fp32 [M, N] (or bf16 with QL_OUT_BF16 in the _ex form)
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Device entry points only enqueue work and return; they never
+ *    synchronize. Errors found before launch are returned and nothing is
+ *    launched.
+ *  - Return value: QL_OK (0) or a negative ql_status. No entry point aborts,
+ *    exits or throws.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QL_OK = 0,
+  QL_EINVAL = -1,        /* bad size, null pointer, K not a multiple of 64  */
+  QL_EALIGN = -2,        /* x / out / packed_q not 16-byte aligned            */
+  QL_EUNSUPPORTED = -3,  /* bits not in {2,4,8}, group != 64, forced path
+                            that cannot serve the shape                       */
+  QL_EWORKSPACE = -4,    /* caller workspace missing or too small             */
+  QL_EHIP = -5,          /* a HIP runtime call or kernel launch failed        */
+  QL_ERANGE = -6         /* non-finite weight, or f16 overflow of scale/bias  */
+} ql_status;
+
+typedef enum { QL_OUT_F32 = 0, QL_OUT_BF16 = 1 } ql_out_dtype;
+
+typedef enum {
+  QL_PATH_AUTO = 0,      /* dispatch table decides                            */
+  QL_PATH_SKINNY = 1,    /* wavefront GEMV kernel, M <= 16                    */
+  QL_PATH_GEMM = 2,      /* fused dequant-GEMM on bf16 MFMA, no K split       */
+  QL_PATH_SPLITK = 3     /* fused dequant-GEMM with split K + ordered reduce  */
+} ql_path;
+
+/* Full-form arguments of qlinear_forward_ex. Zero-initialise, then fill. */
+typedef struct ql_forward_args {
+  const void *x;             /* bf16 [M, K]                                  */
+  const uint32_t *packed_q;  /* uint32 [N, K*bits/32]                        */
+  const void *scales;        /* f16 [N, K/group]                             */
+  const void *biases;        /* f16 [N, K/group]                             */
+  int bits;                  /* 2, 4 or 8                                    */
+  int group;                 /* 64                                           */
+  int64_t M, N, K;
+  void *out;                 /* [M, N], dtype per out_dtype                  */
+  int out_dtype;             /* ql_out_dtype                                 */
+  void *workspace;           /* device scratch, may be NULL if ws_bytes==0   */
+  size_t workspace_bytes;    /* >= qlinear_workspace_bytes(...)              */
+  int path;                  /* ql_path; QL_PATH_AUTO unless testing         */
+  int split_k;               /* 0 = auto; >0 forces the K split count        */
+  int tile;                  /* 0 = auto; >0 forces a GEMM tile id (tests)   */
+} ql_forward_args;
+
+/*
+ * y = x @ W_hat^T with W_hat defined above, fp32 out, default stream.
+ * M, N >= 0 (0 is a no-op), K >= 0 and a multiple of 64 (K == 0 writes zeros),
+ * group must be 64. Scratch memory the kernels need (per-group row sums of x
+ * and split-K partials) comes from a library-owned per-device buffer that is
+ * grown on demand with hipMalloc; calls on one device therefore must not
+ * overlap in time (use qlinear_forward_ex with your own workspace for that).
+ */
+int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales,
+                    const void *biases, int bits, int group, int64_t M, int64_t N,
+                    int64_t K, float *out);
+
+/* Same product with explicit stream, workspace, output dtype and path. If
+ * args->workspace is NULL the library-owned buffer is used as above. */
+int qlinear_forward_ex(const ql_forward_args *args, void *stream);
+
+/* Bytes of device workspace qlinear_forward_ex needs for this shape under
+ * automatic dispatch (an upper bound over all paths and splits it may pick). */
+size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K);
+
+/* Number of uint32 words of packed codes for an [N, K] weight: N*K*bits/32. */
+size_t qlinear_packed_words(int bits, int64_t N, int64_t K);
+
+/* Host packer: q_host uint8 [N, K] with values < 2^bits -> packed_host
+ * uint32 [N, K*bits/32]. QL_ERANGE if a code is out of range. */
+int qlinear_pack_host(const uint8_t *q_host, int bits, int64_t N, int64_t K,
+                      uint32_t *packed_host);
+
+/* Host unpacker, inverse of qlinear_pack_host. */
+int qlinear_unpack_host(const uint32_t *packed_host, int bits, int64_t N, int64_t K,
+                        uint8_t *q_host);
+
+/*
+ * Host min/max round-to-nearest fit (the "candidate 0" fit of the
+ * Ideogram-4-IQ4_M card's section on what "IQ4" means), per row and 64-group:
+ *   scale = f16_rne((max - min) / (2^bits - 1))   (fp32 subtract and divide)
+ *   bias  = f16_rne(min)
+ *   q     = clamp(rint_half_even((w - bias) / scale), 0, 2^bits - 1)  in fp32,
+ *           q = 0 where scale == 0.
+ * w_host fp32 [N, K] -> q_host uint8 [N, K], s16_host/b16_host f16 [N, K/64].
+ * QL_ERANGE for a non-finite weight or an f16 overflow of scale or bias.
+ */
+int qlinear_quantize_rtn_host(const float *w_host, int bits, int group, int64_t N,
+                              int64_t K, uint8_t *q_host, uint16_t *s16_host,
+                              uint16_t *b16_host);
+
+/*
+ * Device load-time quantizer: the same fit as qlinear_quantize_rtn_host,
+ * byte-identical, writing packed codes directly (no dense transient beyond w).
+ * The SceneWorks/ideogram-4-mlx card (section "Provenance & attribution")
+ * describes its packer as byte-equivalent to load-time quantization; this is
+ * that load-time path. w fp32 [N, K] -> packed_q [N, K*bits/32], scales and
+ * biases f16 [N, K/64]. Non-finite input or f16 overflow sets *status_dev
+ * (an int in device memory, may be NULL) to QL_ERANGE; it is never cleared,
+ * so zero it before the call.
+ */
+int qlinear_quantize_rtn(const float *w, int bits, int group, int64_t N, int64_t K,
+                         uint32_t *packed_q, uint16_t *scales, uint16_t *biases,
+                         int *status_dev, void *stream);
+
+/* Device dequantize (check path): W_hat fp32 [N, K], one rounding per value,
+ * bit-identical to fp32(scale)*q + fp32(bias). */
+int qlinear_dequantize(const uint32_t *packed_q, const void *scales, const void *biases,
+                       int bits, int group, int64_t N, int64_t K, float *w_out,
+                       void *stream);
+
+/* Static description of a status code. */
+const char *qlinear_status_string(int status);
+
+/* Name of the kernel/tile/split the calling thread's last forward launched,
+ * NUL-terminated into buf. Returns QL_OK or QL_EINVAL. */
+int qlinear_last_path(char *buf, size_t len);
+
+/* Library ABI version (major*100 + minor). */
+int qlinear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -22,7 +22,7 @@ What it computes (sources are the pages' titles and sections):
 * Product. y = x @ W_hat^T, x given as bf16, accumulated in float64.
 
 Readings where the pages are silent (each also listed in the design notes):
-scale = (max - min) / (2**bits - 1) in fp32; both scale and bias rounded to f16
+min and max order -0 below +0; scale = (max - min) / (2**bits - 1) in fp32; both scale and bias rounded to f16
 with round-half-even; q computed from the *stored* f16 scale and bias in fp32
 (IEEE subtract and divide), rounded half-to-even, clamped to [0, 2**bits - 1];
 a group whose f16 scale is zero gets q = 0; non-finite weights, or a scale or
@@ -122,6 +122,13 @@ def quantize_rtn(w: np.ndarray, bits: int, group: int = GROUP):
     wg = w.reshape(n, g, group)
     mn = wg.min(axis=2)
     mx = wg.max(axis=2)
+    # min/max order -0 below +0 (IEEE 754-2019 minimum/maximum), so that a
+    # group holding both zeros has a well-defined bias sign
+    zero_w = wg == 0
+    neg0 = (zero_w & np.signbit(wg)).any(axis=2)
+    pos0 = (zero_w & ~np.signbit(wg)).any(axis=2)
+    mn = np.where(mn == 0, np.where(neg0, np.float32(-0.0), np.float32(0.0)), mn).astype(np.float32)
+    mx = np.where(mx == 0, np.where(pos0, np.float32(0.0), np.float32(-0.0)), mx).astype(np.float32)
     s32 = (mx - mn) / qmax                       # fp32 subtract, fp32 divide
     s16 = f32_to_f16_bits(s32)
     b16 = f32_to_f16_bits(mn)

@@ -1,0 +1,204 @@
+"""CPU tests of libqlinear: exported symbols, host packer/quantizer byte-equal
+to the oracle, and argument validation (every failing call here is rejected
+before any HIP call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs
+from group_wise_affine_qlinear_amd import qlinear as ql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ql.LIB_PATH):
+        pytest.fail("libqlinear.so is not built (python -m group_wise_affine_qlinear_amd.build)")
+    return ql.load_library()
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "qlinear.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlinear_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_header_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ql.EXPORTED)
+    assert ql.qlinear_version() == 100
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert ql.qlinear_status_string(code) != "unknown status"
+    assert ql.qlinear_status_string(-99) == "unknown status"
+
+
+def test_sizes(lib):
+    assert ql.qlinear_packed_words(4, 4608, 4608) == 4608 * 4608 // 8
+    assert ql.qlinear_packed_words(2, 3, 64) == 3 * 4
+    assert ql.qlinear_packed_words(8, 3, 64) == 3 * 16
+    assert ql.qlinear_packed_words(3, 3, 64) == 0
+    # skinny path needs no workspace; the GEMM path needs per-group row sums of x
+    assert ql.qlinear_workspace_bytes(4, 1, 27648, 4608) == 0
+    ws = ql.qlinear_workspace_bytes(4, 4096, 4608, 4608)
+    assert ws >= 72 * 4096 * 4
+    # long K with few output tiles uses split K partials
+    assert ql.qlinear_workspace_bytes(4, 512, 4608, 53248) > 512 * 4608 * 4
+    assert ql.qlinear_workspace_bytes(4, 64, 256, 100) == 0
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_host_pack_matches_oracle(lib, bits):
+    q = inputs.random_codes(37, 512, bits, workload_id=101)
+    p = ql.qlinear_pack_host(q, bits)
+    assert np.array_equal(p, oracle.pack(q, bits))
+    assert np.array_equal(ql.qlinear_unpack_host(p, bits, 512), q)
+    hw = {"2": 0x40FFE439, "4": 0x87654321, "8": 0x44332211}
+    codes = {2: [1, 2, 3, 0, 0, 1, 2, 3, 3, 3, 3, 3, 0, 0, 0, 1], 4: [1, 2, 3, 4, 5, 6, 7, 8], 8: [17, 34, 51, 68]}
+    one = ql.qlinear_pack_host(np.array([codes[bits]], np.uint8), bits)
+    assert int(one[0, 0]) == hw[str(bits)]
+
+
+def test_host_pack_rejects_bad_code(lib):
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_pack_host(np.full((1, 8), 16, np.uint8), 4)
+    assert e.value.status == ql.QL_ERANGE
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_host_quantize_matches_oracle_random(lib, bits):
+    w = inputs.weights(64, 1024, workload_id=102)
+    qh, sh, bh = ql.qlinear_quantize_rtn_host(w, bits)
+    qo, so, bo = oracle.quantize_rtn(w, bits)
+    assert np.array_equal(sh, so) and np.array_equal(bh, bo) and np.array_equal(qh, qo)
+
+
+def adversarial_weights():
+    rows = []
+    k = np.arange(64, dtype=np.float32)
+    rows.append(-1 + 0.125 * (k % 16))                   # exact grid
+    r = np.zeros(64, np.float32); r[1] = 1.5; r[2] = 2.5 * np.float32(np.float16(0.1)); r[3] = 3.5 * np.float32(np.float16(0.1))
+    rows.append(r)                                         # exact ties
+    rows.append(np.full(64, 0.3, np.float32))             # constant group
+    rows.append(np.where(k % 2 == 0, 0.0, -0.0).astype(np.float32))  # +-0
+    rows.append((k * 1e-7).astype(np.float32))            # f16-subnormal scale
+    rows.append((k * 3e-9).astype(np.float32))            # scale underflows to 0 in f16
+    rows.append(np.linspace(-60000, 60000, 64, dtype=np.float32))  # large but in range
+    rows.append((np.arange(64) % 2 * 2 - 1).astype(np.float32) * np.float32(6.1e-5))
+    rng = np.random.default_rng(3)
+    rows.append(rng.standard_normal(64).astype(np.float32) * 1e3)
+    rows.append(rng.standard_normal(64).astype(np.float32) * 1e-3)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_host_quantize_matches_oracle_adversarial(lib, bits):
+    w = adversarial_weights()
+    qh, sh, bh = ql.qlinear_quantize_rtn_host(w, bits)
+    qo, so, bo = oracle.quantize_rtn(w, bits)
+    assert np.array_equal(sh, so) and np.array_equal(bh, bo)
+    assert np.array_equal(qh, qo)
+
+
+def test_host_f16_conversion_matches_oracle_on_bit_patterns(lib):
+    """Quantizing constant groups exposes the library's f32->f16 rounding of the bias."""
+    rng = np.random.default_rng(17)
+    bits32 = rng.integers(0, 2**32, size=4000, dtype=np.uint64).astype(np.uint32)
+    vals = bits32.view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) < 65504)]
+    extra = np.array([65504, 65519.99, 2**-24, 2**-25, 3 * 2**-26, 2**-14, 2**-14 - 2**-25,
+                      1 + 2**-11, 1 + 3 * 2**-11, -0.0], dtype=np.float32)
+    vals = np.concatenate([vals, extra])
+    w = np.repeat(vals[:, None], 64, axis=1).astype(np.float32)
+    _, _, bh = ql.qlinear_quantize_rtn_host(w, 4)
+    _, _, bo = oracle.quantize_rtn(w, 4)
+    assert np.array_equal(bh, bo)
+
+
+def test_host_quantize_errors(lib):
+    w = np.zeros((1, 64), np.float32)
+    w[0, 3] = np.inf
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_quantize_rtn_host(w, 4)
+    assert e.value.status == ql.QL_ERANGE
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0] = 1e6
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_quantize_rtn_host(w, 4)
+    assert e.value.status == ql.QL_ERANGE
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_quantize_rtn_host(np.zeros((1, 64), np.float32), 3)
+    assert e.value.status == ql.QL_EUNSUPPORTED
+    with pytest.raises(ql.QLinearError) as e:
+        ql.qlinear_quantize_rtn_host(np.zeros((1, 96), np.float32), 4)
+    assert e.value.status == ql.QL_EINVAL
+
+
+def _args(**kw):
+    a = ql.ql_forward_args()
+    base = dict(x=0x1000, packed_q=0x2000, scales=0x3000, biases=0x4000, bits=4, group=64,
+                M=8, N=8, K=64, out=0x5000, out_dtype=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=3), ql.QL_EUNSUPPORTED),
+    (dict(bits=16), ql.QL_EUNSUPPORTED),
+    (dict(group=32), ql.QL_EUNSUPPORTED),
+    (dict(K=100), ql.QL_EINVAL),
+    (dict(M=-1), ql.QL_EINVAL),
+    (dict(N=-5), ql.QL_EINVAL),
+    (dict(out=0), ql.QL_EINVAL),
+    (dict(x=0), ql.QL_EINVAL),
+    (dict(scales=0), ql.QL_EINVAL),
+    (dict(x=0x1008), ql.QL_EALIGN),
+    (dict(out=0x5004), ql.QL_EALIGN),
+    (dict(packed_q=0x2004), ql.QL_EALIGN),
+    (dict(scales=0x3001), ql.QL_EALIGN),
+    (dict(out_dtype=7), ql.QL_EINVAL),
+    (dict(path=1, M=17), ql.QL_EUNSUPPORTED),
+    (dict(path=9), ql.QL_EUNSUPPORTED),
+    (dict(path=3, K=64), ql.QL_EUNSUPPORTED),
+    (dict(M=64, N=64, K=128, workspace=0x7000, workspace_bytes=16), ql.QL_EWORKSPACE),
+    (dict(tile=99, M=64), ql.QL_EUNSUPPORTED),
+])
+def test_forward_validation_rejects_before_launch(lib, kw, status):
+    a = _args(**kw)
+    assert lib.qlinear_forward_ex(ctypes.byref(a), None) == status
+
+
+def test_forward_empty_is_noop(lib):
+    a = _args(M=0, x=0, packed_q=0, scales=0, biases=0, out=0)
+    assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_OK
+    assert ql.qlinear_last_path() == "noop"
+    a = _args(N=0, x=0, packed_q=0, scales=0, biases=0, out=0)
+    assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_OK
+
+
+def test_device_entry_points_validate_before_launch(lib):
+    assert lib.qlinear_dequantize(0x1000, 0x2000, 0x3000, 5, 64, 4, 64, 0x4000, None) == ql.QL_EUNSUPPORTED
+    assert lib.qlinear_dequantize(0x1000, 0x2000, 0x3000, 4, 64, 4, 65, 0x4000, None) == ql.QL_EINVAL
+    assert lib.qlinear_dequantize(0x1004, 0x2000, 0x3000, 4, 64, 4, 64, 0x4000, None) == ql.QL_EALIGN
+    assert lib.qlinear_dequantize(0, 0, 0, 4, 64, 0, 64, 0, None) == ql.QL_OK
+    assert lib.qlinear_quantize_rtn(0x1000, 4, 32, 4, 64, 0x2000, 0x3000, 0x4000, None, None) == ql.QL_EUNSUPPORTED
+    assert lib.qlinear_quantize_rtn(0, 4, 64, 4, 64, 0x2000, 0x3000, 0x4000, None, None) == ql.QL_EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ql, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        ql.load_library(str(tmp_path / "missing.so"))

@@ -391,3 +391,14 @@ def test_generators_are_deterministic():
     xs = inputs.activations_f32(64, 53248, workload_id=4, structure="slices")
     stds = xs.reshape(64, 13, 4096).std(axis=(0, 2))
     assert np.all((stds > 0.4) & (stds < 4.2))
+
+
+def test_signed_zero_ordering_in_min_max():
+    """-0 orders below +0: a group of +-0 gets bias -0 and scale +0."""
+    w = np.zeros((2, 64), np.float32)
+    w[0, 1::2] = -0.0
+    w[1, :] = -0.0
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    assert int(b16[0, 0]) == 0x8000 and int(s16[0, 0]) == 0x0000
+    assert int(b16[1, 0]) == 0x8000 and int(s16[1, 0]) == 0x0000
+    assert not q.any()
