@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the group-wise affine quantized linear hot path on one MI355X.
+
+One step = one pass of the path over one batch: per-group row sums of x
+(qlinear_group_sums) followed by the fused dequant-GEMM (qlinear_forward_ex),
+i.e. exactly the kernels qlinear_forward launches, at the headline workload
+M=4096 tokens, K=N=4608, 4-bit codes, group 64 (square projection of the 4608-wide
+DiT at 1024x1024). Inputs are seeded synthetic tensors already resident in HBM
+when the timed region starts; weights are quantized by the library's device RTN
+quantizer during setup.
+
+Printed: one JSON line with the whole-job throughput (TFLOP/s), the roofline of
+the dominant kernel (fused GEMM, timed live with HIP events on its stream), the
+skinny-M and split-K rows of the path as secondary measurements, and the CPU
+oracle timed on this host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qlinear TFLOP/s (M=4096,K=N=4608, Q4 g64) + % MFMA peak; GB/s skinny-M"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+WORKLOAD = dict(name="dit_square_proj_M4096_K4608_N4608_q4_g64", M=4096, K=4608, N=4608, bits=4, wid=6)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_q4_M4096_K4608_N4608_traffic.txt")
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "ql_device.h"):
+        with open(os.path.join(ROOT, "group_wise_affine_qlinear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(M, N, K, bits):
+    return N * K * bits / 8 + 4 * N * K / 64 + 2 * M * K + 4 * M * N
+
+
+def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1):
+    w = torch.from_numpy(inputs.weights(N, K, wid)).cuda()
+    sets = []
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(copies):
+        p = torch.empty((N, K * bits // 32), dtype=torch.int32, device="cuda")
+        s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+        b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+        ql.qlinear_quantize_rtn(w, bits, 64, N, K, p, s, b, status)
+        sets.append((p, s, b))
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("quantizer reported a range error")
+    del w
+    return sets
+
+
+def time_calls(torch, fn, iters, warmup):
+    """Average per-call time (ms) with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(iters):
+        fn()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def secondary_rows(torch, ql, inputs):
+    rows = {}
+    K, N = 4608, 27648
+    for M in (1, 8):
+        copies = 8  # 8 x 71.7 MB of distinct weights > 256 MB Infinity Cache
+        sets = make_weights(torch, ql, inputs, N, K, 4, 40 + (M > 1), copies)
+        x = torch.from_numpy(inputs.activations_bf16(M, K, 40 + (M > 1)).view("int16")).cuda()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        i = [0]
+
+        def fn():
+            p, s, b = sets[i[0] % copies]
+            i[0] += 1
+            ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out)
+
+        ms = time_calls(torch, fn, 64, 16)
+        by = algorithmic_bytes(M, N, K, 4)
+        gbs = by / (ms * 1e-3) / 1e9
+        rows[f"adaln_skinny_M{M}_K{K}_N{N}_q4"] = {
+            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies_rotated": copies}
+        del sets
+        log(f"skinny M={M}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+    M, K, N = 512, 53248, 4608
+    copies = 4
+    sets = make_weights(torch, ql, inputs, N, K, 4, 4, copies)
+    x = torch.from_numpy(inputs.activations_bf16(M, K, 4, "slices").view("int16")).cuda()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    i = [0]
+
+    def fn2():
+        p, s, b = sets[i[0] % copies]
+        i[0] += 1
+        ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out)
+
+    ms = time_calls(torch, fn2, 20, 5)
+    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+    rows["llm_cond_proj_M512_K53248_N4608_q4"] = {
+        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+        "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "weight_copies_rotated": copies}
+    log(f"llm_cond_proj: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
+    del sets
+    return rows
+
+
+def cpu_baseline(inputs, M, N, K, bits, wid):
+    """The oracle as it stands, timed on this host over the full headline workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    w = inputs.weights(N, K, wid)
+    q, s16, b16 = oracle.quantize_rtn(w, bits)
+    packed = oracle.pack(q, bits)
+    x = inputs.activations_bf16(M, K, wid)
+    del w, q
+    _, t = oracle.timed_forward(x, packed, s16, b16, bits, K)
+    tf = 2 * M * N * K / t["total_s"] / 1e12
+    return {"value": round(tf, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full workload M={M} K={K} N={N} q{bits}, one run: unpack+dequantize "
+                      f"{t['dequant_s']:.2f} s + fp64 GEMM {t['gemm_s']:.2f} s"}
+
+
+def load_traffic(src_hash):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != src_hash:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--profile", choices=["none", "step", "copy"], default="none",
+                    help="short run for rocprofv3: 'step' = the timed step only, 'copy' = a plain copy of known size")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU layout is "
+                                   "a design note, so --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from group_wise_affine_qlinear_amd import inputs
+    from group_wise_affine_qlinear_amd import qlinear as ql
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    ql.load_library()
+
+    if args.profile == "copy":
+        n = 256 * 1024 * 1024 // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy kernel: {n * 4} bytes read and written per launch, 5 launches")
+        return
+
+    M, K, N, bits = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"], WORKLOAD["bits"]
+    log(f"setup {WORKLOAD['name']}")
+    (p, s, b), = make_weights(torch, ql, inputs, N, K, bits, WORKLOAD["wid"])
+    x = torch.from_numpy(inputs.activations_bf16(M, K, WORKLOAD["wid"]).view("int16")).cuda()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    xsum = torch.empty((K // 64, ql.qlinear_group_sums_ld(M)), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    steps, warmup = args.steps, args.warmup
+    if args.profile == "step":
+        steps, warmup = 5, 2
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        ql.qlinear_group_sums(x, M, K, xsum, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, xsum=xsum, stream=stream)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    path = ql.qlinear_last_path()
+    if args.profile == "step":
+        log(f"profiled {steps} steps, path {path}")
+        return
+
+    ms_step = (t1 - t0) * 1e3 / steps
+    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    sums_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    flop = 2.0 * M * N * K
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (gemm_ms * 1e-3) / 1e12
+    log(f"step {ms_step*1e3:.1f} us (group sums {sums_ms*1e3:.1f} us, gemm {gemm_ms*1e3:.1f} us) -> {value:.1f} TFLOP/s")
+
+    secondary = {} if args.no_secondary else secondary_rows(torch, ql, inputs)
+    src_hash = gemm_source_hash()
+    traffic = load_traffic(src_hash)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD["name"], "M": M, "K": K, "N": N, "bits": bits, "group": 64,
+                   "path": path, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fused dequant-GEMM", "kernel_us": round(gemm_ms * 1e3, 2),
+                     "group_sums_us": round(sums_ms * 1e3, 2), "kernel_source_sha": src_hash},
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        rec["cpu_baseline"] = cpu_baseline(inputs, M, N, K, bits, WORKLOAD["wid"])
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

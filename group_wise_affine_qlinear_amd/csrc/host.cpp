@@ -219,6 +219,10 @@ int validate_forward(const ql_forward_args *a) {
   if (!aligned16(a->x) || !aligned16(a->packed_q)) return QL_EALIGN;
   if ((reinterpret_cast<uintptr_t>(a->scales) & 1u) || (reinterpret_cast<uintptr_t>(a->biases) & 1u))
     return QL_EALIGN;
+  if (a->xsum) {
+    if (a->ld_xsum < round_up(a->M, 256) || a->ld_xsum % 4) return QL_EINVAL;
+    if (!aligned16(a->xsum)) return QL_EALIGN;
+  }
   return QL_OK;
 }
 
@@ -293,11 +297,15 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     st = get_owned_workspace(need, &ws);
     if (st != QL_OK) return st;
   }
-  const int64_t Mp = round_up(a->M, 256);
+  int64_t Mp = round_up(a->M, 256);
   float *xsum = static_cast<float *>(ws);
   float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up((int64_t)p.ws_xsum, 256));
-  if (ql::launch_xsum(static_cast<const uint16_t *>(a->x), xsum, a->M, a->K, Mp, stream) != hipSuccess)
+  if (a->xsum) {
+    xsum = const_cast<float *>(a->xsum);
+    Mp = a->ld_xsum;
+  } else if (ql::launch_xsum(static_cast<const uint16_t *>(a->x), xsum, a->M, a->K, Mp, stream) != hipSuccess) {
     return QL_EHIP;
+  }
   ql::GemmArgs g{static_cast<const uint16_t *>(a->x),
                  a->packed_q,
                  static_cast<const uint16_t *>(a->scales),
@@ -319,6 +327,21 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
       return QL_EHIP;
   }
   return QL_OK;
+}
+
+QL_API int64_t qlinear_group_sums_ld(int64_t M) { return M <= 0 ? 0 : round_up(M, 256); }
+
+QL_API int qlinear_group_sums(const void *x, int64_t M, int64_t K, float *xsum, int64_t ld_xsum, void *stream) {
+  if (M < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (M == 0 || K == 0) return QL_OK;
+  if (!x || !xsum) return QL_EINVAL;
+  if (ld_xsum < round_up(M, 256) || ld_xsum % 4) return QL_EINVAL;
+  if (!aligned16(x) || !aligned16(xsum)) return QL_EALIGN;
+  set_last_path("group_sums");
+  return ql::launch_xsum(static_cast<const uint16_t *>(x), xsum, M, K, ld_xsum,
+                         reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
 }
 
 QL_API int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales, const void *biases,

@@ -25,6 +25,7 @@ EXPORTED = (
     "qlinear_forward", "qlinear_forward_ex", "qlinear_workspace_bytes", "qlinear_packed_words",
     "qlinear_pack_host", "qlinear_unpack_host", "qlinear_quantize_rtn_host", "qlinear_quantize_rtn",
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
+    "qlinear_group_sums", "qlinear_group_sums_ld",
 )
 
 
@@ -52,6 +53,8 @@ class ql_forward_args(ctypes.Structure):
         ("path", ctypes.c_int),
         ("split_k", ctypes.c_int),
         ("tile", ctypes.c_int),
+        ("xsum", ctypes.c_void_p),
+        ("ld_xsum", ctypes.c_int64),
     ]
 
 
@@ -82,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_status_string": ([i32], ctypes.c_char_p),
         "qlinear_last_path": ([ctypes.c_char_p, sz], i32),
         "qlinear_version": ([], i32),
+        "qlinear_group_sums": ([vp, i64, i64, vp, i64, vp], i32),
+        "qlinear_group_sums_ld": ([i64], i64),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -151,7 +156,8 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
 
 
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
-                       workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0):
+                       workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
+                       xsum=None):
     """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype and forced path."""
     torch = _torch()
     u16 = _u16(torch)
@@ -174,9 +180,32 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
         a.workspace = _dev_ptr(workspace, "workspace", (workspace.dtype,))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.path, a.split_k, a.tile = path, split_k, tile
+    if xsum is not None:
+        a.xsum = _dev_ptr(xsum, "xsum", (torch.float32,))
+        a.ld_xsum = xsum.shape[1]
+        if xsum.dim() != 2 or xsum.shape[0] != K // group:
+            raise ValueError("xsum must be [K/64, ld_xsum]")
     st = lib.qlinear_forward_ex(ctypes.byref(a), _stream_handle(stream))
     _check(st, "qlinear_forward_ex")
     return out
+
+
+def qlinear_group_sums_ld(M) -> int:
+    return int(load_library().qlinear_group_sums_ld(M))
+
+
+def qlinear_group_sums(x, M, K, xsum=None, stream=None):
+    """C ``qlinear_group_sums``: per-group row sums of x, [K/64, ld] fp32 (allocated if None)."""
+    torch = _torch()
+    lib = load_library()
+    ld = qlinear_group_sums_ld(M)
+    if xsum is None:
+        xsum = torch.empty((K // 64, ld), dtype=torch.float32, device=x.device)
+    st = lib.qlinear_group_sums(_dev_ptr(x, "x", _u16(torch), (M, K)), M, K,
+                                _dev_ptr(xsum, "xsum", (torch.float32,)), xsum.shape[1],
+                                _stream_handle(stream))
+    _check(st, "qlinear_group_sums")
+    return xsum
 
 
 def qlinear_quantize_rtn(w, bits, group, N, K, packed_q, scales, biases, status=None, stream=None):

@@ -78,6 +78,10 @@ typedef struct ql_forward_args {
   int path;                  /* ql_path; QL_PATH_AUTO unless testing         */
   int split_k;               /* 0 = auto; >0 forces the K split count        */
   int tile;                  /* 0 = auto; >0 forces a GEMM tile id (tests)   */
+  const float *xsum;         /* optional: per-group row sums of x from
+                                qlinear_group_sums ([K/64, ld_xsum] fp32);
+                                NULL = computed inside the call             */
+  int64_t ld_xsum;           /* row pitch of xsum, >= qlinear_group_sums_ld(M) */
 } ql_forward_args;
 
 /*
@@ -95,6 +99,22 @@ int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales,
 /* Same product with explicit stream, workspace, output dtype and path. If
  * args->workspace is NULL the library-owned buffer is used as above. */
 int qlinear_forward_ex(const ql_forward_args *args, void *stream);
+
+/*
+ * Per-group row sums of the activations, xsum[g, m] = sum_{k=64g}^{64g+63}
+ * x[m, k] in fp32, written to xsum with row pitch ld_xsum (layout
+ * [K/64, ld_xsum]). The fused kernels fold each group's bias in as
+ * bias[n, g] * xsum[m, g] (the affine form W_hat = s*q + b of the
+ * Ideogram-4-IQ4_M card's section on what "IQ4" means, summed per group).
+ * Several projections of the same x (e.g. Q/K/V, gate/up) can share one call
+ * by passing the result in ql_forward_args.xsum. ld_xsum must be at least
+ * qlinear_group_sums_ld(M); the buffer holds (K/64) * ld_xsum floats.
+ */
+int qlinear_group_sums(const void *x, int64_t M, int64_t K, float *xsum, int64_t ld_xsum,
+                       void *stream);
+
+/* Minimum row pitch (floats) of a group-sum buffer for M rows. */
+int64_t qlinear_group_sums_ld(int64_t M);
 
 /* Bytes of device workspace qlinear_forward_ex needs for this shape under
  * automatic dispatch (an upper bound over all paths and splits it may pick). */
