@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlinear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["host.cpp", "gemm.hip", "skinny.hip", "misc.hip"]
+SOURCES = ["host.cpp", "gemm.hip", "skinny.hip", "misc.hip", "layout.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -25,6 +25,8 @@ COMMON_FLAGS = [
     # packed-fp32 VALU instructions stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # MFMA results in VGPRs: the per-group fp32 epilogue reads them with VALU ops
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -352,6 +352,8 @@ const TileInfo *gemm_tile(int id) {
   return nullptr;
 }
 
+bool gemm_tile_supports_tiled(int id) { (void)id; return false; }
+
 int gemm_tile_count() { return (int)(sizeof(kTiles) / sizeof(kTiles[0])); }
 
 size_t gemm_lds_bytes(int bits, int id) {

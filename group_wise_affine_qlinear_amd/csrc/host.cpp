@@ -211,14 +211,19 @@ int validate_forward(const ql_forward_args *a) {
   if (a->M < 0 || a->N < 0 || a->K < 0 || a->K % kGroup) return QL_EINVAL;
   if (a->M > (1LL << 31) - 1 || a->N > (1LL << 31) - 1 || a->K > (1LL << 30)) return QL_EINVAL;
   if (a->out_dtype != QL_OUT_F32 && a->out_dtype != QL_OUT_BF16) return QL_EINVAL;
+  if (a->layout != QL_LAYOUT_CANONICAL && a->layout != QL_LAYOUT_TILED) return QL_EINVAL;
   if (a->M == 0 || a->N == 0) return QL_OK;
   if (!a->out) return QL_EINVAL;
   if (!aligned16(a->out)) return QL_EALIGN;
   if (a->K == 0) return QL_OK;
-  if (!a->x || !a->packed_q || !a->scales || !a->biases) return QL_EINVAL;
+  const bool tiled = a->layout == QL_LAYOUT_TILED;
+  if (!a->x || !a->packed_q || !a->scales || (!tiled && !a->biases)) return QL_EINVAL;
   if (!aligned16(a->x) || !aligned16(a->packed_q)) return QL_EALIGN;
-  if ((reinterpret_cast<uintptr_t>(a->scales) & 1u) || (reinterpret_cast<uintptr_t>(a->biases) & 1u))
+  if (tiled) {
+    if (reinterpret_cast<uintptr_t>(a->scales) & 3u) return QL_EALIGN;
+  } else if ((reinterpret_cast<uintptr_t>(a->scales) & 1u) || (reinterpret_cast<uintptr_t>(a->biases) & 1u)) {
     return QL_EALIGN;
+  }
   if (a->xsum) {
     if (a->ld_xsum < round_up(a->M, 256) || a->ld_xsum % 4) return QL_EINVAL;
     if (!aligned16(a->xsum)) return QL_EALIGN;
@@ -281,13 +286,18 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   const int out_bf16 = a->out_dtype == QL_OUT_BF16;
   char buf[160];
   if (p.path == QL_PATH_SKINNY) {
-    ql::SkinnyArgs s{static_cast<const uint16_t *>(a->x), a->packed_q,
-                     static_cast<const uint16_t *>(a->scales), static_cast<const uint16_t *>(a->biases),
-                     a->out, a->M, a->N, a->K, G, out_bf16};
-    std::snprintf(buf, sizeof(buf), "skinny_b%d_m%s", a->bits, a->M <= 8 ? "8" : "16");
+    const bool tiled = a->layout == QL_LAYOUT_TILED;
+    ql::SkinnyArgs s{static_cast<const uint16_t *>(a->x),
+                     a->packed_q,
+                     tiled ? nullptr : static_cast<const uint16_t *>(a->scales),
+                     tiled ? nullptr : static_cast<const uint16_t *>(a->biases),
+                     tiled ? static_cast<const uint32_t *>(a->scales) : nullptr,
+                     a->out, a->M, a->N, a->K, G, out_bf16, tiled ? 1 : 0};
+    std::snprintf(buf, sizeof(buf), "skinny_b%d_m%lld_%s", a->bits, (long long)a->M, tiled ? "tiled" : "canonical");
     set_last_path(buf);
     return ql::launch_skinny(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;
   }
+  if (a->layout == QL_LAYOUT_TILED && !ql::gemm_tile_supports_tiled(p.tile)) return QL_EUNSUPPORTED;
   const size_t need = plan_ws(p);
   void *ws = a->workspace;
   if (ws) {
@@ -450,6 +460,45 @@ QL_API int qlinear_quantize_rtn(const float *w, int bits, int group, int64_t N, 
   set_last_path("quantize_rtn");
   return ql::launch_quantize(bits, w, N, K, packed_q, scales, biases, status_dev,
                              reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
+QL_API size_t qlinear_tiled_words(int bits, int64_t N, int64_t K) {
+  if (!bits_ok(bits) || N < 0 || K < 0 || K % kGroup) return 0;
+  return (size_t)round_up(N, 32) * (size_t)K * (size_t)bits / 32u;
+}
+
+QL_API size_t qlinear_tiled_sb_words(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || K % kGroup) return 0;
+  return (size_t)round_up(N, 32) * (size_t)(K / kGroup);
+}
+
+QL_API int qlinear_repack(const uint32_t *packed_q, const void *scales, const void *biases, int bits, int group,
+                          int64_t N, int64_t K, uint32_t *tiled_q, uint32_t *tiled_sb, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!packed_q || !scales || !biases || !tiled_q || !tiled_sb) return QL_EINVAL;
+  if (!aligned16(packed_q) || !aligned16(tiled_q) || (reinterpret_cast<uintptr_t>(tiled_sb) & 3u)) return QL_EALIGN;
+  set_last_path("repack");
+  return ql::launch_repack(bits, packed_q, static_cast<const uint16_t *>(scales),
+                           static_cast<const uint16_t *>(biases), N, K, tiled_q, tiled_sb,
+                           reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
+QL_API int qlinear_unrepack(const uint32_t *tiled_q, const uint32_t *tiled_sb, int bits, int group, int64_t N,
+                            int64_t K, uint32_t *packed_q, void *scales, void *biases, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!packed_q || !scales || !biases || !tiled_q || !tiled_sb) return QL_EINVAL;
+  if (!aligned16(packed_q) || !aligned16(tiled_q) || (reinterpret_cast<uintptr_t>(tiled_sb) & 3u)) return QL_EALIGN;
+  set_last_path("unrepack");
+  return ql::launch_unrepack(bits, tiled_q, tiled_sb, N, K, packed_q, static_cast<uint16_t *>(scales),
+                             static_cast<uint16_t *>(biases), reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? QL_OK
              : QL_EHIP;
 }

@@ -1,0 +1,149 @@
+// Tiled weight layout (QL_LAYOUT_TILED) and the repack / unrepack kernels.
+//
+// The canonical layout stores each output row's codes contiguously, so a wave
+// that works on 32 columns touches 32 rows x 32 bytes per group: partial cache
+// lines, which caps streaming reads well below HBM bandwidth. The tiled layout
+// stores, for every strip of 32 output columns and every 64-wide K group, one
+// contiguous block in the lane order of the kernels:
+//
+//   4-bit: 1 KB   = [h 2][col 32][4 words]   words t: codes 32h+8t .. +7
+//   8-bit: 2 KB   = [part 2][h 2][col 32][4 words]  part p: codes 32h+16p .. +15
+//   2-bit: 512 B  = [h 2][col 32][2 words]   words t: codes 32h+16t .. +15
+//
+// so lane l = 32h + col of a wave reads its 16 (or 8) bytes at l*16 and one
+// load instruction covers whole cache lines. Blocks are ordered [strip][group].
+// Inside a word, 2- and 4-bit codes use a pair order: code 2p sits in the low
+// half and code 2p+1 in the high half at the same bit offset (4-bit: bits
+// 4p and 16+4p; 2-bit: bits 2p and 16+2p), so a shift and one AND-OR give a
+// pair of bf16 operands. 8-bit words keep little-endian byte order.
+// Scale and bias become one uint32 per (strip, group, column): s | b << 16,
+// ordered [strip][group][col]. Columns past N in the last strip are zero.
+#include "ql_device.h"
+#include "ql_kernels.h"
+
+namespace ql {
+
+namespace {
+
+// Canonical word(s) of 8 codes -> pair-order word, 4-bit: c_i at bits 4i ->
+// c_{2p} at 4p, c_{2p+1} at 16+4p.
+__device__ __forceinline__ uint32_t to_pair_b4(uint32_t w) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    r |= ((w >> (8 * p)) & 0xFu) << (4 * p);
+    r |= ((w >> (8 * p + 4)) & 0xFu) << (16 + 4 * p);
+  }
+  return r;
+}
+__device__ __forceinline__ uint32_t from_pair_b4(uint32_t r) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    w |= ((r >> (4 * p)) & 0xFu) << (8 * p);
+    w |= ((r >> (16 + 4 * p)) & 0xFu) << (8 * p + 4);
+  }
+  return w;
+}
+// 2-bit: 16 codes, c_i at bits 2i -> c_{2p} at 2p, c_{2p+1} at 16+2p.
+__device__ __forceinline__ uint32_t to_pair_b2(uint32_t w) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    r |= ((w >> (4 * p)) & 0x3u) << (2 * p);
+    r |= ((w >> (4 * p + 2)) & 0x3u) << (16 + 2 * p);
+  }
+  return r;
+}
+__device__ __forceinline__ uint32_t from_pair_b2(uint32_t r) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    w |= ((r >> (2 * p)) & 0x3u) << (4 * p);
+    w |= ((r >> (16 + 2 * p)) & 0x3u) << (4 * p + 2);
+  }
+  return w;
+}
+
+// One thread per (strip, group, column): moves that column's codes of the group
+// (2*BITS words) and its scale/bias between the layouts.
+template <int BITS, bool TO_TILED>
+__global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32_t *dst,
+                                                     const uint16_t *s, const uint16_t *b,
+                                                     uint32_t *sb, uint16_t *s_out,
+                                                     uint16_t *b_out, int64_t N, int64_t K) {
+  constexpr int WPG = 2 * BITS;  // words of one column per group
+  const int64_t G = K / 64;
+  const int64_t N32 = (N + 31) / 32;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N32 * G * 32) return;
+  const int col = (int)(idx % 32);
+  const int64_t g = (idx / 32) % G;
+  const int64_t strip = idx / (32 * G);
+  const int64_t n = strip * 32 + col;
+  const bool real = n < N;
+  uint32_t *tile = TO_TILED ? dst : const_cast<uint32_t *>(src);
+  uint32_t *blk = tile + (strip * G + g) * (32 * WPG);
+  // tiled position of canonical word j (0..WPG-1) of this column
+  auto tpos = [&](int j) -> int64_t {
+    if (BITS == 4) return (j >> 2) * 128 + col * 4 + (j & 3);          // h = j/4, t = j%4
+    if (BITS == 8) return ((j >> 2) & 1) * 256 + (j >> 3) * 128 + col * 4 + (j & 3);  // h = j/8, part = (j/4)%2
+    return (j >> 1) * 64 + col * 2 + (j & 1);                            // 2-bit: h = j/2, t = j%2
+  };
+  if (TO_TILED) {
+    const uint32_t *crow = src + n * (K * BITS / 32) + g * WPG;
+#pragma unroll
+    for (int j = 0; j < WPG; ++j) {
+      uint32_t w = real ? crow[j] : 0u;
+      if (BITS == 4) w = to_pair_b4(w);
+      if (BITS == 2) w = to_pair_b2(w);
+      blk[tpos(j)] = w;
+    }
+    sb[(strip * G + g) * 32 + col] = real ? ((uint32_t)s[n * G + g] | ((uint32_t)b[n * G + g] << 16)) : 0u;
+  } else {
+    if (!real) return;
+    uint32_t *crow = dst + n * (K * BITS / 32) + g * WPG;
+#pragma unroll
+    for (int j = 0; j < WPG; ++j) {
+      uint32_t w = blk[tpos(j)];
+      if (BITS == 4) w = from_pair_b4(w);
+      if (BITS == 2) w = from_pair_b2(w);
+      crow[j] = w;
+    }
+    const uint32_t v = sb[(strip * G + g) * 32 + col];
+    s_out[n * G + g] = (uint16_t)(v & 0xFFFFu);
+    b_out[n * G + g] = (uint16_t)(v >> 16);
+  }
+}
+
+template <int BITS, bool TO_TILED>
+hipError_t repack_bits(const uint32_t *src, uint32_t *dst, const uint16_t *s, const uint16_t *b,
+                       uint32_t *sb, uint16_t *s_out, uint16_t *b_out, int64_t N, int64_t K,
+                       hipStream_t stream) {
+  const int64_t threads = ((N + 31) / 32) * (K / 64) * 32;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((repack_kernel<BITS, TO_TILED>), dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, s,
+                     b, sb, s_out, b_out, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_repack(int bits, const uint32_t *canon, const uint16_t *s, const uint16_t *b, int64_t N,
+                         int64_t K, uint32_t *tiled, uint32_t *sb, hipStream_t stream) {
+  if (bits == 4) return repack_bits<4, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, stream);
+  if (bits == 8) return repack_bits<8, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, stream);
+  if (bits == 2) return repack_bits<2, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, int64_t N, int64_t K,
+                           uint32_t *canon, uint16_t *s, uint16_t *b, hipStream_t stream) {
+  uint32_t *sbm = const_cast<uint32_t *>(sb);
+  if (bits == 4) return repack_bits<4, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, stream);
+  if (bits == 8) return repack_bits<8, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, stream);
+  if (bits == 2) return repack_bits<2, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ql

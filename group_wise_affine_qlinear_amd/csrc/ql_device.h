@@ -28,6 +28,14 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// (a & mask) | bits in one v_and_or_b32 (the compiler splits it into two ops
+// when both constants would need the scalar bus). Pure ALU, no memory access.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(bits));
+  return r;
+}
+
 // 4-bit: word w holds codes c0..c7 (nibble i = code i). Returns four bf16
 // pairs (c0,c1),(c2,c3),(c4,c5),(c6,c7) as 128 + code.
 __device__ __forceinline__ u32x4 unpack8_b4(uint32_t w) {
@@ -36,10 +44,11 @@ __device__ __forceinline__ u32x4 unpack8_b4(uint32_t w) {
   // byte p of w holds (c_{2p} low nibble, c_{2p+1} high nibble); byte p of t
   // holds c_{2p+1} in its low nibble. Select w.byte_p -> byte 0, t.byte_p ->
   // byte 2, zero bytes 1 and 3, then keep the low nibble of each half.
-  r[0] = (perm(t, w, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
-  r[1] = (perm(t, w, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
-  r[2] = (perm(t, w, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
-  r[3] = (perm(t, w, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
+  const uint32_t hi = 0x43004300u;
+  r[0] = and_or(perm(t, w, 0x0C040C00u), 0x000F000Fu, hi);
+  r[1] = and_or(perm(t, w, 0x0C050C01u), 0x000F000Fu, hi);
+  r[2] = and_or(perm(t, w, 0x0C060C02u), 0x000F000Fu, hi);
+  r[3] = and_or(perm(t, w, 0x0C070C03u), 0x000F000Fu, hi);
   return r;
 }
 
@@ -50,10 +59,11 @@ __device__ __forceinline__ u32x4 unpack8_b2(uint32_t w, int half) {
   const uint32_t v2 = v >> 2, v4 = v >> 4, v6 = v >> 6;
   u32x4 r;
   // byte b of v holds codes 4b..4b+3 at bits 0,2,4,6.
-  r[0] = (perm(v2, v, 0x0C040C00u) & 0x00030003u) | 0x43004300u;  // c0, c1
-  r[1] = (perm(v6, v4, 0x0C040C00u) & 0x00030003u) | 0x43004300u; // c2, c3
-  r[2] = (perm(v2, v, 0x0C050C01u) & 0x00030003u) | 0x43004300u;  // c4, c5
-  r[3] = (perm(v6, v4, 0x0C050C01u) & 0x00030003u) | 0x43004300u; // c6, c7
+  const uint32_t hi = 0x43004300u;
+  r[0] = and_or(perm(v2, v, 0x0C040C00u), 0x00030003u, hi);   // c0, c1
+  r[1] = and_or(perm(v6, v4, 0x0C040C00u), 0x00030003u, hi);  // c2, c3
+  r[2] = and_or(perm(v2, v, 0x0C050C01u), 0x00030003u, hi);   // c4, c5
+  r[3] = and_or(perm(v6, v4, 0x0C050C01u), 0x00030003u, hi);  // c6, c7
   return r;
 }
 
@@ -71,6 +81,32 @@ __device__ __forceinline__ u32x4 unpack8_b8(uint32_t w0, uint32_t w1) {
   r[1] = perm(__float_as_uint(a3), __float_as_uint(a2), 0x07060302u);
   r[2] = perm(__float_as_uint(b1), __float_as_uint(b0), 0x07060302u);
   r[3] = perm(__float_as_uint(b3), __float_as_uint(b2), 0x07060302u);
+  return r;
+}
+
+// Tiled layout (pair order, see layout.hip), 4-bit: word w holds code 2p in
+// bits [4p, 4p+4) and code 2p+1 in bits [16+4p, 16+4p+4). Pair p is one shift
+// and one AND-OR: four bf16 pairs as 128 + code.
+__device__ __forceinline__ u32x4 unpack8_b4_pair(uint32_t w) {
+  const uint32_t hi = 0x43004300u;
+  u32x4 r;
+  r[0] = and_or(w, 0x000F000Fu, hi);
+  r[1] = and_or(w >> 4, 0x000F000Fu, hi);
+  r[2] = and_or(w >> 8, 0x000F000Fu, hi);
+  r[3] = and_or(w >> 12, 0x000F000Fu, hi);
+  return r;
+}
+
+// Tiled layout, 2-bit: word w holds code 2p in bits [2p, 2p+2) and code 2p+1
+// in bits [16+2p, 16+2p+2), p = 0..7; `half` selects pairs 4*half .. 4*half+3.
+__device__ __forceinline__ u32x4 unpack8_b2_pair(uint32_t w, int half) {
+  const uint32_t hi = 0x43004300u;
+  const uint32_t v = half ? (w >> 8) : w;
+  u32x4 r;
+  r[0] = and_or(v, 0x00030003u, hi);
+  r[1] = and_or(v >> 2, 0x00030003u, hi);
+  r[2] = and_or(v >> 4, 0x00030003u, hi);
+  r[3] = and_or(v >> 6, 0x00030003u, hi);
   return r;
 }
 

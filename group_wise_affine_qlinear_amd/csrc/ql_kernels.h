@@ -29,6 +29,7 @@ struct TileInfo {
 
 // GEMM tile configurations compiled into the library (id >= 1).
 const TileInfo *gemm_tile(int id);
+bool gemm_tile_supports_tiled(int id);
 int gemm_tile_count();
 size_t gemm_lds_bytes(int bits, int id);
 
@@ -41,16 +42,24 @@ hipError_t launch_fill_zero(void *out, int64_t count, int out_bf16, hipStream_t 
 
 struct SkinnyArgs {
   const uint16_t *x;
-  const uint32_t *w;
-  const uint16_t *s;
-  const uint16_t *b;
+  const uint32_t *w;      // canonical codes, or tiled codes when tiled != 0
+  const uint16_t *s;      // canonical scales (unused when tiled)
+  const uint16_t *b;      // canonical biases (unused when tiled)
+  const uint32_t *sb;     // tiled scale|bias words (tiled only)
   void *out;
   int64_t M, N, K;
   int G;
   int out_bf16;
+  int tiled;
 };
 // M <= 16 only.
 hipError_t launch_skinny(int bits, const SkinnyArgs &a, hipStream_t stream);
+
+// Tiled layout (see layout.hip): codes [N32][G][32 * 2*bits words], scale|bias [N32][G][32].
+hipError_t launch_repack(int bits, const uint32_t *canon, const uint16_t *s, const uint16_t *b, int64_t N,
+                         int64_t K, uint32_t *tiled, uint32_t *sb, hipStream_t stream);
+hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, int64_t N, int64_t K,
+                           uint32_t *canon, uint16_t *s, uint16_t *b, hipStream_t stream);
 
 hipError_t launch_dequant(int bits, const uint32_t *w, const uint16_t *s, const uint16_t *b,
                           int64_t N, int64_t K, float *out, hipStream_t stream);

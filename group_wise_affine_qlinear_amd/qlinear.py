@@ -20,12 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libqlinear.so")
 QL_OK, QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP, QL_ERANGE = 0, -1, -2, -3, -4, -5, -6
 QL_OUT_F32, QL_OUT_BF16 = 0, 1
 QL_PATH_AUTO, QL_PATH_SKINNY, QL_PATH_GEMM, QL_PATH_SPLITK = 0, 1, 2, 3
+QL_LAYOUT_CANONICAL, QL_LAYOUT_TILED = 0, 1
 
 EXPORTED = (
     "qlinear_forward", "qlinear_forward_ex", "qlinear_workspace_bytes", "qlinear_packed_words",
     "qlinear_pack_host", "qlinear_unpack_host", "qlinear_quantize_rtn_host", "qlinear_quantize_rtn",
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
-    "qlinear_group_sums", "qlinear_group_sums_ld",
+    "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
+    "qlinear_repack", "qlinear_unrepack",
 )
 
 
@@ -55,6 +57,7 @@ class ql_forward_args(ctypes.Structure):
         ("tile", ctypes.c_int),
         ("xsum", ctypes.c_void_p),
         ("ld_xsum", ctypes.c_int64),
+        ("layout", ctypes.c_int),
     ]
 
 
@@ -87,6 +90,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_version": ([], i32),
         "qlinear_group_sums": ([vp, i64, i64, vp, i64, vp], i32),
         "qlinear_group_sums_ld": ([i64], i64),
+        "qlinear_tiled_words": ([i32, i64, i64], sz),
+        "qlinear_tiled_sb_words": ([i64, i64], sz),
+        "qlinear_repack": ([vp, vp, vp, i32, i32, i64, i64, vp, vp, vp], i32),
+        "qlinear_unrepack": ([vp, vp, i32, i32, i64, i64, vp, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -157,17 +164,27 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
 
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
                        workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
-                       xsum=None):
-    """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype and forced path."""
+                       xsum=None, layout=QL_LAYOUT_CANONICAL):
+    """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout and forced path.
+
+    With ``layout=QL_LAYOUT_TILED``, ``packed_q`` and ``scales`` are the outputs of
+    ``qlinear_repack`` (tiled codes, tiled scale|bias words) and ``biases`` is ignored.
+    """
     torch = _torch()
     u16 = _u16(torch)
     lib = load_library()
     G = K // group if group else 0
     a = ql_forward_args()
     a.x = _dev_ptr(x, "x", u16, (M, K))
-    a.packed_q = _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32))
-    a.scales = _dev_ptr(scales, "scales", u16, (N, G))
-    a.biases = _dev_ptr(biases, "biases", u16, (N, G))
+    a.layout = layout
+    if layout == QL_LAYOUT_TILED:
+        a.packed_q = _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (qlinear_tiled_words(bits, N, K),))
+        a.scales = _dev_ptr(scales, "scales", (torch.int32, torch.uint32), (qlinear_tiled_sb_words(N, K),))
+        a.biases = None
+    else:
+        a.packed_q = _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32))
+        a.scales = _dev_ptr(scales, "scales", u16, (N, G))
+        a.biases = _dev_ptr(biases, "biases", u16, (N, G))
     a.bits, a.group, a.M, a.N, a.K = bits, group, M, N, K
     if out.dtype == torch.float32:
         a.out_dtype = QL_OUT_F32
@@ -206,6 +223,51 @@ def qlinear_group_sums(x, M, K, xsum=None, stream=None):
                                 _stream_handle(stream))
     _check(st, "qlinear_group_sums")
     return xsum
+
+
+def qlinear_tiled_words(bits, N, K) -> int:
+    return int(load_library().qlinear_tiled_words(bits, N, K))
+
+
+def qlinear_tiled_sb_words(N, K) -> int:
+    return int(load_library().qlinear_tiled_sb_words(N, K))
+
+
+def qlinear_repack(packed_q, scales, biases, bits, group, N, K, tiled_q=None, tiled_sb=None, stream=None):
+    """C ``qlinear_repack``: canonical -> tiled; returns (tiled_q, tiled_sb) int32 tensors."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    dev = packed_q.device
+    if tiled_q is None:
+        tiled_q = torch.empty(qlinear_tiled_words(bits, N, K), dtype=torch.int32, device=dev)
+    if tiled_sb is None:
+        tiled_sb = torch.empty(qlinear_tiled_sb_words(N, K), dtype=torch.int32, device=dev)
+    st = lib.qlinear_repack(
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)), bits, group, N, K,
+        _dev_ptr(tiled_q, "tiled_q", (torch.int32, torch.uint32), (qlinear_tiled_words(bits, N, K),)),
+        _dev_ptr(tiled_sb, "tiled_sb", (torch.int32, torch.uint32), (qlinear_tiled_sb_words(N, K),)),
+        _stream_handle(stream))
+    _check(st, "qlinear_repack")
+    return tiled_q, tiled_sb
+
+
+def qlinear_unrepack(tiled_q, tiled_sb, bits, group, N, K, packed_q, scales, biases, stream=None):
+    """C ``qlinear_unrepack``: tiled -> canonical into the given tensors."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    st = lib.qlinear_unrepack(
+        _dev_ptr(tiled_q, "tiled_q", (torch.int32, torch.uint32), (qlinear_tiled_words(bits, N, K),)),
+        _dev_ptr(tiled_sb, "tiled_sb", (torch.int32, torch.uint32), (qlinear_tiled_sb_words(N, K),)),
+        bits, group, N, K,
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)),
+        _stream_handle(stream))
+    _check(st, "qlinear_unrepack")
 
 
 def qlinear_quantize_rtn(w, bits, group, N, K, packed_q, scales, biases, status=None, stream=None):

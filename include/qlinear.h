@@ -55,6 +55,16 @@ typedef enum {
 
 typedef enum { QL_OUT_F32 = 0, QL_OUT_BF16 = 1 } ql_out_dtype;
 
+/*
+ * Weight layouts. CANONICAL is the layout described at the top of this file.
+ * TILED is this library's load-time repack into the kernels' lane order (see
+ * qlinear_repack): for each strip of 32 output rows and each 64-wide group the
+ * codes form one contiguous block (4-bit 1 KB, 8-bit 2 KB, 2-bit 512 B) and
+ * the scale and bias become one uint32 (s | b << 16) per row and group, so a
+ * wave's loads cover whole cache lines.
+ */
+typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
+
 typedef enum {
   QL_PATH_AUTO = 0,      /* dispatch table decides                            */
   QL_PATH_SKINNY = 1,    /* wavefront GEMV kernel, M <= 16                    */
@@ -82,6 +92,9 @@ typedef struct ql_forward_args {
                                 qlinear_group_sums ([K/64, ld_xsum] fp32);
                                 NULL = computed inside the call             */
   int64_t ld_xsum;           /* row pitch of xsum, >= qlinear_group_sums_ld(M) */
+  int layout;                /* ql_layout. For QL_LAYOUT_TILED, packed_q holds
+                                the tiled codes, scales the tiled scale|bias
+                                words, and biases is ignored                */
 } ql_forward_args;
 
 /*
@@ -165,6 +178,28 @@ int qlinear_quantize_rtn(const float *w, int bits, int group, int64_t N, int64_t
 int qlinear_dequantize(const uint32_t *packed_q, const void *scales, const void *biases,
                        int bits, int group, int64_t N, int64_t K, float *w_out,
                        void *stream);
+
+/* uint32 words of tiled codes for an [N, K] weight: ceil(N/32)*32*K*bits/32. */
+size_t qlinear_tiled_words(int bits, int64_t N, int64_t K);
+
+/* uint32 words of tiled scale|bias for an [N, K] weight: ceil(N/32)*32*K/64. */
+size_t qlinear_tiled_sb_words(int64_t N, int64_t K);
+
+/*
+ * Device repack, canonical -> tiled (one-time, at load). Reads packed_q
+ * [N, K*bits/32], scales and biases [N, K/64]; writes tiled_q
+ * (qlinear_tiled_words) and tiled_sb (qlinear_tiled_sb_words). Rows past N in
+ * the last strip are zero. A bijection on the rows < N: qlinear_unrepack
+ * restores the canonical arrays bit for bit.
+ */
+int qlinear_repack(const uint32_t *packed_q, const void *scales, const void *biases, int bits,
+                   int group, int64_t N, int64_t K, uint32_t *tiled_q, uint32_t *tiled_sb,
+                   void *stream);
+
+/* Device unrepack, tiled -> canonical (inverse of qlinear_repack). */
+int qlinear_unrepack(const uint32_t *tiled_q, const uint32_t *tiled_sb, int bits, int group,
+                     int64_t N, int64_t K, uint32_t *packed_q, void *scales, void *biases,
+                     void *stream);
 
 /* Static description of a status code. */
 const char *qlinear_status_string(int status);

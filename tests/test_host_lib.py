@@ -202,3 +202,21 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ql, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         ql.load_library(str(tmp_path / "missing.so"))
+
+
+def test_tiled_sizes_and_repack_validation(lib):
+    assert ql.qlinear_tiled_words(4, 70, 256) == 96 * 256 // 8
+    assert ql.qlinear_tiled_words(2, 32, 64) == 32 * 64 // 16
+    assert ql.qlinear_tiled_sb_words(70, 256) == 96 * 4
+    assert ql.qlinear_tiled_words(4, 10, 100) == 0
+    vp = 0x1000
+    assert lib.qlinear_repack(vp, vp, vp, 3, 64, 8, 64, vp, vp, None) == ql.QL_EUNSUPPORTED
+    assert lib.qlinear_repack(vp, vp, vp, 4, 64, 8, 96, vp, vp, None) == ql.QL_EINVAL
+    assert lib.qlinear_repack(vp + 4, vp, vp, 4, 64, 8, 64, vp, vp, None) == ql.QL_EALIGN
+    assert lib.qlinear_repack(0, vp, vp, 4, 64, 8, 64, vp, vp, None) == ql.QL_EINVAL
+    assert lib.qlinear_unrepack(vp, vp + 2, 4, 64, 8, 64, vp, vp, vp, None) == ql.QL_EALIGN
+    a = _args(layout=1, biases=0)
+    a.scales = 0x3002   # tiled scale|bias words need 4-byte alignment
+    assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_EALIGN
+    a = _args(layout=5)
+    assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_EINVAL
