@@ -339,9 +339,11 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream) {
   X(5, 64, 128, 1, 2)
 
 const TileInfo kTiles[] = {
-#define QL_TILE_INFO(id, bm, bn, wmw, wnw) {id, bm, bn, wmw, wnw, "gemm_" #bm "x" #bn "_w" #wmw "x" #wnw},
+#define QL_TILE_INFO(id, bm, bn, wmw, wnw) {id, bm, bn, wmw, wnw, "gemm_" #bm "x" #bn "_w" #wmw "x" #wnw, 1},
     QL_TILES(QL_TILE_INFO)
 #undef QL_TILE_INFO
+    {10, 256, 128, 2, 2, "gemm2_256x128_w2x2", 2},
+    {11, 128, 128, 1, 2, "gemm2_128x128_w1x2", 2},
 };
 
 }  // namespace
@@ -352,7 +354,10 @@ const TileInfo *gemm_tile(int id) {
   return nullptr;
 }
 
-bool gemm_tile_supports_tiled(int id) { (void)id; return false; }
+bool gemm_tile_supports_tiled(int id) {
+  const TileInfo *t = gemm_tile(id);
+  return t && t->gen == 2;
+}
 
 int gemm_tile_count() { return (int)(sizeof(kTiles) / sizeof(kTiles[0])); }
 
@@ -369,6 +374,7 @@ size_t gemm_lds_bytes(int bits, int id) {
 }
 
 hipError_t launch_gemm(int bits, int tile_id, const GemmArgs &a, hipStream_t stream) {
+  if (tile_id >= 10) return launch_gemm2(bits, tile_id, false, a, stream);
 #define QL_TILE_LAUNCH(tid, bm, bn, wmw, wnw)                                      \
   if (tile_id == tid) {                                                            \
     if (bits == 4) return launch_tile<4, bm, bn, wmw, wnw>(a, stream);             \

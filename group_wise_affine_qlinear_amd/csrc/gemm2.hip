@@ -1,0 +1,345 @@
+// Large-M fused dequant-GEMM, second generation: 128x64 wave tiles fed by LDS
+// DMA.
+//
+// Same numerics as gemm.hip (exact integer codes on bf16 MFMA, per-group fp32
+// scale and bias), reorganised for gfx950 throughput:
+//  * each wave owns a 128x64 output tile (8x4 subtiles of 16x16), so one
+//    unpacked code fragment feeds 8 MFMA pairs and one x fragment feeds 4;
+//  * global -> LDS staging uses global_load_lds_dwordx4 (each lane moves 16
+//    bytes straight into LDS at base + 16*lane), so the next group's operands
+//    occupy no registers while the current group is computed; the two LDS
+//    stages are distinct objects and the group loop is unrolled by two, which
+//    lets the compiler see that reads of one stage never wait for the copies
+//    into the other;
+//  * x tiles live in LDS as 128-byte rows with the 16-byte chunks XOR-swizzled
+//    by row (chunk c of row r at position c ^ (r & 7)); the swizzle is applied
+//    on the global side of the copy (lane L of a copy loads logical chunk
+//    (L & 7) ^ (L >> 3) of its row), so fragment reads hit distinct banks;
+//  * codes come either in the canonical layout or in the tiled layout of
+//    layout.hip, copied verbatim; fragment reads pick the right bytes of each.
+#include "ql_device.h"
+#include "ql_kernels.h"
+
+namespace ql {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer resource over `bytes` bytes starting at base + off (stride 0,
+// word 3 = the gfx9 raw-buffer format). Reads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t off, int64_t bytes) {
+  const char *p = reinterpret_cast<const char *>(base) + off;
+  const int n = bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, n, 0x00020000);
+}
+
+// One 16-byte-per-lane copy buffer -> LDS: lane L's bytes (at voff + soff in
+// the buffer) land at lds + 16*L. `lds` and `soff` must be wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne2(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Bytes of one output column's codes per 64-wide group.
+template <int BITS> struct WRow { static constexpr int bytes = 64 * BITS / 8; };
+
+template <int BITS, int BM, int BN>
+struct Stage {
+  unsigned char x[BM * 128];                 // BM rows x 64 bf16, chunk-swizzled
+  unsigned char w[BN * WRow<BITS>::bytes];   // codes as stored in global memory
+  float xs[BM];                              // xsum of the group per row
+  f32x2 sb[BN];                              // (scale, bias - offset*scale) per column
+};
+
+template <int BITS, bool TILED, int BM, int BN, int WARPS_M, int WARPS_N, bool OUT_BF16>
+__global__ __launch_bounds__(64 * WARPS_M * WARPS_N, 2)
+void gemm2_kernel(GemmArgs a) {
+  constexpr int NW = WARPS_M * WARPS_N;
+  constexpr int NT = 64 * NW;
+  constexpr int WM = BM / WARPS_M, WN = BN / WARPS_N;
+  constexpr int MI = WM / 16, NI = WN / 16;
+  constexpr int WB = WRow<BITS>::bytes;
+  constexpr int XCOPIES = BM / 8;              // 1 KB copies of x per group (8 rows each)
+  constexpr int XPW = XCOPIES / NW;            // per wave
+  constexpr int WCOPIES = BN * WB / 1024;      // 1 KB copies of codes per group
+  constexpr int WPW = (WCOPIES + NW - 1) / NW;
+  constexpr int BB = 32 * WB;                  // bytes of one tiled block (32 columns)
+  static_assert(XCOPIES % NW == 0, "x copies must split evenly over waves");
+  static_assert(BN * WB % 1024 == 0, "code tile must be whole 1 KB copies");
+  static_assert(BM == 128 || BM == 256, "xsum copy covers 128 or 256 rows");
+  static_assert(BN <= NT && BN % 32 == 0, "scale staging");
+
+  __shared__ __attribute__((aligned(16))) Stage<BITS, BM, BN> st0;
+  __shared__ __attribute__((aligned(16))) Stage<BITS, BM, BN> st1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WARPS_N, wn = wave % WARPS_N;
+  const int r16 = lane & 15, h = lane >> 4;
+
+  const int tiles_n = (int)((a.N + BN - 1) / BN);
+  const int tiles_m = (int)((a.M + BM - 1) / BM);
+  const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int split = blockIdx.y;
+  const int g_begin = split * a.groups_per_split;
+  const int g_end = min(a.G, g_begin + a.groups_per_split);
+  const int G = a.G;
+  const float offset = CodeOffset<BITS>::value;
+
+  // ---- copy plan: buffer resources based at this block's first row / column
+  // (so every per-lane offset is a small 32-bit value) and per-lane offsets
+  // fixed for the whole K loop; the group step goes into the scalar offset.
+  // x: copy i of this wave covers rows R = (wave*XPW + i)*8 .. R+7; lane L
+  // takes row R + L/8 and logical chunk (L & 7) ^ (L >> 3). Rows past M are
+  // clamped to the last row (their outputs are never stored).
+  const int64_t row_bytes_x = a.K * 2;
+  const int64_t mrows = min<int64_t>(BM, a.M - m0);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, m0 * row_bytes_x, mrows * row_bytes_x);
+  uint32_t xo[XPW];
+#pragma unroll
+  for (int i = 0; i < XPW; ++i) {
+    int r = (wave * XPW + i) * 8 + (lane >> 3);
+    if (r >= mrows) r = (int)mrows - 1;
+    xo[i] = (uint32_t)(r * row_bytes_x) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  }
+  // codes: copy j = wave + i*NW covers tile bytes e = j*1024 + 16*lane
+  const int64_t nstrips = (a.N + 31) / 32;
+  const int64_t row_bytes = a.K * BITS / 8;
+  __amdgpu_buffer_rsrc_t wr;
+  uint32_t wo[WPW];
+  if constexpr (TILED) {
+    const int64_t s0 = n0 / 32, ns = min<int64_t>(BN / 32, nstrips - s0);
+    wr = make_rsrc(a.w, s0 * G * BB, ns * G * BB);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int j = wave + i * NW;
+      const int e = (j < WCOPIES ? j : 0) * 1024 + 16 * lane;
+      int st = e / BB;
+      if (st >= ns) st = (int)ns - 1;
+      wo[i] = (uint32_t)(st * G * BB + (e % BB));
+    }
+  } else {
+    const int64_t nrows = min<int64_t>(BN, a.N - n0);
+    wr = make_rsrc(a.w, n0 * row_bytes, nrows * row_bytes);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int j = wave + i * NW;
+      const int e = (j < WCOPIES ? j : 0) * 1024 + 16 * lane;
+      int r = e / WB;
+      if (r >= nrows) r = (int)nrows - 1;
+      wo[i] = (uint32_t)(r * row_bytes + (e % WB));
+    }
+  }
+  const uint32_t w_gstride = TILED ? BB : WB;  // bytes per group step
+  // scale / bias: thread tid < BN stages column tid through one register
+  const bool sb_on = tid < BN;
+  const uint16_t *sg = nullptr, *bg = nullptr;
+  const uint32_t *sbg = nullptr;
+  {
+    const int c = sb_on ? tid : 0;
+    if constexpr (TILED) {
+      int64_t s = n0 / 32 + c / 32;
+      if (s >= nstrips) s = nstrips - 1;
+      sbg = a.sb + s * G * 32 + (c % 32);
+    } else {
+      int64_t n = n0 + c;
+      if (n >= a.N) n = a.N - 1;
+      sg = a.s + n * G;
+      bg = a.b + n * G;
+    }
+  }
+  uint32_t sbr = 0;
+
+  auto issue = [&](Stage<BITS, BM, BN> &S, int gv) {
+    const int g = __builtin_amdgcn_readfirstlane(gv);  // uniform: scalar offsets below
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) dma16(xr, xo[i], (uint32_t)g * 128u, S.x + (wave * XPW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int j = wave + i * NW;
+      if (j < WCOPIES) dma16(wr, wo[i], (uint32_t)g * w_gstride, S.w + j * 1024);
+    }
+    if (wave == 0 && (BM == 256 || lane < 32)) {
+      // this group's xsum row block: floats 4L .. 4L+3 for lane L
+      const __amdgpu_buffer_rsrc_t xsr = make_rsrc(a.xsum, ((int64_t)g * a.Mp + m0) * 4, BM * 4);
+      dma16(xsr, 16u * lane, 0u, S.xs);
+    }
+    if (sb_on) {
+      if constexpr (TILED) sbr = sbg[g * 32];
+      else sbr = (uint32_t)sg[g] | ((uint32_t)bg[g] << 16);
+    }
+  };
+  auto finish = [&](Stage<BITS, BM, BN> &S) {
+    if (sb_on) {
+      const float sf = f16_to_f32((uint16_t)(sbr & 0xFFFFu));
+      const float bf = f16_to_f32((uint16_t)(sbr >> 16));
+      S.sb[tid] = f32x2{sf, __builtin_fmaf(-offset, sf, bf)};
+    }
+  };
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment read offsets inside a stage (rows of subtile mi add mi*16)
+  const int sw = r16 & 7;
+  const int xa0 = (wm * WM + r16) * 128 + ((2 * h) ^ sw) * 16;
+  const int xa1 = (wm * WM + r16) * 128 + ((2 * h + 1) ^ sw) * 16;
+  const int xsa = wm * WM + 4 * h;
+
+  auto compute = [&](const Stage<BITS, BM, BN> &S) {
+    bf16x8 bq[NI][2];
+    f32x2 sbv[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = wn * WN + ni * 16 + r16;
+      // lane group h takes codes 16h .. 16h+15 of the group (k-blocks 2h, 2h+1)
+      if constexpr (BITS == 4) {
+        const int off = TILED ? (col / 32) * BB + (h >> 1) * 512 + (col % 32) * 16 + (h & 1) * 8 : col * WB + h * 8;
+        const u32x2 wv = *reinterpret_cast<const u32x2 *>(S.w + off);
+        bq[ni][0] = as_bf16x8(TILED ? unpack8_b4_pair(wv[0]) : unpack8_b4(wv[0]));
+        bq[ni][1] = as_bf16x8(TILED ? unpack8_b4_pair(wv[1]) : unpack8_b4(wv[1]));
+      } else if constexpr (BITS == 8) {
+        const int off = TILED ? (col / 32) * BB + (h & 1) * 1024 + (h >> 1) * 512 + (col % 32) * 16 : col * WB + h * 16;
+        const u32x4 wv = *reinterpret_cast<const u32x4 *>(S.w + off);
+        bq[ni][0] = as_bf16x8(unpack8_b8(wv[0], wv[1]));
+        bq[ni][1] = as_bf16x8(unpack8_b8(wv[2], wv[3]));
+      } else {
+        const int off = TILED ? (col / 32) * BB + (h >> 1) * 256 + (col % 32) * 8 + (h & 1) * 4 : col * WB + h * 4;
+        const uint32_t wv = *reinterpret_cast<const uint32_t *>(S.w + off);
+        bq[ni][0] = as_bf16x8(TILED ? unpack8_b2_pair(wv, 0) : unpack8_b2(wv, 0));
+        bq[ni][1] = as_bf16x8(TILED ? unpack8_b2_pair(wv, 1) : unpack8_b2(wv, 1));
+      }
+      sbv[ni] = S.sb[col];
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      // subtile rows start at multiples of 16: the swizzle term is per lane only
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(S.x + xa0 + mi * 2048);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(S.x + xa1 + mi * 2048);
+      const f32x4 xs = *reinterpret_cast<const f32x4 *>(&S.xs[xsa + mi * 16]);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[ni][0], p, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq[ni][1], p, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = __builtin_fmaf(sbv[ni][0], p[i], acc[mi][ni][i]);
+          acc[mi][ni][i] = __builtin_fmaf(sbv[ni][1], xs[i], t);
+        }
+        // keep the update here: sinking it would hold every subtile's P live
+        asm volatile("" : "+v"(acc[mi][ni]));
+      }
+      // bound register pressure: no hoisting of later subtile rows' operands
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Groups run in pairs (stage 0 then stage 1) with a single loop exit; an odd
+  // last group runs after the loop from stage 0.
+  if (g_begin < g_end) {
+    issue(st0, g_begin);
+    finish(st0);
+  }
+  __syncthreads();
+  int g = g_begin;
+  for (; g + 1 < g_end; g += 2) {
+    issue(st1, g + 1);
+    compute(st0);
+    finish(st1);
+    __syncthreads();
+    const bool more2 = g + 2 < g_end;
+    if (more2) issue(st0, g + 2);
+    compute(st1);
+    if (more2) finish(st0);
+    __syncthreads();
+  }
+  if (g < g_end) compute(st0);
+
+  // ---- store
+  const int64_t row0 = m0 + wm * WM + 4 * h;
+  const int64_t col0 = n0 + wn * WN + r16;
+  const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+  if (a.splits > 1) {
+    float *outp = a.partial + (int64_t)split * a.M * a.N;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + mi * 16 + i, n = col0 + ni * 16;
+          if (full || (m < a.M && n < a.N)) outp[m * a.N + n] = acc[mi][ni][i];
+        }
+  } else if constexpr (OUT_BF16) {
+    uint16_t *outp = reinterpret_cast<uint16_t *>(a.out);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + mi * 16 + i, n = col0 + ni * 16;
+          if (full || (m < a.M && n < a.N)) outp[m * a.N + n] = f32_to_bf16_rne2(acc[mi][ni][i]);
+        }
+  } else {
+    float *outp = reinterpret_cast<float *>(a.out);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + mi * 16 + i, n = col0 + ni * 16;
+          if (full || (m < a.M && n < a.N)) outp[m * a.N + n] = acc[mi][ni][i];
+        }
+  }
+}
+
+template <int BITS, bool TILED, int BM, int BN, int WMW, int WNW>
+hipError_t launch2(const GemmArgs &a, hipStream_t stream) {
+  const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
+  dim3 grid(tiles, a.splits);
+  if (a.out_bf16 && a.splits == 1)
+    hipLaunchKernelGGL((gemm2_kernel<BITS, TILED, BM, BN, WMW, WNW, true>), grid, dim3(64 * WMW * WNW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm2_kernel<BITS, TILED, BM, BN, WMW, WNW, false>), grid, dim3(64 * WMW * WNW), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WMW, int WNW>
+hipError_t launch2_any(int bits, bool tiled, const GemmArgs &a, hipStream_t stream) {
+  if (bits == 4) return tiled ? launch2<4, true, BM, BN, WMW, WNW>(a, stream) : launch2<4, false, BM, BN, WMW, WNW>(a, stream);
+  if (bits == 8) return tiled ? launch2<8, true, BM, BN, WMW, WNW>(a, stream) : launch2<8, false, BM, BN, WMW, WNW>(a, stream);
+  if (bits == 2) return tiled ? launch2<2, true, BM, BN, WMW, WNW>(a, stream) : launch2<2, false, BM, BN, WMW, WNW>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t gemm2_lds_bytes(int bits, int id) {
+  if (id == 10) return 2 * (bits == 4 ? sizeof(Stage<4, 256, 128>) : bits == 8 ? sizeof(Stage<8, 256, 128>) : sizeof(Stage<2, 256, 128>));
+  if (id == 11) return 2 * (bits == 4 ? sizeof(Stage<4, 128, 128>) : bits == 8 ? sizeof(Stage<8, 128, 128>) : sizeof(Stage<2, 128, 128>));
+  return 0;
+}
+
+hipError_t launch_gemm2(int bits, int tile_id, bool tiled, const GemmArgs &a, hipStream_t stream) {
+  if (tile_id == 10) return launch2_any<256, 128, 2, 2>(bits, tiled, a, stream);
+  if (tile_id == 11) return launch2_any<128, 128, 1, 2>(bits, tiled, a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ql

@@ -316,10 +316,12 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   } else if (ql::launch_xsum(static_cast<const uint16_t *>(a->x), xsum, a->M, a->K, Mp, stream) != hipSuccess) {
     return QL_EHIP;
   }
+  const bool tiled = a->layout == QL_LAYOUT_TILED;
   ql::GemmArgs g{static_cast<const uint16_t *>(a->x),
                  a->packed_q,
-                 static_cast<const uint16_t *>(a->scales),
-                 static_cast<const uint16_t *>(a->biases),
+                 tiled ? nullptr : static_cast<const uint16_t *>(a->scales),
+                 tiled ? nullptr : static_cast<const uint16_t *>(a->biases),
+                 tiled ? static_cast<const uint32_t *>(a->scales) : nullptr,
                  xsum,
                  a->out,
                  partial,
@@ -329,9 +331,12 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                  p.groups_per_split,
                  out_bf16};
   const ql::TileInfo *ti = ql::gemm_tile(p.tile);
-  std::snprintf(buf, sizeof(buf), "%s_b%d_split%d", ti ? ti->name : "gemm", a->bits, p.splits);
+  std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
+                tiled ? "tiled" : "canonical");
   set_last_path(buf);
-  if (ql::launch_gemm(a->bits, p.tile, g, stream) != hipSuccess) return QL_EHIP;
+  const hipError_t le = (ti && ti->gen == 2) ? ql::launch_gemm2(a->bits, p.tile, tiled, g, stream)
+                                             : ql::launch_gemm(a->bits, p.tile, g, stream);
+  if (le != hipSuccess) return QL_EHIP;
   if (p.splits > 1) {
     if (ql::launch_splitk_reduce(partial, p.splits, a->M, a->N, a->out, out_bf16, stream) != hipSuccess)
       return QL_EHIP;

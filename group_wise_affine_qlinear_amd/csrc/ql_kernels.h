@@ -10,8 +10,9 @@ namespace ql {
 struct GemmArgs {
   const uint16_t *x;      // bf16 [M, K]
   const uint32_t *w;      // packed codes [N, K*bits/32]
-  const uint16_t *s;      // f16 [N, G]
-  const uint16_t *b;      // f16 [N, G]
+  const uint16_t *s;      // f16 [N, G] (canonical layout)
+  const uint16_t *b;      // f16 [N, G] (canonical layout)
+  const uint32_t *sb;     // scale|bias words (tiled layout)
   const float *xsum;      // [G, Mp] per-group row sums of x
   void *out;              // [M, N] fp32 or bf16 (splits == 1)
   float *partial;         // [splits, M, N] fp32 (splits > 1)
@@ -25,6 +26,7 @@ struct GemmArgs {
 struct TileInfo {
   int id, bm, bn, warps_m, warps_n;
   const char *name;
+  int gen;  // 1: gemm.hip (canonical only), 2: gemm2.hip (canonical or tiled)
 };
 
 // GEMM tile configurations compiled into the library (id >= 1).
@@ -36,6 +38,9 @@ size_t gemm_lds_bytes(int bits, int id);
 hipError_t launch_xsum(const uint16_t *x, float *xsum, int64_t M, int64_t K, int64_t Mp,
                        hipStream_t stream);
 hipError_t launch_gemm(int bits, int tile_id, const GemmArgs &a, hipStream_t stream);
+// second-generation kernel (gemm2.hip), tile ids >= 10, canonical or tiled codes
+hipError_t launch_gemm2(int bits, int tile_id, bool tiled, const GemmArgs &a, hipStream_t stream);
+size_t gemm2_lds_bytes(int bits, int id);
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N,
                                 void *out, int out_bf16, hipStream_t stream);
 hipError_t launch_fill_zero(void *out, int64_t count, int out_bf16, hipStream_t stream);

@@ -60,15 +60,19 @@ class Case:
         return oracle.forward_rows(self.x, self.packed, self.s16, self.b16, self.bits, self.K, rows, cols)
 
 
-def run_forward(torch, case, path=ql.QL_PATH_AUTO, split_k=0, tile=0, out_dtype="f32", via_ex=True):
+def run_forward(torch, case, path=ql.QL_PATH_AUTO, split_k=0, tile=0, out_dtype="f32", via_ex=True,
+                layout=ql.QL_LAYOUT_CANONICAL):
     x, p, s, b = case.device(torch)
+    if layout == ql.QL_LAYOUT_TILED:
+        p, s = ql.qlinear_repack(p, s, b, case.bits, 64, case.N, case.K)
+        b = None
     if out_dtype == "f32":
         out = torch.full((case.M, case.N), float("nan"), dtype=torch.float32, device="cuda")
     else:
         out = torch.zeros((case.M, case.N), dtype=torch.bfloat16, device="cuda")
     if via_ex:
         ql.qlinear_forward_ex(x, p, s, b, case.bits, case.M, case.N, case.K, out, path=path,
-                              split_k=split_k, tile=tile)
+                              split_k=split_k, tile=tile, layout=layout)
     else:
         ql.qlinear_forward(x, p, s, b, case.bits, 64, case.M, case.N, case.K, out)
     torch.cuda.synchronize()

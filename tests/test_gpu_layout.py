@@ -5,9 +5,9 @@ import numpy as np
 import pytest
 
 import oracle
-from group_wise_affine_qlinear_amd import qlinear as ql
+from group_wise_affine_qlinear_amd import inputs, qlinear as ql
 
-from gpu_helpers import Case, assert_parity, dev, host_u16, host_u32, torch_or_skip
+from gpu_helpers import Case, assert_parity, dev, host_u16, host_u32, run_forward, torch_or_skip
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,35 @@ def test_tiled_identity_rows_exact(torch):
     ql.qlinear_forward_ex(xd, tq, tsb, None, 8, M, N, K, out, layout=ql.QL_LAYOUT_TILED)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), oracle.dequantize(c.q, c.s16, c.b16)[:, cols].T)
+
+
+# Shapes for the 128x64-wave-tile GEMM: several block tiles in M and N with
+# ragged edges, odd and even group counts (its K loop runs groups in pairs).
+GEMM2_SHAPES = [(520, 390, 320), (200, 300, 1024), (129, 129, 192), (17, 40, 64), (384, 256, 512)]
+
+
+@pytest.mark.parametrize("layout", [ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED])
+@pytest.mark.parametrize("tile", [10, 11])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("shape", GEMM2_SHAPES)
+def test_gemm2_parity(torch, shape, bits, tile, layout):
+    M, N, K = shape
+    c = Case(M, N, K, bits, wid=330 + bits, x_structure="outlier")
+    ref = c.reference()
+    y = run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=tile, layout=layout)
+    assert ql.qlinear_last_path().startswith("gemm2"), ql.qlinear_last_path()
+    assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
+    if K >= 192:
+        y = run_forward(torch, c, path=ql.QL_PATH_SPLITK, split_k=3, tile=tile, layout=layout)
+        assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
+
+
+@pytest.mark.parametrize("layout", [ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_gemm2_bf16_out(torch, bits, layout):
+    c = Case(300, 260, 384, bits, wid=340 + bits)
+    ref = run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=10, layout=layout).cpu().numpy()
+    y = run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=10, layout=layout, out_dtype="bf16")
+    # same accumulation, rounded to nearest-even bf16 at the store
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(ref))

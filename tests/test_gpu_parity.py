@@ -114,7 +114,7 @@ def test_gemm_ragged(torch, bits, shape):
         assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 5, 10, 11])
 def test_gemm_every_tile(torch, tile):
     c = Case(300, 520, 640, 4, wid=220, x_structure="outlier")
     ref = c.reference()
