@@ -58,9 +58,19 @@ struct Stage {
   f32x2 sb[BN];                              // (scale, bias - offset*scale) per column
 };
 
-template <int BITS, bool TILED, int BM, int BN, int WARPS_M, int WARPS_N, bool OUT_BF16>
-__global__ __launch_bounds__(64 * WARPS_M * WARPS_N, 2)
-void gemm2_kernel(GemmArgs a) {
+template <int BITS, bool TILED, int BM, int BN, int WARPS_M, int WARPS_N>
+struct Gemm2Shape {
+  static constexpr int NT = 64 * WARPS_M * WARPS_N;
+  static constexpr int MI = BM / WARPS_M / 16, NI = BN / WARPS_N / 16;
+};
+
+// Accumulates groups [g_begin, g_end) of the BM x BN output tile at (m0, n0)
+// into acc (zeroed first). Leaves both LDS stages free on return.
+template <int BITS, bool TILED, int BM, int BN, int WARPS_M, int WARPS_N>
+__device__ __forceinline__ void tile_accumulate(const GemmArgs &a, Stage<BITS, BM, BN> &st0,
+                                                Stage<BITS, BM, BN> &st1, int64_t m0, int64_t n0,
+                                                int g_begin, int g_end,
+                                                f32x4 (&acc)[BM / WARPS_M / 16][BN / WARPS_N / 16]) {
   constexpr int NW = WARPS_M * WARPS_N;
   constexpr int NT = 64 * NW;
   constexpr int WM = BM / WARPS_M, WN = BN / WARPS_N;
@@ -76,23 +86,11 @@ void gemm2_kernel(GemmArgs a) {
   static_assert(BM == 128 || BM == 256, "xsum copy covers 128 or 256 rows");
   static_assert(BN <= NT && BN % 32 == 0, "scale staging");
 
-  __shared__ __attribute__((aligned(16))) Stage<BITS, BM, BN> st0;
-  __shared__ __attribute__((aligned(16))) Stage<BITS, BM, BN> st1;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WARPS_N, wn = wave % WARPS_N;
   const int r16 = lane & 15, h = lane >> 4;
-
-  const int tiles_n = (int)((a.N + BN - 1) / BN);
-  const int tiles_m = (int)((a.M + BM - 1) / BM);
-  const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int split = blockIdx.y;
-  const int g_begin = split * a.groups_per_split;
-  const int g_end = min(a.G, g_begin + a.groups_per_split);
   const int G = a.G;
   const float offset = CodeOffset<BITS>::value;
 
@@ -187,7 +185,6 @@ void gemm2_kernel(GemmArgs a) {
     }
   };
 
-  f32x4 acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -224,26 +221,53 @@ void gemm2_kernel(GemmArgs a) {
       }
       sbv[ni] = S.sb[col];
     }
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    // Software pipeline over the wave's subtile rows. Step t reads the x
+    // fragments of row t+1, issues the 8 MFMAs of row t and applies the fp32
+    // epilogue of row t-1 (scale) and row t (bias), so the MFMA and VALU pipes
+    // work at the same time; each MFMA is paired with four VALU ops.
+    bf16x8 a0[2], a1[2];
+    f32x4 xs[2];
+    f32x4 P[2][NI];
+    auto read_a = [&](int mi, int slot) {
       // subtile rows start at multiples of 16: the swizzle term is per lane only
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(S.x + xa0 + mi * 2048);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(S.x + xa1 + mi * 2048);
-      const f32x4 xs = *reinterpret_cast<const f32x4 *>(&S.xs[xsa + mi * 16]);
+      a0[slot] = *reinterpret_cast<const bf16x8 *>(S.x + xa0 + mi * 2048);
+      a1[slot] = *reinterpret_cast<const bf16x8 *>(S.x + xa1 + mi * 2048);
+      xs[slot] = *reinterpret_cast<const f32x4 *>(&S.xs[xsa + mi * 16]);
+    };
+    read_a(0, 0);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
-        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[ni][0], p, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq[ni][1], p, 0, 0, 0);
+    for (int t = 0; t <= MI; ++t) {
+      const int cur = t & 1, nxt = cur ^ 1;
+      if (t + 1 < MI) read_a(t + 1, nxt);
+      if (t < MI) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float t = __builtin_fmaf(sbv[ni][0], p[i], acc[mi][ni][i]);
-          acc[mi][ni][i] = __builtin_fmaf(sbv[ni][1], xs[i], t);
-        }
-        // keep the update here: sinking it would hold every subtile's P live
-        asm volatile("" : "+v"(acc[mi][ni]));
+        for (int ni = 0; ni < NI; ++ni)
+          P[cur][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[cur], bq[ni][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          P[cur][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[cur], bq[ni][1], P[cur][ni], 0, 0, 0);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][ni][i] = __builtin_fmaf(sbv[ni][1], xs[cur][i], acc[t][ni][i]);
       }
-      // bound register pressure: no hoisting of later subtile rows' operands
+      if (t >= 1) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t - 1][ni][i] = __builtin_fmaf(sbv[ni][0], P[nxt][ni][i], acc[t - 1][ni][i]);
+          // keep the update here: sinking it would hold every subtile's P live
+          asm volatile("" : "+v"(acc[t - 1][ni]));
+        }
+      }
+      if (t + 1 < MI) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // fragment reads first
+      if (t < MI) {
+#pragma unroll
+        for (int k = 0; k < 2 * NI; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -268,8 +292,21 @@ void gemm2_kernel(GemmArgs a) {
     __syncthreads();
   }
   if (g < g_end) compute(st0);
+  __syncthreads();  // every wave is done with both stages before they are refilled
+}
 
-  // ---- store
+// Stores a finished tile: fp32 or bf16 into out, or fp32 into the split-K
+// partial buffer of `split`.
+template <int BITS, bool TILED, int BM, int BN, int WARPS_M, int WARPS_N, bool OUT_BF16>
+__device__ __forceinline__ void tile_store(const GemmArgs &a, int64_t m0, int64_t n0, int split,
+                                           const f32x4 (&acc)[BM / WARPS_M / 16][BN / WARPS_N / 16]) {
+  constexpr int WM = BM / WARPS_M, WN = BN / WARPS_N;
+  constexpr int MI = WM / 16, NI = WN / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WARPS_N, wn = wave % WARPS_N;
+  const int r16 = lane & 15, h = lane >> 4;
   const int64_t row0 = m0 + wm * WM + 4 * h;
   const int64_t col0 = n0 + wn * WN + r16;
   const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N);
@@ -309,10 +346,90 @@ void gemm2_kernel(GemmArgs a) {
   }
 }
 
+// One launch covers `dp_tiles` whole tiles (tile t = blockIdx.x, blockIdx.x +
+// gridDim.x, ..., split over K by blockIdx.y when splits > 1) and, when
+// sk_tiles > 0, the last sk_tiles tiles cut into sk_pieces K-ranges that run
+// first, one per block. A tile that does not fill the machine's last round is
+// thereby spread over every block instead of leaving most of them idle. Each
+// piece writes its fp32 partial to workspace; the piece that finishes last
+// (atomic count) adds all partials in piece order, so the result does not
+// depend on timing, stores the tile and re-arms the count.
+template <int BITS, bool TILED, int BM, int BN, int WARPS_M, int WARPS_N, bool OUT_BF16>
+__global__ __launch_bounds__(64 * WARPS_M * WARPS_N, 2)
+void gemm2_kernel(GemmArgs a) {
+  using Sh = Gemm2Shape<BITS, TILED, BM, BN, WARPS_M, WARPS_N>;
+  constexpr int NT = Sh::NT, MI = Sh::MI, NI = Sh::NI;
+  __shared__ __attribute__((aligned(16))) Stage<BITS, BM, BN> st0;
+  __shared__ __attribute__((aligned(16))) Stage<BITS, BM, BN> st1;
+  __shared__ int s_arrived;
+
+  const int tid = threadIdx.x;
+  const int tiles_n = (int)((a.N + BN - 1) / BN);
+  f32x4 acc[MI][NI];
+
+  if (a.sk_tiles > 0 && (int)blockIdx.x < a.sk_tiles * a.sk_pieces) {
+    // pieces of one tail tile stay on one XCD (block ids dealt round-robin
+    // over 8 XCDs) so their partials meet in one L2
+    int tail, piece;
+    if (a.sk_tiles % 8 == 0 && gridDim.x % 8 == 0) {
+      const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+      tail = (j / a.sk_pieces) * 8 + x;
+      piece = j % a.sk_pieces;
+    } else {
+      tail = blockIdx.x / a.sk_pieces;
+      piece = blockIdx.x % a.sk_pieces;
+    }
+    const int tile = a.dp_tiles + tail;
+    const int64_t m0 = (int64_t)(tile / tiles_n) * BM, n0 = (int64_t)(tile % tiles_n) * BN;
+    const int gpp = (a.G + a.sk_pieces - 1) / a.sk_pieces;
+    const int gb = piece * gpp, ge = min(a.G, gb + gpp);
+    tile_accumulate<BITS, TILED, BM, BN, WARPS_M, WARPS_N>(a, st0, st1, m0, n0, gb, ge, acc);
+    // partial in thread-major order: each (mi, ni) fragment is NT*16 contiguous bytes
+    float *part = a.sk_partial + (int64_t)tail * a.sk_pieces * (BM * BN);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        *reinterpret_cast<f32x4 *>(part + (int64_t)piece * (BM * BN) + ((mi * NI + ni) * NT + tid) * 4) = acc[mi][ni];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_arrived = atomicAdd(&a.sk_count[tail], 1);
+    __syncthreads();
+    if (s_arrived == a.sk_pieces - 1) {
+      __threadfence();
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const f32x4 mine = acc[mi][ni];
+          f32x4 sum = piece == 0 ? mine : *reinterpret_cast<const f32x4 *>(part + ((mi * NI + ni) * NT + tid) * 4);
+          for (int p = 1; p < a.sk_pieces; ++p) {
+            const f32x4 v = p == piece ? mine
+                                       : *reinterpret_cast<const f32x4 *>(part + (int64_t)p * (BM * BN) +
+                                                                         ((mi * NI + ni) * NT + tid) * 4);
+            sum += v;
+          }
+          acc[mi][ni] = sum;
+        }
+      tile_store<BITS, TILED, BM, BN, WARPS_M, WARPS_N, OUT_BF16>(a, m0, n0, 0, acc);
+      if (tid == 0) a.sk_count[tail] = 0;
+    }
+  }
+
+  const int split = blockIdx.y;
+  const int g_begin = split * a.groups_per_split;
+  const int g_end = min(a.G, g_begin + a.groups_per_split);
+  for (int t = blockIdx.x; t < a.dp_tiles; t += gridDim.x) {
+    const int tile = xcd_remap(t, a.dp_tiles);
+    const int64_t m0 = (int64_t)(tile / tiles_n) * BM, n0 = (int64_t)(tile % tiles_n) * BN;
+    tile_accumulate<BITS, TILED, BM, BN, WARPS_M, WARPS_N>(a, st0, st1, m0, n0, g_begin, g_end, acc);
+    tile_store<BITS, TILED, BM, BN, WARPS_M, WARPS_N, OUT_BF16>(a, m0, n0, split, acc);
+  }
+}
+
 template <int BITS, bool TILED, int BM, int BN, int WMW, int WNW>
 hipError_t launch2(const GemmArgs &a, hipStream_t stream) {
-  const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
-  dim3 grid(tiles, a.splits);
+  dim3 grid(a.grid_x, a.splits);
   if (a.out_bf16 && a.splits == 1)
     hipLaunchKernelGGL((gemm2_kernel<BITS, TILED, BM, BN, WMW, WNW, true>), grid, dim3(64 * WMW * WNW), 0, stream, a);
   else
@@ -334,6 +451,36 @@ size_t gemm2_lds_bytes(int bits, int id) {
   if (id == 10) return 2 * (bits == 4 ? sizeof(Stage<4, 256, 128>) : bits == 8 ? sizeof(Stage<8, 256, 128>) : sizeof(Stage<2, 256, 128>));
   if (id == 11) return 2 * (bits == 4 ? sizeof(Stage<4, 128, 128>) : bits == 8 ? sizeof(Stage<8, 128, 128>) : sizeof(Stage<2, 128, 128>));
   return 0;
+}
+
+Gemm2Plan gemm2_plan(int bits, int tile_id, int64_t M, int64_t N, int G, int splits, int slots) {
+  const int bm = tile_id == 10 ? 256 : 128, bn = 128;
+  Gemm2Plan p{};
+  p.tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  p.dp_tiles = (int)p.tiles;
+  p.grid_x = (int)p.tiles;
+  // This kernel is bound by per-SIMD instruction issue, not by rounds of
+  // blocks: a CU with one resident block already runs at full rate, so the
+  // tiles past the last full round cost their share of work either way, and
+  // splitting them only adds partial traffic and fences (measured slower on
+  // MI355X at 4096x4608x4608). The split runs only when a caller-side slot
+  // count is given (tests of the split itself).
+  if (splits > 1 || G < 2 || p.tiles < 2 || slots <= 0) return p;
+  if (p.tiles <= slots || p.tiles % slots == 0) return p;
+  const int64_t dp = (p.tiles / slots) * slots;
+  const int tail = (int)(p.tiles - dp);
+  int pieces = slots / tail;
+  if (pieces > G) pieces = G;
+  if (pieces < 2) return p;
+  const int gpp = (G + pieces - 1) / pieces;
+  pieces = (G + gpp - 1) / gpp;  // no empty piece
+  p.dp_tiles = (int)dp;
+  p.sk_tiles = tail;
+  p.sk_pieces = pieces;
+  p.grid_x = slots;
+  const size_t part = (size_t)tail * pieces * bm * bn * 4u;
+  p.sk_partial_bytes = ((part + 255) / 256) * 256 + (((size_t)tail * 4u + 255) / 256) * 256;
+  return p;
 }
 
 hipError_t launch_gemm2(int bits, int tile_id, bool tiled, const GemmArgs &a, hipStream_t stream) {

@@ -121,7 +121,13 @@ struct Plan {
   int splits = 1;
   int groups_per_split = 0;
   size_t ws_xsum = 0, ws_partial = 0;
+  ql::Gemm2Plan g2{};
 };
+
+size_t ti_sizes(int tile) {
+  const ql::TileInfo *t = ql::gemm_tile(tile);
+  return t ? (size_t)t->bm * (size_t)t->bn : 0;
+}
 
 int env_int(const char *name, int dflt) {
   const char *v = std::getenv(name);
@@ -197,6 +203,12 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   p->groups_per_split = gps;
   p->ws_xsum = (size_t)G * (size_t)round_up(M, 256) * 4u;
   p->ws_partial = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4u : 0;
+  if (ti->gen == 2) {
+    // QLINEAR_GEMM_SLOTS: resident-block count override, for tests of the
+    // split tail on small shapes
+    p->g2 = ql::gemm2_plan(bits, tile, M, N, G, splits, env_int("QLINEAR_GEMM_SLOTS", 0));
+    if (p->g2.sk_partial_bytes > p->ws_partial) p->ws_partial = p->g2.sk_partial_bytes;
+  }
   return QL_OK;
 }
 
@@ -329,10 +341,22 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                  G,
                  p.splits,
                  p.groups_per_split,
-                 out_bf16};
+                 out_bf16,
+                 p.g2.dp_tiles, p.g2.sk_tiles, p.g2.sk_pieces, p.g2.grid_x,
+                 nullptr, nullptr};
+  if (p.g2.sk_tiles > 0) {
+    const size_t part = (size_t)p.g2.sk_tiles * p.g2.sk_pieces * ti_sizes(p.tile);
+    g.sk_partial = partial;
+    g.sk_count = reinterpret_cast<int *>(reinterpret_cast<char *>(partial) + round_up((int64_t)part * 4, 256));
+    if (ql::launch_fill_zero(g.sk_count, p.g2.sk_tiles, 0, stream) != hipSuccess) return QL_EHIP;
+  }
   const ql::TileInfo *ti = ql::gemm_tile(p.tile);
-  std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
-                tiled ? "tiled" : "canonical");
+  if (p.g2.sk_tiles > 0)
+    std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_tail%dx%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
+                  p.g2.sk_tiles, p.g2.sk_pieces, tiled ? "tiled" : "canonical");
+  else
+    std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
+                  tiled ? "tiled" : "canonical");
   set_last_path(buf);
   const hipError_t le = (ti && ti->gen == 2) ? ql::launch_gemm2(a->bits, p.tile, tiled, g, stream)
                                              : ql::launch_gemm(a->bits, p.tile, g, stream);

@@ -21,6 +21,10 @@ struct GemmArgs {
   int splits;
   int groups_per_split;
   int out_bf16;
+  // second-generation kernel only (see Gemm2Plan)
+  int dp_tiles, sk_tiles, sk_pieces, grid_x;
+  float *sk_partial;      // [sk_tiles, sk_pieces, BM*BN] fp32
+  int *sk_count;          // [sk_tiles], zero before the launch; left zero after it
 };
 
 struct TileInfo {
@@ -41,6 +45,16 @@ hipError_t launch_gemm(int bits, int tile_id, const GemmArgs &a, hipStream_t str
 // second-generation kernel (gemm2.hip), tile ids >= 10, canonical or tiled codes
 hipError_t launch_gemm2(int bits, int tile_id, bool tiled, const GemmArgs &a, hipStream_t stream);
 size_t gemm2_lds_bytes(int bits, int id);
+// Work split of one second-generation launch over the blocks the device holds
+// at once (`slots`; <= 0 queries the device): dp_tiles whole tiles, then the
+// remaining sk_tiles tiles cut into sk_pieces K-ranges each when the whole
+// tiles leave part of the last round idle.
+struct Gemm2Plan {
+  int64_t tiles;
+  int dp_tiles, sk_tiles, sk_pieces, grid_x;
+  size_t sk_partial_bytes;  // includes the counters, 256-byte aligned pieces
+};
+Gemm2Plan gemm2_plan(int bits, int tile_id, int64_t M, int64_t N, int G, int splits, int slots);
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N,
                                 void *out, int out_bf16, hipStream_t stream);
 hipError_t launch_fill_zero(void *out, int64_t count, int out_bf16, hipStream_t stream);

@@ -73,6 +73,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"libqlinear.so not found at {path}; build it with "
             "`python -m group_wise_affine_qlinear_amd.build` (hipcc, gfx950)")
+    # torch ships its own HIP runtime; loading it first makes the library bind
+    # to that same runtime, so device pointers and streams from torch are valid
+    # in the library's calls (a second runtime instance would not know them)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     sig = {

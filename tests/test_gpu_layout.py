@@ -132,3 +132,35 @@ def test_gemm2_bf16_out(torch, bits, layout):
     # same accumulation, rounded to nearest-even bf16 at the store
     got = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, inputs.f32_to_bf16_bits(ref))
+
+
+# Split tail: with the resident-block count forced small, the tiles past the
+# last full round are cut into K pieces whose partials the last finisher adds.
+# (slots, shape) pairs cover 2 and 5 pieces, an uneven last piece, the 8-XCD
+# piece placement (8 tail tiles, 16 slots) and both tile heights.
+SPLIT_TAIL_CASES = [
+    (10, 10, (520, 390, 320)),    # 12 tiles: 10 whole, 2 tail tiles x 5 pieces of 1 group
+    (10, 8, (520, 390, 448)),     # 12 tiles: 8 whole, 4 tail tiles x 2 pieces (G=7: 4+3)
+    (10, 16, (520, 1000, 640)),   # 24 tiles: 16 whole, 8 tail tiles x 2 pieces, XCD placement
+    (11, 6, (300, 260, 576)),     # 128x128 tiles: 9 tiles, 6 whole, 3 tail tiles x 2 pieces
+]
+
+
+@pytest.mark.parametrize("layout", [ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("tile,slots,shape", SPLIT_TAIL_CASES)
+def test_gemm2_split_tail(torch, monkeypatch, tile, slots, shape, bits, layout):
+    M, N, K = shape
+    monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
+    c = Case(M, N, K, bits, wid=350 + bits)
+    ref = c.reference()
+    y1 = run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=tile, layout=layout)
+    assert "_tail" in ql.qlinear_last_path(), ql.qlinear_last_path()
+    assert_parity(y1.cpu().numpy(), ref, what=ql.qlinear_last_path())
+    # the counters are re-armed and the piece order is fixed: a second call is
+    # bit-identical
+    y2 = run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=tile, layout=layout)
+    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    yb = run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=tile, layout=layout, out_dtype="bf16")
+    got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(y1.cpu().numpy()))
