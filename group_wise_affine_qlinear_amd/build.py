@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlinear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["host.cpp", "gemm.hip", "gemm2.hip", "skinny.hip", "misc.hip", "layout.hip"]
+SOURCES = ["host.cpp", "gemm.hip", "gemm2.hip", "gemm3.hip", "skinny.hip", "misc.hip", "layout.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -344,6 +344,7 @@ const TileInfo kTiles[] = {
 #undef QL_TILE_INFO
     {10, 256, 128, 2, 2, "gemm2_256x128_w2x2", 2},
     {11, 128, 128, 1, 2, "gemm2_128x128_w1x2", 2},
+    {20, 256, 256, 2, 4, "gemm3_f16_256x256_w2x4", 3},
 };
 
 }  // namespace
@@ -356,7 +357,7 @@ const TileInfo *gemm_tile(int id) {
 
 bool gemm_tile_supports_tiled(int id) {
   const TileInfo *t = gemm_tile(id);
-  return t && t->gen == 2;
+  return t && t->gen >= 2;
 }
 
 int gemm_tile_count() { return (int)(sizeof(kTiles) / sizeof(kTiles[0])); }
@@ -374,7 +375,7 @@ size_t gemm_lds_bytes(int bits, int id) {
 }
 
 hipError_t launch_gemm(int bits, int tile_id, const GemmArgs &a, hipStream_t stream) {
-  if (tile_id >= 10) return launch_gemm2(bits, tile_id, false, a, stream);
+  if (tile_id >= 10 && tile_id < 20) return launch_gemm2(bits, tile_id, false, a, stream);
 #define QL_TILE_LAUNCH(tid, bm, bn, wmw, wnw)                                      \
   if (tile_id == tid) {                                                            \
     if (bits == 4) return launch_tile<4, bm, bn, wmw, wnw>(a, stream);             \

@@ -24,22 +24,6 @@ namespace ql {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Raw buffer resource over `bytes` bytes starting at base + off (stride 0,
-// word 3 = the gfx9 raw-buffer format). Reads past `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t off, int64_t bytes) {
-  const char *p = reinterpret_cast<const char *>(base) + off;
-  const int n = bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, n, 0x00020000);
-}
-
-// One 16-byte-per-lane copy buffer -> LDS: lane L's bytes (at voff + soff in
-// the buffer) land at lds + 16*L. `lds` and `soff` must be wave-uniform.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)voff, (int)soff, 0, 0);
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne2(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));

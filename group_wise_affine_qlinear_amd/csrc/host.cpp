@@ -117,11 +117,14 @@ int get_owned_workspace(size_t need, void **out) {
 // ---- dispatch
 struct Plan {
   int path = QL_PATH_AUTO;
+  int mode = QL_MODE_EXACT;
   int tile = 0;
   int splits = 1;
   int groups_per_split = 0;
   size_t ws_xsum = 0, ws_partial = 0;
+  size_t ws_x16 = 0;  // fast mode: fp16 x and per-row scales
   ql::Gemm2Plan g2{};
+  ql::Gemm3Plan g3{};
 };
 
 size_t ti_sizes(int tile) {
@@ -158,8 +161,11 @@ int choose_splits(int64_t tiles, int G) {
   return s < 1 ? 1 : s;
 }
 
+// Large-M fast-mode tile (gemm3.hip).
+constexpr int kFastTile = 20;
+
 int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int force_split,
-              int force_tile, Plan *p) {
+              int force_tile, bool tiled, int mode, Plan *p) {
   const int G = (int)(K / kGroup);
   int path = force_path;
   if (path == QL_PATH_AUTO) {
@@ -168,12 +174,36 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   }
   if (path == QL_PATH_AUTO) path = (M <= kMaxSkinnyM) ? QL_PATH_SKINNY : QL_PATH_GEMM;
   if (path == QL_PATH_SKINNY) {
-    if (M > kMaxSkinnyM) return QL_EUNSUPPORTED;
+    if (M > kMaxSkinnyM || mode == QL_MODE_FAST) return QL_EUNSUPPORTED;
     p->path = QL_PATH_SKINNY;
+    p->mode = QL_MODE_EXACT;
     return QL_OK;
   }
   if (path != QL_PATH_GEMM && path != QL_PATH_SPLITK) return QL_EUNSUPPORTED;
   int tile = force_tile > 0 ? force_tile : env_int("QLINEAR_TILE", 0);
+  const ql::TileInfo *forced = tile > 0 ? ql::gemm_tile(tile) : nullptr;
+  if (tile > 0 && !forced) return QL_EUNSUPPORTED;
+  if (mode == QL_MODE_AUTO) {
+    if (forced) mode = forced->gen == 3 ? QL_MODE_FAST : QL_MODE_EXACT;
+    else mode = (tiled && path == QL_PATH_GEMM) ? QL_MODE_FAST : QL_MODE_EXACT;
+  }
+  if (mode != QL_MODE_EXACT && mode != QL_MODE_FAST) return QL_EINVAL;
+  p->mode = mode;
+  if (mode == QL_MODE_FAST) {
+    if (!tiled || path == QL_PATH_SPLITK || force_split > 1) return QL_EUNSUPPORTED;
+    if (forced && forced->gen != 3) return QL_EUNSUPPORTED;
+    p->path = QL_PATH_GEMM;
+    p->tile = kFastTile;
+    p->splits = 1;
+    p->groups_per_split = G;
+    p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
+    // QLINEAR_GEMM_SLOTS: resident-block count override, for tests of the
+    // split tail on small shapes
+    p->g3 = ql::gemm3_plan(M, N, G, env_int("QLINEAR_GEMM_SLOTS", 0));
+    p->ws_partial = p->g3.sk_partial_bytes;
+    return QL_OK;
+  }
+  if (forced && forced->gen == 3) return QL_EUNSUPPORTED;
   int splits = 0;
   if (tile <= 0) {
     for (const TableEntry &e : kTable) {
@@ -185,6 +215,9 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
       }
     }
     if (tile <= 0) tile = 1;
+    // exact mode on tiled codes: the second-generation kernel (the 256-row
+    // tile does not fit two blocks per CU with 8-bit codes)
+    if (tiled && !ql::gemm_tile_supports_tiled(tile)) tile = bits == 8 ? 11 : 10;
   }
   const ql::TileInfo *ti = ql::gemm_tile(tile);
   if (!ti) return QL_EUNSUPPORTED;
@@ -204,8 +237,7 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   p->ws_xsum = (size_t)G * (size_t)round_up(M, 256) * 4u;
   p->ws_partial = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4u : 0;
   if (ti->gen == 2) {
-    // QLINEAR_GEMM_SLOTS: resident-block count override, for tests of the
-    // split tail on small shapes
+    // QLINEAR_GEMM_SLOTS: as above
     p->g2 = ql::gemm2_plan(bits, tile, M, N, G, splits, env_int("QLINEAR_GEMM_SLOTS", 0));
     if (p->g2.sk_partial_bytes > p->ws_partial) p->ws_partial = p->g2.sk_partial_bytes;
   }
@@ -214,7 +246,7 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
 
 size_t plan_ws(const Plan &p) {
   if (p.path == QL_PATH_SKINNY) return 0;
-  return (size_t)round_up((int64_t)p.ws_xsum, 256) + p.ws_partial;
+  return (size_t)round_up((int64_t)p.ws_xsum, 256) + (size_t)round_up((int64_t)p.ws_x16, 256) + p.ws_partial;
 }
 
 int validate_forward(const ql_forward_args *a) {
@@ -224,6 +256,7 @@ int validate_forward(const ql_forward_args *a) {
   if (a->M > (1LL << 31) - 1 || a->N > (1LL << 31) - 1 || a->K > (1LL << 30)) return QL_EINVAL;
   if (a->out_dtype != QL_OUT_F32 && a->out_dtype != QL_OUT_BF16) return QL_EINVAL;
   if (a->layout != QL_LAYOUT_CANONICAL && a->layout != QL_LAYOUT_TILED) return QL_EINVAL;
+  if (a->mode != QL_MODE_AUTO && a->mode != QL_MODE_EXACT && a->mode != QL_MODE_FAST) return QL_EINVAL;
   if (a->M == 0 || a->N == 0) return QL_OK;
   if (!a->out) return QL_EINVAL;
   if (!aligned16(a->out)) return QL_EALIGN;
@@ -273,9 +306,13 @@ QL_API size_t qlinear_packed_words(int bits, int64_t N, int64_t K) {
 
 QL_API size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K) {
   if (!bits_ok(bits) || M <= 0 || N <= 0 || K <= 0 || K % kGroup) return 0;
-  Plan p;
-  if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, &p) != QL_OK) return 0;
-  return plan_ws(p);
+  // the larger of the canonical (exact) and tiled (fast) needs
+  Plan pc, pt;
+  size_t need = 0;
+  if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, false, QL_MODE_AUTO, &pc) == QL_OK) need = plan_ws(pc);
+  if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, QL_MODE_AUTO, &pt) == QL_OK && plan_ws(pt) > need)
+    need = plan_ws(pt);
+  return need;
 }
 
 QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
@@ -292,7 +329,8 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                                                                                                        : QL_EHIP;
   }
   Plan p;
-  st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, &p);
+  st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, a->layout == QL_LAYOUT_TILED, a->mode,
+                 &p);
   if (st != QL_OK) return st;
   const int G = (int)(a->K / kGroup);
   const int out_bf16 = a->out_dtype == QL_OUT_BF16;
@@ -318,6 +356,27 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   } else {
     st = get_owned_workspace(need, &ws);
     if (st != QL_OK) return st;
+  }
+  if (p.mode == QL_MODE_FAST) {
+    uint16_t *x16 = static_cast<uint16_t *>(ws);
+    float *rowscale = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up(a->M * a->K * 2, 256));
+    char *after = static_cast<char *>(ws) + round_up((int64_t)p.ws_x16, 256);
+    if (ql::launch_x16(static_cast<const uint16_t *>(a->x), x16, rowscale, a->M, a->K, stream) != hipSuccess)
+      return QL_EHIP;
+    ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales), a->out,
+                     a->M, a->N, a->K, G, out_bf16,
+                     p.g3.dp_tiles, p.g3.sk_tiles, p.g3.sk_pieces, p.g3.grid_x, nullptr, nullptr};
+    if (p.g3.sk_tiles > 0) {
+      const size_t part = (size_t)p.g3.sk_tiles * p.g3.sk_pieces * ti_sizes(p.tile);
+      g3.sk_partial = reinterpret_cast<float *>(after);
+      g3.sk_count = reinterpret_cast<int *>(after + round_up((int64_t)part * 4, 256));
+      if (ql::launch_fill_zero(g3.sk_count, p.g3.sk_tiles, 0, stream) != hipSuccess) return QL_EHIP;
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_tiled", a->bits, p.g3.sk_tiles, p.g3.sk_pieces);
+    } else {
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tiled", a->bits);
+    }
+    set_last_path(buf);
+    return ql::launch_gemm3(a->bits, g3, stream) == hipSuccess ? QL_OK : QL_EHIP;
   }
   int64_t Mp = round_up(a->M, 256);
   float *xsum = static_cast<float *>(ws);

@@ -30,7 +30,8 @@ struct GemmArgs {
 struct TileInfo {
   int id, bm, bn, warps_m, warps_n;
   const char *name;
-  int gen;  // 1: gemm.hip (canonical only), 2: gemm2.hip (canonical or tiled)
+  int gen;  // 1: gemm.hip (canonical, exact), 2: gemm2.hip (either layout, exact),
+            // 3: gemm3.hip (tiled, fast)
 };
 
 // GEMM tile configurations compiled into the library (id >= 1).
@@ -55,6 +56,31 @@ struct Gemm2Plan {
   size_t sk_partial_bytes;  // includes the counters, 256-byte aligned pieces
 };
 Gemm2Plan gemm2_plan(int bits, int tile_id, int64_t M, int64_t N, int G, int splits, int slots);
+// Fast mode (gemm3.hip): fp16 x with per-row power-of-two scales, tiled codes
+// dequantized to fp16 in LDS, 256 x 256 block tiles.
+struct Gemm3Args {
+  const uint16_t *x16;    // fp16 [M, K]
+  const float *rowscale;  // [M], 2^e per row
+  const uint32_t *w;      // tiled codes
+  const uint32_t *sb;     // tiled scale|bias words
+  void *out;              // [M, N] fp32 or bf16
+  int64_t M, N, K;
+  int G;
+  int out_bf16;
+  int dp_tiles, sk_tiles, sk_pieces, grid_x;
+  float *sk_partial;      // [sk_tiles, sk_pieces, 256*256]
+  int *sk_count;          // [sk_tiles], zero before the launch; left zero after it
+};
+struct Gemm3Plan {
+  int64_t tiles;
+  int dp_tiles, sk_tiles, sk_pieces, grid_x;
+  size_t sk_partial_bytes;
+};
+// slots <= 0: one block per CU of the current device
+Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots);
+hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream);
+hipError_t launch_gemm3(int bits, const Gemm3Args &a, hipStream_t stream);
+
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N,
                                 void *out, int out_bf16, hipStream_t stream);
 hipError_t launch_fill_zero(void *out, int64_t count, int out_bf16, hipStream_t stream);

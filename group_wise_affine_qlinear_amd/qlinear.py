@@ -21,6 +21,7 @@ QL_OK, QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP, QL_ERANGE 
 QL_OUT_F32, QL_OUT_BF16 = 0, 1
 QL_PATH_AUTO, QL_PATH_SKINNY, QL_PATH_GEMM, QL_PATH_SPLITK = 0, 1, 2, 3
 QL_LAYOUT_CANONICAL, QL_LAYOUT_TILED = 0, 1
+QL_MODE_AUTO, QL_MODE_EXACT, QL_MODE_FAST = 0, 1, 2
 
 EXPORTED = (
     "qlinear_forward", "qlinear_forward_ex", "qlinear_workspace_bytes", "qlinear_packed_words",
@@ -58,6 +59,7 @@ class ql_forward_args(ctypes.Structure):
         ("xsum", ctypes.c_void_p),
         ("ld_xsum", ctypes.c_int64),
         ("layout", ctypes.c_int),
+        ("mode", ctypes.c_int),
     ]
 
 
@@ -171,11 +173,13 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
 
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
                        workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
-                       xsum=None, layout=QL_LAYOUT_CANONICAL):
-    """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout and forced path.
+                       xsum=None, layout=QL_LAYOUT_CANONICAL, mode=QL_MODE_AUTO):
+    """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout, numerics mode
+    and forced path.
 
     With ``layout=QL_LAYOUT_TILED``, ``packed_q`` and ``scales`` are the outputs of
     ``qlinear_repack`` (tiled codes, tiled scale|bias words) and ``biases`` is ignored.
+    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights).
     """
     torch = _torch()
     u16 = _u16(torch)
@@ -203,7 +207,7 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
     if workspace is not None:
         a.workspace = _dev_ptr(workspace, "workspace", (workspace.dtype,))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
-    a.path, a.split_k, a.tile = path, split_k, tile
+    a.path, a.split_k, a.tile, a.mode = path, split_k, tile, mode
     if xsum is not None:
         a.xsum = _dev_ptr(xsum, "xsum", (torch.float32,))
         a.ld_xsum = xsum.shape[1]

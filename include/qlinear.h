@@ -65,6 +65,25 @@ typedef enum { QL_OUT_F32 = 0, QL_OUT_BF16 = 1 } ql_out_dtype;
  */
 typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
 
+/*
+ * Numerics of the large-M GEMM path.
+ * EXACT: codes enter the bf16 MFMA as exact integers and each group's scale
+ *   and bias are applied to the fp32 accumulator; the only rounding is fp32
+ *   accumulation (relative Frobenius error ~1e-6 against an fp64 product).
+ * FAST: each weight is dequantized once per block tile to fp16 with a single
+ *   rounding, W16 = fp16(s*q + b), and x enters as fp16 after scaling each
+ *   row by a power of two 2^-e (e >= 0, the smallest keeping the row below
+ *   2^15), exact for every scaled value of magnitude >= 2^-14; outputs are
+ *   scaled back by 2^e and accumulated in fp32 on fp16 MFMA. The added error
+ *   is the half-ulp of fp16 on W (relative Frobenius error ~2e-4 on normal
+ *   weights). Requires the TILED layout and |W| < 65504, which holds for
+ *   weights quantized from fp16-range values (W lies between b and
+ *   b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x.
+ * AUTO: FAST for the large-M path on TILED weights, EXACT otherwise. The
+ *   skinny (M <= 16) path is always EXACT.
+ */
+typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
+
 typedef enum {
   QL_PATH_AUTO = 0,      /* dispatch table decides                            */
   QL_PATH_SKINNY = 1,    /* wavefront GEMV kernel, M <= 16                    */
@@ -95,6 +114,9 @@ typedef struct ql_forward_args {
   int layout;                /* ql_layout. For QL_LAYOUT_TILED, packed_q holds
                                 the tiled codes, scales the tiled scale|bias
                                 words, and biases is ignored                */
+  int mode;                  /* ql_mode; FAST needs QL_LAYOUT_TILED and the
+                                GEMM path (path AUTO or GEMM), else
+                                QL_EUNSUPPORTED; xsum is unused in FAST     */
 } ql_forward_args;
 
 /*

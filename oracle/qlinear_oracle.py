@@ -31,6 +31,12 @@ bias that overflows f16, are rejected.
 Every function here is pinned by ``tests/test_oracle.py`` to facts other than
 itself (hand-worked examples, exact rational arithmetic, brute force, closed
 forms, special cases).
+
+The library's FAST mode is an approximation of the product above that the
+pages do not describe; ``forward_fast`` writes out its definition (weights
+rounded once to fp16, activations scaled per row by a power of two into
+fp16) so the GPU path can be compared with it to fp32-accumulation accuracy,
+while ``forward`` remains the reference for the error budget.
 """
 from __future__ import annotations
 
@@ -44,6 +50,7 @@ __all__ = [
     "f16_bits_to_f32", "f32_to_f16_bits", "bf16_bits_to_f64",
     "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
     "forward_rows", "error_metrics", "timed_forward",
+    "fast_weights_f16", "fast_activations_f16", "forward_fast",
 ]
 
 GROUP = 64
@@ -220,6 +227,46 @@ def forward_rows(x_bf16, packed, s16, b16, bits, k, rows, cols=None, group: int 
         cols = np.asarray(cols)
         packed, s16, b16 = packed[cols], s16[cols], b16[cols]
     return forward(x_sel, packed, s16, b16, bits, k, group)
+
+
+def fast_weights_f16(q: np.ndarray, s16: np.ndarray, b16: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """FAST-mode weights: s*q + b rounded once to fp16 (nearest, ties to even).
+
+    With s, b in f16 and q < 256 the value s*q + b is exact in float64, so the
+    float64 -> float16 conversion is the only rounding.
+    """
+    q = np.asarray(q)
+    n, k = q.shape
+    g = k // group
+    s = f16_bits_to_f32(s16).astype(np.float64).reshape(n, g, 1)
+    b = f16_bits_to_f32(b16).astype(np.float64).reshape(n, g, 1)
+    w = s * q.astype(np.float64).reshape(n, g, group) + b
+    return w.reshape(n, k).astype(np.float16)
+
+
+def fast_activations_f16(x_bf16: np.ndarray):
+    """FAST-mode activations: per row the smallest e >= 0 with max|x|*2^-e < 2^15,
+    then x*2^-e rounded to fp16 (exact for |x*2^-e| >= 2^-14). Returns
+    (x16 as float16 [M, K], 2^e as float64 [M])."""
+    x = bf16_bits_to_f64(x_bf16)
+    m = x.shape[0]
+    scale = np.ones(m, dtype=np.float64)
+    for r in range(m):
+        mx = float(np.max(np.abs(x[r]))) if x.shape[1] else 0.0
+        e = 0
+        while mx * 2.0 ** -e >= 32768.0 and e < 120:
+            e += 1
+        scale[r] = 2.0 ** e
+    x16 = (x / scale[:, None]).astype(np.float16)
+    return x16, scale
+
+
+def forward_fast(x_bf16, packed, s16, b16, bits, k, group: int = GROUP) -> np.ndarray:
+    """FAST-mode product: 2^e_row * (x16 @ W16^T), accumulated in float64."""
+    q = unpack(packed, bits, k)
+    w16 = fast_weights_f16(q, s16, b16, group).astype(np.float64)
+    x16, scale = fast_activations_f16(x_bf16)
+    return scale[:, None] * (x16.astype(np.float64) @ w16.T)
 
 
 def error_metrics(y: np.ndarray, y_ref: np.ndarray) -> dict:

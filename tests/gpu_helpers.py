@@ -61,7 +61,7 @@ class Case:
 
 
 def run_forward(torch, case, path=ql.QL_PATH_AUTO, split_k=0, tile=0, out_dtype="f32", via_ex=True,
-                layout=ql.QL_LAYOUT_CANONICAL):
+                layout=ql.QL_LAYOUT_CANONICAL, mode=ql.QL_MODE_AUTO):
     x, p, s, b = case.device(torch)
     if layout == ql.QL_LAYOUT_TILED:
         p, s = ql.qlinear_repack(p, s, b, case.bits, 64, case.N, case.K)
@@ -72,7 +72,7 @@ def run_forward(torch, case, path=ql.QL_PATH_AUTO, split_k=0, tile=0, out_dtype=
         out = torch.zeros((case.M, case.N), dtype=torch.bfloat16, device="cuda")
     if via_ex:
         ql.qlinear_forward_ex(x, p, s, b, case.bits, case.M, case.N, case.K, out, path=path,
-                              split_k=split_k, tile=tile, layout=layout)
+                              split_k=split_k, tile=tile, layout=layout, mode=mode)
     else:
         ql.qlinear_forward(x, p, s, b, case.bits, 64, case.M, case.N, case.K, out)
     torch.cuda.synchronize()

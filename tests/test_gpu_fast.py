@@ -1,0 +1,150 @@
+"""GPU tests of the FAST numerics mode (fp16 dequant-GEMM on tiled weights).
+
+Each case is compared twice: with the oracle's written-out definition of the
+mode (``oracle.forward_fast``: weights rounded once to fp16, rows scaled by a
+power of two into fp16), where only fp32 accumulation separates the two, and
+with the exact product (``oracle.forward``) under the acceptance bound and the
+mode's own error budget (fp16 half-ulp on the weights)."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs, qlinear as ql
+
+from gpu_helpers import (Case, MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, assert_parity, dev,
+                         run_forward, torch_or_skip)
+
+pytestmark = pytest.mark.gpu
+
+# error budget of the mode against the exact product: fp16 rounding of W
+# (relative ~2^-11/sqrt(3) per weight, 1.7e-4 relative Frobenius on these
+# weights) with room for the max over ~1e6 outputs
+RELF_FAST = 5e-4
+MAXABS_RMS_FAST = 4e-3
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_or_skip()
+    ql.load_library()
+    return t
+
+
+def check_fast(y, c):
+    y = np.asarray(y, dtype=np.float64)
+    assert np.all(np.isfinite(y)), "non-finite output"
+    ref_def = oracle.forward_fast(c.x, c.packed, c.s16, c.b16, c.bits, c.K)
+    e = oracle.error_metrics(y, ref_def)
+    assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, ("vs definition", e)
+    e2 = oracle.error_metrics(y, c.reference())
+    assert e2["relF"] <= RELF_TOL and e2["maxabs_over_rms"] <= MAXABS_RMS_TOL, ("vs exact, acceptance", e2)
+    assert e2["relF"] <= RELF_FAST and e2["maxabs_over_rms"] <= MAXABS_RMS_FAST, ("vs exact, budget", e2)
+
+
+FAST_SHAPES = [(520, 390, 320), (300, 520, 640), (17, 40, 64), (256, 256, 512), (777, 1000, 448)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("shape", FAST_SHAPES)
+def test_fast_parity(torch, shape, bits):
+    M, N, K = shape
+    c = Case(M, N, K, bits, wid=400 + bits, x_structure="outlier")
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST)
+    assert ql.qlinear_last_path().startswith("gemm3"), ql.qlinear_last_path()
+    check_fast(y.cpu().numpy(), c)
+
+
+def test_fast_is_auto_choice_for_tiled_large_m(torch):
+    c = Case(64, 256, 256, 4, wid=410)
+    run_forward(torch, c, layout=ql.QL_LAYOUT_TILED)
+    assert ql.qlinear_last_path().startswith("gemm3")
+    run_forward(torch, c)
+    assert not ql.qlinear_last_path().startswith("gemm3")
+    run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
+    assert ql.qlinear_last_path().startswith("gemm2")
+    c8 = Case(8, 256, 256, 4, wid=411)   # skinny M is always exact
+    run_forward(torch, c8, layout=ql.QL_LAYOUT_TILED)
+    assert ql.qlinear_last_path().startswith("skinny")
+
+
+def test_fast_rejects_unsupported_requests(torch):
+    c = Case(64, 256, 256, 4, wid=412)
+    with pytest.raises(ql.QLinearError):   # canonical layout
+        run_forward(torch, c, mode=ql.QL_MODE_FAST)
+    with pytest.raises(ql.QLinearError):   # split-K path
+        run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=ql.QL_PATH_SPLITK)
+    with pytest.raises(ql.QLinearError):   # skinny path
+        run_forward(torch, Case(4, 256, 256, 4, wid=413), layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST,
+                    path=ql.QL_PATH_SKINNY)
+
+
+def test_fast_rows_scaled_into_fp16_range(torch):
+    M, N, K = 64, 256, 512
+    x = inputs.activations_f32(M, K, 420)
+    x[3] *= 1.0e5          # |x| up to ~5e5: needs e > 0
+    x[7, 100] = 70000.0    # one large value in an otherwise normal row
+    x[11] *= 2.0 ** -20    # small row: values in the fp16 subnormal range
+    c = Case(M, N, K, 4, wid=420, x=inputs.f32_to_bf16_bits(x))
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    ref_def = oracle.forward_fast(c.x, c.packed, c.s16, c.b16, 4, K)
+    for r in range(M):   # row by row: the rows differ in scale by 10^5
+        e = oracle.error_metrics(y[r:r + 1], ref_def[r:r + 1])
+        assert e["relF"] <= RELF_DESIGN, (r, e)
+
+
+def test_fast_one_hot_rows_give_fp16_weights_exactly(torch):
+    K, N, M = 512, 100, 24
+    cols = np.arange(M) * 21 % K
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), cols] = 0x3F80   # 1.0
+    c = Case(M, N, K, 4, wid=430, x=x)
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    w16 = oracle.fast_weights_f16(c.q, c.s16, c.b16).astype(np.float32)
+    assert np.array_equal(y, w16[:, cols].T)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_fast_bf16_out_is_rounded_fp32_out(torch, bits):
+    c = Case(300, 260, 384, bits, wid=440 + bits)
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    yb = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, out_dtype="bf16")
+    got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(y))
+
+
+# split tail and multi-tile blocks with the resident-block count forced small: (slots, shape)
+FAST_TAIL_CASES = [
+    (4, (520, 1000, 640)),    # 12 tiles over 4 blocks: 3 whole tiles per block, no split
+    (5, (520, 1000, 640)),    # 12 tiles: 10 whole, 2 tail tiles x 2 pieces (G=10: 5+5)
+    (3, (300, 600, 448)),     # 6 tiles over 3 blocks: 2 whole tiles per block (G=7, odd)
+    (4, (300, 600, 448)),     # 6 tiles: 4 whole, 2 tail tiles x 2 pieces (G=7: 4+3)
+    (7, (520, 520, 576)),     # 9 tiles: 7 whole, 2 tail tiles x 3 pieces (G=9: 3+3+3)
+]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("slots,shape", FAST_TAIL_CASES)
+def test_fast_split_tail(torch, monkeypatch, slots, shape, bits):
+    M, N, K = shape
+    monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
+    c = Case(M, N, K, bits, wid=450 + bits)
+    y1 = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    check_fast(y1, c)
+    y2 = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("K", [4608, 8192, 9216])
+def test_fast_prepass_row_widths(torch, K):
+    # rows held in registers (K <= 8192, two vector counts) and the two-pass
+    # conversion for wider rows; one row per scale regime
+    M, N = 40, 64
+    x = inputs.activations_f32(M, K, 460)
+    x[5] *= 3.0e5
+    x[9] *= 2.0 ** -18
+    c = Case(M, N, K, 4, wid=460, x=inputs.f32_to_bf16_bits(x))
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    ref_def = oracle.forward_fast(c.x, c.packed, c.s16, c.b16, 4, K)
+    for r in range(M):
+        e = oracle.error_metrics(y[r:r + 1], ref_def[r:r + 1])
+        assert e["relF"] <= RELF_DESIGN, (r, e)

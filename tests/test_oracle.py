@@ -402,3 +402,83 @@ def test_signed_zero_ordering_in_min_max():
     assert int(b16[0, 0]) == 0x8000 and int(s16[0, 0]) == 0x0000
     assert int(b16[1, 0]) == 0x8000 and int(s16[1, 0]) == 0x0000
     assert not q.any()
+
+
+# ----------------------------------------------------------------- FAST-mode definition
+
+def test_fast_weights_single_rounding_matches_exact_rne():
+    # every code of several (scale, bias) pairs, including full-mantissa scales
+    # whose s*q + b needs more than 11 bits, against exact rational rounding
+    rng = np.random.default_rng(5)
+    s_bits = [0x3555, 0x2E66, 0x1C01, 0x3BFF] + list(rng.integers(0x1000, 0x3C00, 6))
+    b_bits = [0xBC01, 0x3C01, 0x0000, 0xC3FF] + list(rng.integers(0x8400, 0xC000, 6))
+    for bits in (2, 4, 8):
+        qmax = 2 ** bits - 1
+        for sb, bb in zip(s_bits, b_bits):
+            q = np.arange(64, dtype=np.int64).reshape(1, 64) % (qmax + 1)
+            s16 = np.array([[sb]], np.uint16)
+            b16 = np.array([[bb]], np.uint16)
+            got = oracle.fast_weights_f16(q, s16, b16).view(np.uint16)[0]
+            for k in range(64):
+                exact = f16_value(int(sb)) * int(q[0, k]) + f16_value(int(bb))
+                assert int(got[k]) == exact_f16_rne(exact), (bits, hex(sb), hex(bb), k)
+
+
+def test_fast_weights_tie_goes_to_even():
+    # s = 0.5, b = 2048: q = 2 gives 2049, halfway between 2048 and 2050 -> 2048
+    q = np.array([[2, 6] + [0] * 62])
+    s16 = np.array([[0x3800]], np.uint16)  # 0.5
+    b16 = np.array([[0x6800]], np.uint16)  # 2048
+    w = oracle.fast_weights_f16(q, s16, b16).astype(np.float64)[0]
+    assert w[0] == 2048.0 and w[1] == 2052.0   # 2051 is also a tie: 2050 (odd) -> 2052 (even)
+
+
+def test_fast_equals_exact_when_everything_is_representable():
+    rng = np.random.default_rng(8)
+    n, k, m = 12, 128, 5
+    q = rng.integers(0, 16, (n, k))
+    s16 = np.full((n, k // 64), 0x3400, np.uint16)   # 0.25
+    b16 = np.full((n, k // 64), 0xC000, np.uint16)   # -2
+    packed = oracle.pack(q, 4)
+    xb = inputs.f32_to_bf16_bits(rng.integers(-8, 9, (m, k)).astype(np.float32))
+    assert np.array_equal(oracle.forward_fast(xb, packed, s16, b16, 4, k),
+                          oracle.forward(xb, packed, s16, b16, 4, k))
+
+
+def test_fast_row_scaling_is_a_power_of_two():
+    k = 64
+    x = np.zeros((4, k), np.float32)
+    x[0, :3] = [65536.0, -3.0, 0.5]     # max 2^16 -> e = 2 (2^16 / 4 = 2^14 < 2^15)
+    x[1, 0] = 32768.0                   # exactly 2^15 is not below 2^15 -> e = 1
+    x[2, 0] = 32512.0                   # largest bf16 below 2^15 -> e = 0
+    x[3, 0] = -3.0e38                   # near the top of the bf16 range
+    xb = inputs.f32_to_bf16_bits(x)
+    x16, scale = oracle.fast_activations_f16(xb)
+    assert list(scale[:3]) == [4.0, 2.0, 1.0]
+    e3 = int(round(math.log2(scale[3])))
+    xmax = float(oracle.bf16_bits_to_f64(xb[3:4, :1])[0, 0])
+    assert abs(xmax) * 2.0 ** -e3 < 32768 <= abs(xmax) * 2.0 ** -(e3 - 1)
+    # scaled values that are powers of two or small integers stay exact
+    assert float(x16[0, 0]) * 4 == 65536.0 and float(x16[0, 1]) * 4 == -3.0 and float(x16[0, 2]) * 4 == 0.5
+
+
+def test_fast_activation_subnormals_round_to_nearest():
+    vals = [2.0 ** -20, 1.5 * 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 * (1 + 2.0 ** -7)]
+    xb = inputs.f32_to_bf16_bits(np.array([vals], np.float32))
+    x16, scale = oracle.fast_activations_f16(xb)
+    assert scale[0] == 1.0
+    for v, got in zip(oracle.bf16_bits_to_f64(xb)[0], x16.view(np.uint16)[0]):
+        assert int(got) == exact_f16_rne(Fraction(float(v))), v
+
+
+def test_fast_error_budget_on_normal_weights():
+    # the FAST mode's only extra rounding is fp16 on W: relative Frobenius error
+    # ~2^-11 / sqrt(3) per weight, far inside the 2e-3 acceptance bound
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    packed = oracle.pack(q, 4)
+    xb = inputs.f32_to_bf16_bits(rng.standard_normal((48, 512)).astype(np.float32))
+    e = oracle.error_metrics(oracle.forward_fast(xb, packed, s16, b16, 4, 512),
+                             oracle.forward(xb, packed, s16, b16, 4, 512))
+    assert 5e-5 < e["relF"] < 5e-4 and e["maxabs_over_rms"] < 3e-3, e
