@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the group-wise affine quantized linear hot path on one MI355X.
 
-One step = one pass of the path over one batch: per-group row sums of x
-(qlinear_group_sums) followed by the fused dequant-GEMM (qlinear_forward_ex),
-i.e. exactly the kernels qlinear_forward launches, at the headline workload
-M=4096 tokens, K=N=4608, 4-bit codes, group 64 (square projection of the 4608-wide
-DiT at 1024x1024). Inputs are seeded synthetic tensors already resident in HBM
-when the timed region starts; weights are quantized by the library's device RTN
-quantizer during setup.
+One step = one pass of the path over one batch at the headline workload
+M=4096 tokens, K=N=4608, 4-bit codes, group 64 (square projection of the
+4608-wide DiT at 1024x1024): the activation prepass (qlinear_fast_activations:
+bf16 x to fp16 with per-row power-of-two scales) followed by the fused
+dequant-GEMM on tiled weights (qlinear_forward_ex, FAST mode), i.e. exactly the
+kernels qlinear_forward_ex launches for this layer. Weights are quantized by the
+library's device RTN quantizer and repacked to the tiled layout during setup, as
+a loader does once per checkpoint; inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.
 
 Printed: one JSON line with the whole-job throughput (TFLOP/s), the roofline of
 the dominant kernel (fused GEMM, timed live with HIP events on its stream), the
-skinny-M and split-K rows of the path as secondary measurements, and the CPU
-oracle timed on this host as a reported baseline.
+exact-mode, skinny-M and text-conditioning rows as secondary measurements, and
+the CPU oracle timed on this host as a reported baseline.
 """
 from __future__ import annotations
 
@@ -28,9 +30,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "qlinear TFLOP/s (M=4096,K=N=4608, Q4 g64) + % MFMA peak; GB/s skinny-M"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 WORKLOAD = dict(name="dit_square_proj_M4096_K4608_N4608_q4_g64", M=4096, K=4608, N=4608, bits=4, wid=6)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_q4_M4096_K4608_N4608_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm3_fast_q4_M4096_K4608_N4608_traffic.txt")
 
 
 def log(msg):
@@ -40,7 +43,7 @@ def log(msg):
 
 def gemm_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "ql_device.h"):
+    for f in ("gemm3.hip", "ql_device.h"):
         with open(os.path.join(ROOT, "group_wise_affine_qlinear_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -50,7 +53,9 @@ def algorithmic_bytes(M, N, K, bits):
     return N * K * bits / 8 + 4 * N * K / 64 + 2 * M * K + 4 * M * N
 
 
-def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1):
+def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1, tiled=False):
+    """Device-quantized weight sets; tiled=True repacks each set for the GEMM kernels
+    (then a set is (tiled_q, tiled_sb, None))."""
     w = torch.from_numpy(inputs.weights(N, K, wid)).cuda()
     sets = []
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -59,7 +64,12 @@ def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1):
         s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
         b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
         ql.qlinear_quantize_rtn(w, bits, 64, N, K, p, s, b, status)
-        sets.append((p, s, b))
+        if tiled:
+            tq, tsb = ql.qlinear_repack(p, s, b, bits, 64, N, K)
+            sets.append((tq, tsb, None))
+            del p, s, b
+        else:
+            sets.append((p, s, b))
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError("quantizer reported a range error")
@@ -83,48 +93,71 @@ def time_calls(torch, fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
-def secondary_rows(torch, ql, inputs):
+def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     rows = {}
+    M, K, N, bits = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"], WORKLOAD["bits"]
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    p, s, _ = exact_sets
+
+    def fe():
+        ql.qlinear_forward_ex(x_main, p, s, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
+                              mode=ql.QL_MODE_EXACT)
+
+    ms = time_calls(torch, fe, 20, 5)
+    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+    rows[f"exact_mode_M{M}_K{K}_N{N}_q{bits}"] = {
+        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+        "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
+    log(f"exact mode: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
+    del out
+
     K, N = 4608, 27648
     for M in (1, 8):
-        copies = 8  # 8 x 71.7 MB of distinct weights > 256 MB Infinity Cache
-        sets = make_weights(torch, ql, inputs, N, K, 4, 40 + (M > 1), copies)
-        x = torch.from_numpy(inputs.activations_bf16(M, K, 40 + (M > 1)).view("int16")).cuda()
-        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        i = [0]
+        for tiled in (False, True):
+            copies = 8  # 8 x 71.7 MB of distinct weights > 256 MB Infinity Cache
+            sets = make_weights(torch, ql, inputs, N, K, 4, 40 + (M > 1), copies, tiled=tiled)
+            x = torch.from_numpy(inputs.activations_bf16(M, K, 40 + (M > 1)).view("int16")).cuda()
+            out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
+            i = [0]
 
-        def fn():
-            p, s, b = sets[i[0] % copies]
-            i[0] += 1
-            ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out)
+            def fn():
+                p, s, b = sets[i[0] % copies]
+                i[0] += 1
+                ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out, layout=layout)
 
-        ms = time_calls(torch, fn, 64, 16)
-        by = algorithmic_bytes(M, N, K, 4)
-        gbs = by / (ms * 1e-3) / 1e9
-        rows[f"adaln_skinny_M{M}_K{K}_N{N}_q4"] = {
-            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies_rotated": copies}
-        del sets
-        log(f"skinny M={M}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+            ms = time_calls(torch, fn, 64, 16)
+            by = algorithmic_bytes(M, N, K, 4)
+            gbs = by / (ms * 1e-3) / 1e9
+            lname = "tiled" if tiled else "canonical"
+            rows[f"adaln_skinny_M{M}_K{K}_N{N}_q4_{lname}"] = {
+                "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies_rotated": copies}
+            del sets
+            log(f"skinny M={M} {lname}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+
     M, K, N = 512, 53248, 4608
     copies = 4
-    sets = make_weights(torch, ql, inputs, N, K, 4, 4, copies)
     x = torch.from_numpy(inputs.activations_bf16(M, K, 4, "slices").view("int16")).cuda()
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    i = [0]
+    for tiled in (False, True):
+        sets = make_weights(torch, ql, inputs, N, K, 4, 4, copies, tiled=tiled)
+        layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
+        i = [0]
 
-    def fn2():
-        p, s, b = sets[i[0] % copies]
-        i[0] += 1
-        ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out)
+        def fn2():
+            p, s, b = sets[i[0] % copies]
+            i[0] += 1
+            ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out, layout=layout)
 
-    ms = time_calls(torch, fn2, 20, 5)
-    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-    rows["llm_cond_proj_M512_K53248_N4608_q4"] = {
-        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-        "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "weight_copies_rotated": copies}
-    log(f"llm_cond_proj: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
-    del sets
+        ms = time_calls(torch, fn2, 20, 5)
+        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+        lname = "tiled" if tiled else "canonical"
+        rows[f"llm_cond_proj_M512_K53248_N4608_q4_{lname}"] = {
+            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+            "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "weight_copies_rotated": copies}
+        log(f"llm_cond_proj {lname}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
+        del sets
     return rows
 
 
@@ -197,10 +230,11 @@ def main():
 
     M, K, N, bits = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"], WORKLOAD["bits"]
     log(f"setup {WORKLOAD['name']}")
-    (p, s, b), = make_weights(torch, ql, inputs, N, K, bits, WORKLOAD["wid"])
+    (p, s, _), = make_weights(torch, ql, inputs, N, K, bits, WORKLOAD["wid"], tiled=True)
     x = torch.from_numpy(inputs.activations_bf16(M, K, WORKLOAD["wid"]).view("int16")).cuda()
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    xsum = torch.empty((K // 64, ql.qlinear_group_sums_ld(M)), dtype=torch.float32, device="cuda")
+    x16 = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    rowscale = torch.empty((M,), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     steps, warmup = args.steps, args.warmup
@@ -212,10 +246,11 @@ def main():
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        ql.qlinear_group_sums(x, M, K, xsum, stream=stream)
+        ql.qlinear_fast_activations(x, M, K, x16, rowscale, stream=stream)
         if evs:
             evs[1].record(stream)
-        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, xsum=xsum, stream=stream)
+        ql.qlinear_forward_ex(x, p, s, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
+                              mode=ql.QL_MODE_FAST, x16=x16, rowscale=rowscale, stream=stream)
         if evs:
             evs[2].record(stream)
 
@@ -234,13 +269,13 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / steps
     gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    sums_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     flop = 2.0 * M * N * K
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (gemm_ms * 1e-3) / 1e12
-    log(f"step {ms_step*1e3:.1f} us (group sums {sums_ms*1e3:.1f} us, gemm {gemm_ms*1e3:.1f} us) -> {value:.1f} TFLOP/s")
+    log(f"step {ms_step*1e3:.1f} us (prepass {pre_ms*1e3:.1f} us, gemm {gemm_ms*1e3:.1f} us) -> {value:.1f} TFLOP/s")
 
-    secondary = {} if args.no_secondary else secondary_rows(torch, ql, inputs)
+    secondary = {} if args.no_secondary else secondary_rows(torch, ql, inputs, (p, s, None), x)
     src_hash = gemm_source_hash()
     traffic = load_traffic(src_hash)
 
@@ -255,14 +290,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD["name"], "M": M, "K": K, "N": N, "bits": bits, "group": 64,
-                   "path": path, "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "fused dequant-GEMM", "kernel_us": round(gemm_ms * 1e3, 2),
-                     "group_sums_us": round(sums_ms * 1e3, 2), "kernel_source_sha": src_hash},
+                   "path": path, "mode": "fast", "layout": "tiled", "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fused dequant-GEMM (fp16 MFMA)", "kernel_us": round(gemm_ms * 1e3, 2),
+                     "prepass_us": round(pre_ms * 1e3, 2), "kernel_source_sha": src_hash},
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:

@@ -257,6 +257,7 @@ int validate_forward(const ql_forward_args *a) {
   if (a->out_dtype != QL_OUT_F32 && a->out_dtype != QL_OUT_BF16) return QL_EINVAL;
   if (a->layout != QL_LAYOUT_CANONICAL && a->layout != QL_LAYOUT_TILED) return QL_EINVAL;
   if (a->mode != QL_MODE_AUTO && a->mode != QL_MODE_EXACT && a->mode != QL_MODE_FAST) return QL_EINVAL;
+  if ((a->x16 == nullptr) != (a->rowscale == nullptr)) return QL_EINVAL;
   if (a->M == 0 || a->N == 0) return QL_OK;
   if (!a->out) return QL_EINVAL;
   if (!aligned16(a->out)) return QL_EALIGN;
@@ -273,6 +274,7 @@ int validate_forward(const ql_forward_args *a) {
     if (a->ld_xsum < round_up(a->M, 256) || a->ld_xsum % 4) return QL_EINVAL;
     if (!aligned16(a->xsum)) return QL_EALIGN;
   }
+  if (a->x16 && !aligned16(a->x16)) return QL_EALIGN;
   return QL_OK;
 }
 
@@ -348,6 +350,7 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     return ql::launch_skinny(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;
   }
   if (a->layout == QL_LAYOUT_TILED && !ql::gemm_tile_supports_tiled(p.tile)) return QL_EUNSUPPORTED;
+  if (p.mode == QL_MODE_FAST && a->x16) p.ws_x16 = 0;  // caller's fp16 activations
   const size_t need = plan_ws(p);
   void *ws = a->workspace;
   if (ws) {
@@ -358,11 +361,17 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     if (st != QL_OK) return st;
   }
   if (p.mode == QL_MODE_FAST) {
-    uint16_t *x16 = static_cast<uint16_t *>(ws);
-    float *rowscale = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up(a->M * a->K * 2, 256));
+    const uint16_t *x16 = static_cast<const uint16_t *>(a->x16);
+    const float *rowscale = a->rowscale;
     char *after = static_cast<char *>(ws) + round_up((int64_t)p.ws_x16, 256);
-    if (ql::launch_x16(static_cast<const uint16_t *>(a->x), x16, rowscale, a->M, a->K, stream) != hipSuccess)
-      return QL_EHIP;
+    if (!x16) {
+      uint16_t *x16w = static_cast<uint16_t *>(ws);
+      float *rsw = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up(a->M * a->K * 2, 256));
+      if (ql::launch_x16(static_cast<const uint16_t *>(a->x), x16w, rsw, a->M, a->K, stream) != hipSuccess)
+        return QL_EHIP;
+      x16 = x16w;
+      rowscale = rsw;
+    }
     ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales), a->out,
                      a->M, a->N, a->K, G, out_bf16,
                      p.g3.dp_tiles, p.g3.sk_tiles, p.g3.sk_pieces, p.g3.grid_x, nullptr, nullptr};
@@ -428,6 +437,19 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
 }
 
 QL_API int64_t qlinear_group_sums_ld(int64_t M) { return M <= 0 ? 0 : round_up(M, 256); }
+
+QL_API int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x16, float *rowscale,
+                                    void *stream) {
+  if (M < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (M == 0 || K == 0) return QL_OK;
+  if (!x || !x16 || !rowscale) return QL_EINVAL;
+  if (!aligned16(x) || !aligned16(x16)) return QL_EALIGN;
+  set_last_path("fast_activations");
+  return ql::launch_x16(static_cast<const uint16_t *>(x), static_cast<uint16_t *>(x16), rowscale, M, K,
+                        reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
 
 QL_API int qlinear_group_sums(const void *x, int64_t M, int64_t K, float *xsum, int64_t ld_xsum, void *stream) {
   if (M < 0 || K < 0 || K % kGroup) return QL_EINVAL;

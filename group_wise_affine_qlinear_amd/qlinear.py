@@ -28,7 +28,7 @@ EXPORTED = (
     "qlinear_pack_host", "qlinear_unpack_host", "qlinear_quantize_rtn_host", "qlinear_quantize_rtn",
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
     "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
-    "qlinear_repack", "qlinear_unrepack",
+    "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations",
 )
 
 
@@ -60,6 +60,8 @@ class ql_forward_args(ctypes.Structure):
         ("ld_xsum", ctypes.c_int64),
         ("layout", ctypes.c_int),
         ("mode", ctypes.c_int),
+        ("x16", ctypes.c_void_p),
+        ("rowscale", ctypes.c_void_p),
     ]
 
 
@@ -99,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_version": ([], i32),
         "qlinear_group_sums": ([vp, i64, i64, vp, i64, vp], i32),
         "qlinear_group_sums_ld": ([i64], i64),
+        "qlinear_fast_activations": ([vp, i64, i64, vp, vp, vp], i32),
         "qlinear_tiled_words": ([i32, i64, i64], sz),
         "qlinear_tiled_sb_words": ([i64, i64], sz),
         "qlinear_repack": ([vp, vp, vp, i32, i32, i64, i64, vp, vp, vp], i32),
@@ -173,13 +176,15 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
 
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
                        workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
-                       xsum=None, layout=QL_LAYOUT_CANONICAL, mode=QL_MODE_AUTO):
+                       xsum=None, layout=QL_LAYOUT_CANONICAL, mode=QL_MODE_AUTO, x16=None,
+                       rowscale=None):
     """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout, numerics mode
     and forced path.
 
     With ``layout=QL_LAYOUT_TILED``, ``packed_q`` and ``scales`` are the outputs of
     ``qlinear_repack`` (tiled codes, tiled scale|bias words) and ``biases`` is ignored.
-    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights).
+    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights);
+    ``x16``/``rowscale`` are optional FAST-mode activations from ``qlinear_fast_activations``.
     """
     torch = _torch()
     u16 = _u16(torch)
@@ -213,6 +218,9 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
         a.ld_xsum = xsum.shape[1]
         if xsum.dim() != 2 or xsum.shape[0] != K // group:
             raise ValueError("xsum must be [K/64, ld_xsum]")
+    if x16 is not None:
+        a.x16 = _dev_ptr(x16, "x16", (torch.float16, torch.int16), (M, K))
+        a.rowscale = _dev_ptr(rowscale, "rowscale", (torch.float32,), (M,))
     st = lib.qlinear_forward_ex(ctypes.byref(a), _stream_handle(stream))
     _check(st, "qlinear_forward_ex")
     return out
@@ -234,6 +242,22 @@ def qlinear_group_sums(x, M, K, xsum=None, stream=None):
                                 _stream_handle(stream))
     _check(st, "qlinear_group_sums")
     return xsum
+
+
+def qlinear_fast_activations(x, M, K, x16=None, rowscale=None, stream=None):
+    """C ``qlinear_fast_activations``: fp16 x with per-row power-of-two scales (FAST mode)."""
+    torch = _torch()
+    lib = load_library()
+    if x16 is None:
+        x16 = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    if rowscale is None:
+        rowscale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    st = lib.qlinear_fast_activations(_dev_ptr(x, "x", _u16(torch), (M, K)), M, K,
+                                      _dev_ptr(x16, "x16", (torch.float16, torch.int16), (M, K)),
+                                      _dev_ptr(rowscale, "rowscale", (torch.float32,), (M,)),
+                                      _stream_handle(stream))
+    _check(st, "qlinear_fast_activations")
+    return x16, rowscale
 
 
 def qlinear_tiled_words(bits, N, K) -> int:

@@ -78,7 +78,8 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  *   is the half-ulp of fp16 on W (relative Frobenius error ~2e-4 on normal
  *   weights). Requires the TILED layout and |W| < 65504, which holds for
  *   weights quantized from fp16-range values (W lies between b and
- *   b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x.
+ *   b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x
+ *   unless the caller passes it (qlinear_fast_activations, x16/rowscale).
  * AUTO: FAST for the large-M path on TILED weights, EXACT otherwise. The
  *   skinny (M <= 16) path is always EXACT.
  */
@@ -117,6 +118,11 @@ typedef struct ql_forward_args {
   int mode;                  /* ql_mode; FAST needs QL_LAYOUT_TILED and the
                                 GEMM path (path AUTO or GEMM), else
                                 QL_EUNSUPPORTED; xsum is unused in FAST     */
+  const void *x16;           /* optional, FAST only: fp16 [M, K] activations
+                                and                                         */
+  const float *rowscale;     /* [M] row scales from qlinear_fast_activations
+                                for this x; both NULL = computed inside the
+                                call (both or neither must be given)        */
 } ql_forward_args;
 
 /*
@@ -150,6 +156,18 @@ int qlinear_group_sums(const void *x, int64_t M, int64_t K, float *xsum, int64_t
 
 /* Minimum row pitch (floats) of a group-sum buffer for M rows. */
 int64_t qlinear_group_sums_ld(int64_t M);
+
+/*
+ * FAST-mode activations (see ql_mode): for each row m of the bf16 [M, K]
+ * input, e = the smallest integer >= 0 with max_k |x[m,k]| * 2^-e < 2^15;
+ * x16[m, k] = fp16(x[m, k] * 2^-e) (round to nearest even; exact for scaled
+ * magnitudes >= 2^-14) and rowscale[m] = 2^e. x16 is [M, K] fp16 (16-byte
+ * aligned), rowscale [M] fp32. Several projections of the same x (Q/K/V,
+ * gate/up) can share one call by passing the results in ql_forward_args.
+ * Returns QL_EINVAL for bad sizes or null pointers, QL_EALIGN for misaligned
+ * x or x16.
+ */
+int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x16, float *rowscale, void *stream);
 
 /* Bytes of device workspace qlinear_forward_ex needs for this shape under
  * automatic dispatch (an upper bound over all paths and splits it may pick). */

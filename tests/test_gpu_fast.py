@@ -148,3 +148,36 @@ def test_fast_prepass_row_widths(torch, K):
     for r in range(M):
         e = oracle.error_metrics(y[r:r + 1], ref_def[r:r + 1])
         assert e["relF"] <= RELF_DESIGN, (r, e)
+
+
+def test_fast_activations_match_definition_bitwise(torch):
+    # the standalone prepass: fp16 codes and row scales equal the oracle's
+    # definition exactly (both round once, to nearest even)
+    M, K = 70, 4608
+    x = inputs.activations_f32(M, K, 470)
+    x[2] *= 4.0e5
+    x[6] *= 2.0 ** -19
+    x[9, 17] = -65504.0 * 3
+    xb = inputs.f32_to_bf16_bits(x)
+    xd = dev(torch, xb)
+    x16, rs = ql.qlinear_fast_activations(xd, M, K)
+    torch.cuda.synchronize()
+    ref16, refscale = oracle.fast_activations_f16(xb)
+    assert np.array_equal(x16.cpu().numpy().view(np.uint16), ref16.view(np.uint16))
+    assert np.array_equal(rs.cpu().numpy().astype(np.float64), np.asarray(refscale, np.float64))
+
+
+def test_fast_forward_with_given_activations_is_identical(torch):
+    M, N, K = 300, 520, 640
+    c = Case(M, N, K, 4, wid=480, x_structure="outlier")
+    x, p, s, b = c.device(torch)
+    p, s = ql.qlinear_repack(p, s, b, 4, 64, N, K)
+    y1 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    y2 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ql.qlinear_forward_ex(x, p, s, None, 4, M, N, K, y1, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST)
+    x16, rs = ql.qlinear_fast_activations(x, M, K)
+    ql.qlinear_forward_ex(x, p, s, None, 4, M, N, K, y2, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST,
+                          x16=x16, rowscale=rs)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    check_fast(y2.cpu().numpy(), c)
