@@ -238,8 +238,6 @@ def main():
     stream = torch.cuda.current_stream()
 
     steps, warmup = args.steps, args.warmup
-    if args.profile == "step":
-        steps, warmup = 5, 2
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
 

@@ -27,6 +27,13 @@
 // stages (rows of 128 bytes, 16-byte chunks XOR-swizzled by row, see xswz),
 // issued 1.5 groups ahead of its use; one barrier per group, in the middle
 // of the group's MFMAs, so the waves of a SIMD never idle at a group edge.
+//
+// Grid. One block per CU runs whole tiles (t, t + gridDim.x, ...). When the
+// tile count is a little past a multiple of the CU count, the last tiles are
+// cut along M into pieces of 32, 64 or 128 rows (same code, fewer 16-row
+// subtiles per wave) that run first, so every CU does the same work and no
+// partial sums are needed. When there are fewer tiles than CUs, K is split
+// into ranges (blockIdx.y) that write fp32 partials for an ordered reduction.
 #include "ql_device.h"
 #include "ql_kernels.h"
 
@@ -38,9 +45,9 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBM = 256, kBN = 256, kNW = 8, kNT = 64 * kNW;
-constexpr int kWarpsN = 8;                       // waves side by side along N
-constexpr int kWM = 256, kWN = 32, kMI = kWM / 16, kNI = kWN / 16;
+constexpr int kWN = 32, kMI = kBM / 16, kNI = kWN / 16;  // a wave: all rows x 32 columns
 constexpr int kXStage = kBM * 128;               // bytes of one x stage
+constexpr int kStages = 3;                       // x stages in the LDS ring
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne3(float f) {
   uint32_t u = __float_as_uint(f);
@@ -56,34 +63,25 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t v, h2 s2, h2 b2) {
 }
 
 // A lane's codes of one column and group: codes 16h .. 16h+15 (h = lane / 16),
-// i.e. k-blocks 2h and 2h+1, as they sit in the tiled layout.
+// i.e. k-blocks 2h and 2h+1, as they sit in the tiled layout. pair(w, c, p)
+// gives word p of the B fragment of k-block 2h + c (two fp16 weights).
 template <int BITS> struct LaneCodes;
 // 4-bit block [h'2][col32][4 words]: words 2(h%2), +1 of half h/2, pair order
 // (code 2p at bits 4p, code 2p+1 at 16 + 4p).
 template <> struct LaneCodes<4> {
   static constexpr int kWords = 2;
   __device__ static constexpr uint32_t offset(int col, int h) { return (h >> 1) * 512 + col * 16 + (h & 1) * 8; }
-  __device__ static h8 frag(const uint32_t (&w)[kWords], int c, h2 s2, h2 b2) {
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = dq_pair(and_or(w[c] >> (4 * p), 0x000F000Fu, 0x64006400u), s2, b2);
-    return __builtin_bit_cast(h8, o);
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return dq_pair(and_or(w[c] >> (4 * p), 0x000F000Fu, 0x64006400u), s2, b2);
   }
 };
 // 8-bit block [part2][h'2][col32][4 words]: part h%2, half h/2, little-endian.
 template <> struct LaneCodes<8> {
   static constexpr int kWords = 4;
   __device__ static constexpr uint32_t offset(int col, int h) { return (h & 1) * 1024 + (h >> 1) * 512 + col * 16; }
-  __device__ static h8 frag(const uint32_t (&w)[kWords], int c, h2 s2, h2 b2) {
-    u32x4 o;
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const uint32_t x = w[2 * c + v];
-      // bytes (b0, b1) and (b2, b3) into the halves, over 0x6400 (1024)
-      o[2 * v] = dq_pair(perm(0u, x, 0x0C010C00u) | 0x64006400u, s2, b2);
-      o[2 * v + 1] = dq_pair(perm(0u, x, 0x0C030C02u) | 0x64006400u, s2, b2);
-    }
-    return __builtin_bit_cast(h8, o);
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    // bytes (b0, b1) or (b2, b3) of word 2c + p/2 into the halves, over 0x6400 (1024)
+    return dq_pair(perm(0u, w[2 * c + (p >> 1)], (p & 1) ? 0x0C030C02u : 0x0C010C00u) | 0x64006400u, s2, b2);
   }
 };
 // 2-bit block [h'2][col32][2 words]: word h%2 of half h/2, pair order (code 2p
@@ -91,12 +89,8 @@ template <> struct LaneCodes<8> {
 template <> struct LaneCodes<2> {
   static constexpr int kWords = 1;
   __device__ static constexpr uint32_t offset(int col, int h) { return (h >> 1) * 256 + col * 8 + (h & 1) * 4; }
-  __device__ static h8 frag(const uint32_t (&w)[kWords], int c, h2 s2, h2 b2) {
-    u32x4 o;
-    const uint32_t x = w[0] >> (8 * c);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = dq_pair(and_or(x >> (2 * p), 0x00030003u, 0x64006400u), s2, b2);
-    return __builtin_bit_cast(h8, o);
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return dq_pair(and_or(w[0] >> (8 * c + 2 * p), 0x00030003u, 0x64006400u), s2, b2);
   }
 };
 
@@ -106,20 +100,32 @@ template <> struct LaneCodes<2> {
 // XOR swizzles measured on MI355X (194 B/clk/CU against 140 for c ^ (r & 7)).
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int BITS>
-__device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *x0, unsigned char *x1,
-                                                 unsigned char *x2, int64_t m0, int64_t n0, int g_begin,
-                                                 int g_end, f32x4 (&acc)[kMI][kNI]) {
+// Accumulates rows m0 .. m0 + 16*MI of the block tile at (m0, n0) over groups
+// [g_begin, g_end): MI = 16 for a whole tile, fewer for a row piece.
+template <int BITS, int MI>
+__device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages], int64_t m0,
+                                                 int64_t n0, int g_begin, int g_end, f32x4 (&acc)[MI][kNI]) {
+  constexpr int S = kStages;
   using LC = LaneCodes<BITS>;
   constexpr int WB = 64 * BITS / 8;     // code bytes of one column per group
   constexpr int BB = 32 * WB;           // bytes of one tiled block (32 columns x 1 group)
-  constexpr int XPW = (kBM / 8) / kNW;  // 1 KB x copies per wave per group
-  constexpr int kSteps = 2 * kMI;       // steps (c, mi) of kNI MFMAs per group
+  constexpr int kRows = 16 * MI;
+  constexpr int XC = kRows / 8;         // 1 KB x copies per group (8 rows each)
+  constexpr int XPW = XC >= kNW ? XC / kNW : 1;  // copies per issuing wave
+  static_assert(XC % kNW == 0 || kNW % XC == 0, "x copies must spread evenly over the waves");
+  constexpr int kSteps = 2 * MI;        // steps (c, mi) of kNI MFMAs per group
+  constexpr int kHalf = kSteps / 2;
   // A fragments are read this many steps ahead of their use; the ring index
   // t % (kAhead + 1) continues across groups, whose reads ahead wrap into
-  // the next stage
-  constexpr int kAhead = 3;
+  // the next stage, which is complete only after the mid-group barrier
+  constexpr int kAhead = (kSteps % 4 == 0 && kHalf >= 3) ? 3 : 1;
   static_assert(kSteps % (kAhead + 1) == 0, "A-fragment ring must divide the steps of a group");
+  static_assert(kAhead <= kHalf, "reads of the next stage must follow the mid-group barrier");
+  // the next group's B fragments are built in 4 * 2 * kNI pieces of one word
+  // (two weights), spread over the steps of the second half so the vector
+  // work sits between MFMAs instead of in bursts
+  constexpr int kPieces = 8 * kNI;
+  constexpr int kPerStep = (kPieces + kHalf - 1) / kHalf;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,9 +134,11 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
 
   // x copies: copy i of this wave fills block rows (wave*XPW + i)*8 .. +7, lane L
   // row +L/8 at chunk position L & 7, which holds logical chunk
-  // (L & 7) ^ xswz(row). Rows past M repeat the last row.
+  // (L & 7) ^ xswz(row). Rows past M repeat the last row. With fewer copies
+  // than waves only the first XC waves copy.
   const int64_t xrow = a.K * 2;
-  const int64_t mrows = min<int64_t>(kBM, a.M - m0);
+  const int64_t mrows = min<int64_t>(kRows, a.M - m0);
+  const bool x_issuer = XC >= kNW || wave < XC;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x16, m0 * xrow, mrows * xrow);
   uint32_t xo[XPW];
 #pragma unroll
@@ -168,8 +176,10 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   };
   auto issue_x = [&](unsigned char *X, int gv) {
     const int g = __builtin_amdgcn_readfirstlane(gv);
+    if (x_issuer) {
 #pragma unroll
-    for (int i = 0; i < XPW; ++i) dma16(xr, xo[i], (uint32_t)g * 128u, X + (wave * XPW + i) * 1024);
+      for (int i = 0; i < XPW; ++i) dma16(xr, xo[i], (uint32_t)g * 128u, X + (wave * XPW + i) * 1024);
+    }
   };
 
   // A fragments: rows mi*16 + r16, k-block 2h + c, at chunk position
@@ -183,102 +193,121 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   const int a_base = r16 * 128;
   h8 af[kAhead + 1];
   auto read_a = [&](const unsigned char *X, int t) {
-    const int c = t / kMI, mi = t % kMI;
+    const int c = t / MI, mi = t % MI;
     af[t % (kAhead + 1)] = *reinterpret_cast<const h8 *>(X + a_base + mi * 2048 + a_off[c][mi & 3]);
   };
 
   // B fragments of the group being multiplied, built from codes that arrived
-  // one group earlier; a group past the end gets zero scale and bias, so its
-  // weights are zero and its step adds nothing.
-  h8 bf[kNI][2];
-  uint32_t cw[kNI][LC::kWords];  // codes of the group after the one in bf
-  uint32_t sbw[kNI];
-  auto dequant_frag = [&](h8 (&dst)[kNI][2], bool valid, int f) {
-    const int ni = f >> 1, c = f & 1;
-    const uint32_t v = valid ? sbw[ni] : 0u;
+  // earlier; a group past the end gets zero scale and bias, so its weights
+  // are zero and its step adds nothing. Codes and scale|bias words of groups
+  // g+1 .. g+S-2 are held (cq[0] = g+1); those of g+S-1 are requested in
+  // group g.
+  u32x4 bf[kNI][2];
+  uint32_t cq[S - 1][kNI][LC::kWords];
+  uint32_t sq[S - 1][kNI];
+  // piece i of the B fragments from cq[0]/sq[0]: fragment (ni, c) = i / 4, word i % 4
+  auto dequant_piece = [&](u32x4 (&dst)[kNI][2], bool valid, int i) {
+    const int f = i >> 2, p = i & 3, ni = f >> 1, c = f & 1;
+    const uint32_t v = valid ? sq[0][ni] : 0u;
     const h2 s2 = __builtin_bit_cast(h2, (v & 0xFFFFu) * 0x10001u);
     const h2 b2 = __builtin_bit_cast(h2, (v >> 16) * 0x10001u);
-    dst[ni][c] = LC::frag(cw[ni], c, s2, b2);
+    uint32_t r = LC::pair(cq[0][ni], c, p, s2, b2);
+    asm volatile("" : "+v"(r));  // keeps the piece where it is placed, between MFMAs
+    dst[ni][c][p] = r;
   };
 
   // One group on stage X. First half: MFMAs on the fragments in hand. Then
-  // one barrier, after which the next stage XN is complete and the stage of
-  // the previous group (XD) is free: the x copies for two groups ahead go
-  // into XD and the codes for two groups ahead are requested. Second half:
-  // MFMAs, with the next group's B fragments dequantized in between and the
-  // first A fragments of XN read ahead, so the next group starts without a
-  // stall.
+  // the barrier, after which the next stage XN is complete and the stage of
+  // the previous group (XD) is free: the x copies for S-1 groups ahead go
+  // into XD and their codes are requested. Second half: MFMAs, with the next
+  // group's B fragments dequantized in between and the first A fragments of
+  // XN read ahead, so the next group starts without a stall.
   auto step = [&](const unsigned char *X, const unsigned char *XN, unsigned char *XD, int g) {
-    h8 bn[kNI][2];
-    uint32_t cn[kNI][LC::kWords], sn[kNI];
+    u32x4 bn[kNI][2];
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
-      const int c = t / kMI, mi = t % kMI;
-      if (t == kSteps / 2) {
-        __syncthreads();
-        issue_x(XD, min(g + 2, g_end - 1));
-        load_codes(cn, sn, min(g + 2, g_end - 1));
+      const int c = t / MI, mi = t % MI;
+      if (t == kHalf) {
+        __syncthreads();  // stage g+1 has landed everywhere, stage g-1 is free
+        issue_x(XD, min(g + S - 1, g_end - 1));
+        load_codes(cq[S - 2], sq[S - 2], min(g + S - 1, g_end - 1));
       }
       if (t + kAhead < kSteps) read_a(X, t + kAhead);
       else read_a(XN, t + kAhead - kSteps);
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t % (kAhead + 1)], bf[ni][c], acc[mi][ni], 0, 0, 0);
-      if (t >= kSteps / 2 && (t & 3) == 1) dequant_frag(bn, g + 1 < g_end, (t - kSteps / 2) >> 2);
+      for (int ni = 0; ni < kNI; ++ni) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t % (kAhead + 1)], __builtin_bit_cast(h8, bf[ni][c]),
+                                                             acc[mi][ni], 0, 0, 0);
+        if (t >= kHalf) {
+#pragma unroll
+          for (int u = 0; u < kPerStep; ++u) {
+            const int i = (t - kHalf) * kPerStep + u;
+            if ((u % kNI) == ni && i < kPieces) dequant_piece(bn, g + 1 < g_end, i);
+          }
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
       bf[ni][0] = bn[ni][0];
       bf[ni][1] = bn[ni][1];
-      sbw[ni] = sn[ni];
 #pragma unroll
-      for (int u = 0; u < LC::kWords; ++u) cw[ni][u] = cn[ni][u];
+      for (int j = 0; j + 1 < S - 1; ++j) {
+        sq[j][ni] = sq[j + 1][ni];
+#pragma unroll
+        for (int u = 0; u < LC::kWords; ++u) cq[j][ni][u] = cq[j + 1][ni][u];
+      }
     }
   };
 
 #pragma unroll
-  for (int i = 0; i < kMI; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Groups run in threes (x stages 0, 1, 2) in straight-line code: loads for
-  // a group past the end are clamped to the last group and its weights
+  // Groups run S at a time (one per x stage) in straight-line code: loads
+  // for a group past the end are clamped to the last group and its weights
   // dequantize to zero, so the accumulators never pass through a branch.
   if (g_begin < g_end) {
-    load_codes(cw, sbw, g_begin);
-    issue_x(x0, g_begin);
-    issue_x(x1, min(g_begin + 1, g_end - 1));
+    load_codes(cq[0], sq[0], g_begin);
+    issue_x(xs[0], g_begin);
+    issue_x(xs[1], min(g_begin + 1, g_end - 1));
   }
   __syncthreads();  // first two stages and the first codes have arrived
   if (g_begin < g_end) {
 #pragma unroll
-    for (int f = 0; f < 2 * kNI; ++f) dequant_frag(bf, true, f);
-    load_codes(cw, sbw, min(g_begin + 1, g_end - 1));
+    for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
+    load_codes(cq[0], sq[0], min(g_begin + 1, g_end - 1));
 #pragma unroll
-    for (int t = 0; t < kAhead; ++t) read_a(x0, t);
+    for (int j = 2; j < S; ++j) {
+      issue_x(xs[j], min(g_begin + j, g_end - 1));
+      load_codes(cq[j - 1], sq[j - 1], min(g_begin + j, g_end - 1));
+    }
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) read_a(xs[0], t);
   }
-  for (int g = g_begin; g < g_end; g += 3) {
-    step(x0, x1, x2, g);
-    step(x1, x2, x0, g + 1);
-    step(x2, x0, x1, g + 2);
+  for (int g = g_begin; g < g_end; g += S) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) step(xs[k], xs[(k + 1) % S], xs[(k + S - 1) % S], g + k);
   }
   __syncthreads();  // every copy has landed and every stage is free
 }
 
-template <bool OUT_BF16>
-__device__ __forceinline__ void tile_store3(const Gemm3Args &a, int64_t m0, int64_t n0,
-                                            const f32x4 (&acc)[kMI][kNI]) {
+// Stores rows m0 .. m0 + 16*MI of a tile, times the row scales, into out
+// ([M, N] fp32 or bf16).
+template <bool OUT_BF16, int MI>
+__device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64_t m0, int64_t n0,
+                                            const f32x4 (&acc)[MI][kNI]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWarpsN, wn = wave % kWarpsN;  // wm == 0
   const int r16 = lane & 15, h = lane >> 4;
-  const int64_t row0 = m0 + wm * kWM + 4 * h;
-  const int64_t col0 = n0 + wn * kWN + r16;
-  const bool full = (m0 + kBM <= a.M) && (n0 + kBN <= a.N);
+  const int64_t row0 = m0 + 4 * h;
+  const int64_t col0 = n0 + wave * kWN + r16;
+  const bool full = (m0 + 16 * MI <= a.M) && (n0 + kBN <= a.N);
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = row0 + mi * 16 + i;
@@ -289,73 +318,51 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, int64_t m0, int6
         const int64_t n = col0 + ni * 16;
         if (!full && n >= a.N) continue;
         const float v = acc[mi][ni][i] * rs;
-        if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(a.out)[m * a.N + n] = f32_to_bf16_rne3(v);
-        else reinterpret_cast<float *>(a.out)[m * a.N + n] = v;
+        if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * a.N + n] = f32_to_bf16_rne3(v);
+        else reinterpret_cast<float *>(out)[m * a.N + n] = v;
       }
     }
 }
 
-// One launch covers dp_tiles whole tiles (t = blockIdx.x, + gridDim.x, ...)
-// and, when sk_tiles > 0, the last sk_tiles tiles cut into sk_pieces K-ranges
-// that run first, one per block: with one block per CU a tile count just past
-// a multiple of the CU count would otherwise leave most CUs idle for a whole
-// tile time. Each piece writes an fp32 partial (thread-major, so writes and the
-// later reads are contiguous); the piece that arrives last (atomic count)
-// adds all partials in piece order, so the result is independent of timing,
-// stores the tile and re-arms the count.
-template <int BITS, bool OUT_BF16>
+// blockIdx.y = K range (a.splits of them; each writes its own fp32 slice of
+// out, [splits, M, N], for an ordered reduction afterwards). Blocks
+// [0, tail_tiles * 16/PMI) first run the row pieces of the last tail_tiles
+// tiles (PMI 16-row subtiles each, pieces of one tile on one XCD), then every
+// block takes whole tiles t = blockIdx.x, + gridDim.x, ... below dp_tiles.
+// Power-of-two row scales commute exactly with the summation, so partials
+// carry them already.
+template <int BITS, bool OUT_BF16, int PMI>
 __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char x0[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x2[kXStage];
-  __shared__ int s_arrived;
-  const int tid = threadIdx.x;
+  unsigned char *const xs[kStages] = {x0, x1, x2};
   const int tiles_n = (int)((a.N + kBN - 1) / kBN);
-  f32x4 acc[kMI][kNI];
+  const int split = blockIdx.y;
+  const int gps = (a.G + a.splits - 1) / a.splits;
+  const int gb = split * gps, ge = min(a.G, gb + gps);
+  void *out = a.splits > 1 ? static_cast<void *>(static_cast<float *>(a.out) + (int64_t)split * a.M * a.N) : a.out;
 
-  if (a.sk_tiles > 0 && (int)blockIdx.x < a.sk_tiles * a.sk_pieces) {
-    const int tail = blockIdx.x / a.sk_pieces, piece = blockIdx.x % a.sk_pieces;
-    const int tile = a.dp_tiles + tail;
-    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
-    const int gpp = (a.G + a.sk_pieces - 1) / a.sk_pieces;
-    const int gb = piece * gpp, ge = min(a.G, gb + gpp);
-    tile_accumulate3<BITS>(a, x0, x1, x2, m0, n0, gb, ge, acc);
-    float *part = a.sk_partial + (int64_t)tail * a.sk_pieces * (kBM * kBN);
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-        *reinterpret_cast<f32x4 *>(part + (int64_t)piece * (kBM * kBN) + ((mi * kNI + ni) * kNT + tid) * 4) =
-            acc[mi][ni];
-    __syncthreads();  // every thread's partial stores are complete
-    if (tid == 0) {
-      // make this block's partial visible device-wide, then count it
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      s_arrived = __hip_atomic_fetch_add(&a.sk_count[tail], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (s_arrived == a.sk_pieces - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    __syncthreads();
-    if (s_arrived == a.sk_pieces - 1) {
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kNI; ++ni) {
-          const f32x4 mine = acc[mi][ni];
-          const int64_t e = ((mi * kNI + ni) * kNT + tid) * 4;
-          f32x4 sum = piece == 0 ? mine : *reinterpret_cast<const f32x4 *>(part + e);
-          for (int p = 1; p < a.sk_pieces; ++p)
-            sum += p == piece ? mine : *reinterpret_cast<const f32x4 *>(part + (int64_t)p * (kBM * kBN) + e);
-          acc[mi][ni] = sum;
-        }
-      tile_store3<OUT_BF16>(a, m0, n0, acc);
-      if (tid == 0) a.sk_count[tail] = 0;
+  if constexpr (PMI > 0) {
+    constexpr int kPieces = 16 / PMI;
+    if ((int)blockIdx.x < a.tail_tiles * kPieces) {
+      const int tail = blockIdx.x % a.tail_tiles, piece = blockIdx.x / a.tail_tiles;
+      const int tile = a.dp_tiles + tail;
+      const int64_t m0 = (int64_t)(tile / tiles_n) * kBM + piece * 16 * PMI;
+      const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
+      if (m0 < a.M) {  // uniform per block
+        f32x4 pacc[PMI][kNI];
+        tile_accumulate3<BITS, PMI>(a, xs, m0, n0, gb, ge, pacc);
+        tile_store3<OUT_BF16, PMI>(a, out, m0, n0, pacc);
+      }
     }
   }
+  f32x4 acc[kMI][kNI];
   for (int t = blockIdx.x; t < a.dp_tiles; t += gridDim.x) {
     const int tile = xcd_remap(t, a.dp_tiles);
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
-    tile_accumulate3<BITS>(a, x0, x1, x2, m0, n0, 0, a.G, acc);
-    tile_store3<OUT_BF16>(a, m0, n0, acc);
+    tile_accumulate3<BITS, kMI>(a, xs, m0, n0, gb, ge, acc);
+    tile_store3<OUT_BF16, kMI>(a, out, m0, n0, acc);
   }
 }
 
@@ -438,12 +445,23 @@ __global__ __launch_bounds__(256) void x16_row_kernel(const uint16_t *x, uint16_
   }
 }
 
+template <int BITS, bool OUT_BF16>
+void launch3_out(const Gemm3Args &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.grid_x, (unsigned)a.splits);
+  switch (a.tail_tiles > 0 ? a.tail_mi : 0) {
+    case 2: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 2>), grid, dim3(kNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 4>), grid, dim3(kNT), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 8>), grid, dim3(kNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 0>), grid, dim3(kNT), 0, stream, a); break;
+  }
+}
+
 template <int BITS>
 hipError_t launch3_bits(const Gemm3Args &a, hipStream_t stream) {
-  if (a.out_bf16)
-    hipLaunchKernelGGL((gemm3_kernel<BITS, true>), dim3(a.grid_x), dim3(kNT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gemm3_kernel<BITS, false>), dim3(a.grid_x), dim3(kNT), 0, stream, a);
+  if (a.tail_tiles > 0 && a.tail_mi != 2 && a.tail_mi != 4 && a.tail_mi != 8) return hipErrorInvalidValue;
+  if (a.splits < 1 || (a.splits > 1 && a.tail_tiles > 0)) return hipErrorInvalidValue;
+  if (a.out_bf16 && a.splits == 1) launch3_out<BITS, true>(a, stream);
+  else launch3_out<BITS, false>(a, stream);
   return hipGetLastError();
 }
 
@@ -461,26 +479,36 @@ int device_cus() {
 
 }  // namespace
 
-Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots) {
+Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits) {
   Gemm3Plan p{};
   p.tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   p.dp_tiles = (int)p.tiles;
   p.grid_x = (int)p.tiles;
+  p.splits = 1;
   if (slots <= 0) slots = device_cus();  // one block per CU
-  if (G < 2 || p.tiles <= slots || p.tiles % slots == 0) return p;
-  const int64_t dp = (p.tiles / slots) * slots;
-  const int tail = (int)(p.tiles - dp);
-  int pieces = slots / tail;
-  if (pieces > G) pieces = G;
+  int splits = force_splits;
+  if (splits <= 0 && p.tiles * 2 <= slots && G >= 16) {
+    // too few tiles for the CUs: split K, keeping >= 8 groups per range
+    splits = (int)(slots / p.tiles);
+    if (splits > G / 8) splits = G / 8;
+    if (splits > 16) splits = 16;
+  }
+  if (splits > G) splits = G;
+  if (splits > 1) {
+    const int gps = (G + splits - 1) / splits;
+    p.splits = (G + gps - 1) / gps;  // no empty range
+    if (p.splits > 1) p.partial_bytes = (size_t)p.splits * (size_t)M * (size_t)N * 4u;
+    return p;
+  }
+  if (p.tiles <= slots || p.tiles % slots == 0) return p;
+  const int64_t tail = p.tiles % slots;
+  int pieces = 8;
+  while (pieces >= 2 && tail * pieces > slots) pieces /= 2;
   if (pieces < 2) return p;
-  const int gpp = (G + pieces - 1) / pieces;
-  pieces = (G + gpp - 1) / gpp;
-  p.dp_tiles = (int)dp;
-  p.sk_tiles = tail;
-  p.sk_pieces = pieces;
+  p.dp_tiles = (int)(p.tiles - tail);
+  p.tail_tiles = (int)tail;
+  p.tail_mi = 16 / pieces;
   p.grid_x = slots;
-  const size_t part = (size_t)tail * pieces * kBM * kBN * 4u;
-  p.sk_partial_bytes = ((part + 255) / 256) * 256 + (((size_t)tail * 4u + 255) / 256) * 256;
   return p;
 }
 

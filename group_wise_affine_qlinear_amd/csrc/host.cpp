@@ -185,22 +185,27 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   if (tile > 0 && !forced) return QL_EUNSUPPORTED;
   if (mode == QL_MODE_AUTO) {
     if (forced) mode = forced->gen == 3 ? QL_MODE_FAST : QL_MODE_EXACT;
-    else mode = (tiled && path == QL_PATH_GEMM) ? QL_MODE_FAST : QL_MODE_EXACT;
+    else mode = tiled ? QL_MODE_FAST : QL_MODE_EXACT;
   }
   if (mode != QL_MODE_EXACT && mode != QL_MODE_FAST) return QL_EINVAL;
   p->mode = mode;
   if (mode == QL_MODE_FAST) {
-    if (!tiled || path == QL_PATH_SPLITK || force_split > 1) return QL_EUNSUPPORTED;
+    if (!tiled) return QL_EUNSUPPORTED;
     if (forced && forced->gen != 3) return QL_EUNSUPPORTED;
-    p->path = QL_PATH_GEMM;
-    p->tile = kFastTile;
-    p->splits = 1;
-    p->groups_per_split = G;
-    p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
+    int fs = force_split > 0 ? force_split : 0;
+    if (path == QL_PATH_GEMM && force_path == QL_PATH_GEMM) fs = force_split > 0 ? force_split : 1;
+    if (path == QL_PATH_SPLITK && fs < 2) fs = 2;
+    if (fs > G) fs = G;
     // QLINEAR_GEMM_SLOTS: resident-block count override, for tests of the
-    // split tail on small shapes
-    p->g3 = ql::gemm3_plan(M, N, G, env_int("QLINEAR_GEMM_SLOTS", 0));
-    p->ws_partial = p->g3.sk_partial_bytes;
+    // tail pieces and K splits on small shapes
+    p->g3 = ql::gemm3_plan(M, N, G, env_int("QLINEAR_GEMM_SLOTS", 0), fs);
+    if (path == QL_PATH_SPLITK && p->g3.splits < 2) return QL_EUNSUPPORTED;
+    p->path = p->g3.splits > 1 ? QL_PATH_SPLITK : QL_PATH_GEMM;
+    p->tile = kFastTile;
+    p->splits = p->g3.splits;
+    p->groups_per_split = G > 0 ? (G + p->splits - 1) / p->splits : 0;
+    p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
+    p->ws_partial = p->g3.partial_bytes;
     return QL_OK;
   }
   if (forced && forced->gen == 3) return QL_EUNSUPPORTED;
@@ -372,20 +377,24 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
       x16 = x16w;
       rowscale = rsw;
     }
-    ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales), a->out,
-                     a->M, a->N, a->K, G, out_bf16,
-                     p.g3.dp_tiles, p.g3.sk_tiles, p.g3.sk_pieces, p.g3.grid_x, nullptr, nullptr};
-    if (p.g3.sk_tiles > 0) {
-      const size_t part = (size_t)p.g3.sk_tiles * p.g3.sk_pieces * ti_sizes(p.tile);
-      g3.sk_partial = reinterpret_cast<float *>(after);
-      g3.sk_count = reinterpret_cast<int *>(after + round_up((int64_t)part * 4, 256));
-      if (ql::launch_fill_zero(g3.sk_count, p.g3.sk_tiles, 0, stream) != hipSuccess) return QL_EHIP;
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_tiled", a->bits, p.g3.sk_tiles, p.g3.sk_pieces);
-    } else {
+    const bool split = p.g3.splits > 1;
+    float *partial = reinterpret_cast<float *>(after);
+    ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales),
+                     split ? static_cast<void *>(partial) : a->out,
+                     a->M, a->N, a->K, G, split ? 0 : out_bf16,
+                     p.g3.dp_tiles, p.g3.tail_tiles, p.g3.tail_mi, p.g3.splits, p.g3.grid_x};
+    if (split)
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_split%d_tiled", a->bits, p.g3.splits);
+    else if (p.g3.tail_tiles > 0)
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_tiled", a->bits, p.g3.tail_tiles,
+                    16 / p.g3.tail_mi);
+    else
       std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tiled", a->bits);
-    }
     set_last_path(buf);
-    return ql::launch_gemm3(a->bits, g3, stream) == hipSuccess ? QL_OK : QL_EHIP;
+    if (ql::launch_gemm3(a->bits, g3, stream) != hipSuccess) return QL_EHIP;
+    if (split && ql::launch_splitk_reduce(partial, p.g3.splits, a->M, a->N, a->out, out_bf16, stream) != hipSuccess)
+      return QL_EHIP;
+    return QL_OK;
   }
   int64_t Mp = round_up(a->M, 256);
   float *xsum = static_cast<float *>(ws);

@@ -57,27 +57,30 @@ struct Gemm2Plan {
 };
 Gemm2Plan gemm2_plan(int bits, int tile_id, int64_t M, int64_t N, int G, int splits, int slots);
 // Fast mode (gemm3.hip): fp16 x with per-row power-of-two scales, tiled codes
-// dequantized to fp16 in LDS, 256 x 256 block tiles.
+// dequantized to fp16 in registers, 256 x 256 block tiles.
 struct Gemm3Args {
   const uint16_t *x16;    // fp16 [M, K]
   const float *rowscale;  // [M], 2^e per row
   const uint32_t *w;      // tiled codes
   const uint32_t *sb;     // tiled scale|bias words
-  void *out;              // [M, N] fp32 or bf16
+  void *out;              // [M, N] fp32 or bf16; with splits > 1 fp32 [splits, M, N]
   int64_t M, N, K;
   int G;
-  int out_bf16;
-  int dp_tiles, sk_tiles, sk_pieces, grid_x;
-  float *sk_partial;      // [sk_tiles, sk_pieces, 256*256]
-  int *sk_count;          // [sk_tiles], zero before the launch; left zero after it
+  int out_bf16;           // ignored when splits > 1 (partials are fp32)
+  int dp_tiles;           // whole tiles, t = blockIdx.x, + gridDim.x, ...
+  int tail_tiles;         // tiles after dp_tiles, cut along M into 16/tail_mi pieces
+  int tail_mi;            // 16-row subtiles per piece: 2, 4 or 8
+  int splits;             // K ranges (grid y)
+  int grid_x;
 };
 struct Gemm3Plan {
   int64_t tiles;
-  int dp_tiles, sk_tiles, sk_pieces, grid_x;
-  size_t sk_partial_bytes;
+  int dp_tiles, tail_tiles, tail_mi, splits, grid_x;
+  size_t partial_bytes;   // splits > 1: fp32 [splits, M, N]
 };
-// slots <= 0: one block per CU of the current device
-Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots);
+// slots <= 0: one block per CU of the current device; force_splits > 0 fixes
+// the K split
+Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits);
 hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream);
 hipError_t launch_gemm3(int bits, const Gemm3Args &a, hipStream_t stream);
 

@@ -79,9 +79,10 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  *   weights). Requires the TILED layout and |W| < 65504, which holds for
  *   weights quantized from fp16-range values (W lies between b and
  *   b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x
- *   unless the caller passes it (qlinear_fast_activations, x16/rowscale).
- * AUTO: FAST for the large-M path on TILED weights, EXACT otherwise. The
- *   skinny (M <= 16) path is always EXACT.
+ *   unless the caller passes it (qlinear_fast_activations, x16/rowscale),
+ *   plus splits*M*N*4 bytes of fp32 partials when K is split.
+ * AUTO: FAST for the large-M paths (GEMM, SPLITK) on TILED weights, EXACT
+ *   otherwise. The skinny (M <= 16) path is always EXACT.
  */
 typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
 
@@ -115,9 +116,10 @@ typedef struct ql_forward_args {
   int layout;                /* ql_layout. For QL_LAYOUT_TILED, packed_q holds
                                 the tiled codes, scales the tiled scale|bias
                                 words, and biases is ignored                */
-  int mode;                  /* ql_mode; FAST needs QL_LAYOUT_TILED and the
-                                GEMM path (path AUTO or GEMM), else
-                                QL_EUNSUPPORTED; xsum is unused in FAST     */
+  int mode;                  /* ql_mode; FAST needs QL_LAYOUT_TILED and a
+                                large-M path (AUTO with M > 16, GEMM or
+                                SPLITK), else QL_EUNSUPPORTED; xsum is
+                                unused in FAST                              */
   const void *x16;           /* optional, FAST only: fp16 [M, K] activations
                                 and                                         */
   const float *rowscale;     /* [M] row scales from qlinear_fast_activations

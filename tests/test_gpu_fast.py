@@ -71,8 +71,9 @@ def test_fast_rejects_unsupported_requests(torch):
     c = Case(64, 256, 256, 4, wid=412)
     with pytest.raises(ql.QLinearError):   # canonical layout
         run_forward(torch, c, mode=ql.QL_MODE_FAST)
-    with pytest.raises(ql.QLinearError):   # split-K path
-        run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=ql.QL_PATH_SPLITK)
+    with pytest.raises(ql.QLinearError):   # a K split needs two groups at least
+        run_forward(torch, Case(64, 256, 64, 4, wid=414), layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST,
+                    path=ql.QL_PATH_SPLITK)
     with pytest.raises(ql.QLinearError):   # skinny path
         run_forward(torch, Case(4, 256, 256, 4, wid=413), layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST,
                     path=ql.QL_PATH_SKINNY)
@@ -112,17 +113,27 @@ def test_fast_bf16_out_is_rounded_fp32_out(torch, bits):
     assert np.array_equal(got, inputs.f32_to_bf16_bits(y))
 
 
-# split tail and multi-tile blocks with the resident-block count forced small: (slots, shape)
+# tail pieces and multi-tile blocks with the resident-block count forced small:
+# (slots, shape). Tiles are 256 x 256; tail tiles are cut along M into pieces
+# of 128, 64 or 32 rows; pieces wholly past M are skipped.
 FAST_TAIL_CASES = [
-    (4, (520, 1000, 640)),    # 12 tiles over 4 blocks: 3 whole tiles per block, no split
-    (5, (520, 1000, 640)),    # 12 tiles: 10 whole, 2 tail tiles x 2 pieces (G=10: 5+5)
+    (4, (520, 1000, 640)),    # 12 tiles over 4 blocks: 3 whole tiles per block, no pieces
     (3, (300, 600, 448)),     # 6 tiles over 3 blocks: 2 whole tiles per block (G=7, odd)
-    (4, (300, 600, 448)),     # 6 tiles: 4 whole, 2 tail tiles x 2 pieces (G=7: 4+3)
-    (7, (520, 520, 576)),     # 9 tiles: 7 whole, 2 tail tiles x 3 pieces (G=9: 3+3+3)
+    (9, (600, 1100, 320)),    # 15 tiles, 6 past 9: too many for pieces, whole tiles only
+    (5, (520, 1000, 640)),    # 12 tiles: 10 whole, 2 tail tiles x 2 pieces of 128 rows (tile row: 8 rows)
+    (4, (300, 600, 448)),     # 6 tiles: 4 whole, 2 tail tiles x 2 pieces (rows 256..299: one partial piece)
+    (6, (700, 600, 384)),     # 9 tiles: 6 whole, 3 tail tiles x 2 pieces (rows 512..699)
+    (12, (512, 1792, 320)),   # 14 tiles: 12 whole, 2 tail tiles x 4 pieces of 64 rows
+    (17, (800, 1280, 320)),   # 20 tiles: 17 whole, 3 tail tiles x 4 pieces (rows 768..799)
+    (8, (1030, 512, 256)),    # 10 tiles: 8 whole, 2 tail tiles x 4 pieces (rows 1024..1029)
+    (17, (300, 2304, 448)),   # 18 tiles: 17 whole, 1 tail tile x 8 pieces of 32 rows (rows 256..299)
+    (9, (256, 2560, 320)),    # 10 tiles: 9 whole, 1 tail tile x 8 pieces
+    (33, (768, 3072, 320)),   # 36 tiles: 33 whole, 3 tail tiles x 8 pieces
+    (33, (520, 3072, 320)),   # same grid, tail tiles hold rows 512..519 only: 7 of 8 pieces skipped
 ]
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("slots,shape", FAST_TAIL_CASES)
 def test_fast_split_tail(torch, monkeypatch, slots, shape, bits):
     M, N, K = shape
@@ -181,3 +192,33 @@ def test_fast_forward_with_given_activations_is_identical(torch):
     torch.cuda.synchronize()
     assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
     check_fast(y2.cpu().numpy(), c)
+
+
+# K split (grid y) with fp32 partials and the ordered reduction: forced split
+# counts, including uneven group ranges, and the automatic split of shapes with
+# fewer tiles than CUs
+FAST_SPLIT_CASES = [
+    ((300, 520, 640), 2),      # G=10: 5+5
+    ((300, 520, 640), 3),      # G=10: 4+4+2
+    ((777, 300, 1344), 7),     # G=21: 3 x 7
+    ((64, 1000, 4608), 0),     # automatic: 4 tiles, G=72
+    ((512, 600, 8192), 0),     # automatic: 6 tiles, G=128
+]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("shape,splits", FAST_SPLIT_CASES)
+def test_fast_split_k(torch, shape, splits, bits):
+    M, N, K = shape
+    c = Case(M, N, K, bits, wid=490 + bits, x_structure="outlier")
+    path = ql.QL_PATH_SPLITK if splits else ql.QL_PATH_AUTO
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=path, split_k=splits)
+    lp = ql.qlinear_last_path()
+    assert lp.startswith("gemm3") and "_split" in lp, lp
+    if splits:
+        assert f"_split{len(range(0, K // 64, -(-(K // 64) // splits)))}_" in lp, lp
+    check_fast(y.cpu().numpy(), c)
+    yb = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=path, split_k=splits,
+                     out_dtype="bf16")
+    got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(y.cpu().numpy()))
