@@ -279,8 +279,10 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
     load_codes(cq[0], sq[0], min(g_begin + 1, g_end - 1));
+    // stages and codes up to g_begin + S - 2 are in flight now; each group g
+    // requests g + S - 1
 #pragma unroll
-    for (int j = 2; j < S; ++j) {
+    for (int j = 2; j < S - 1; ++j) {
       issue_x(xs[j], min(g_begin + j, g_end - 1));
       load_codes(cq[j - 1], sq[j - 1], min(g_begin + j, g_end - 1));
     }
