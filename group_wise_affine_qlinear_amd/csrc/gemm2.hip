@@ -262,18 +262,18 @@ __device__ __forceinline__ void tile_accumulate(const GemmArgs &a, Stage<BITS, B
     issue(st0, g_begin);
     finish(st0);
   }
-  __syncthreads();
+  dma_barrier();
   int g = g_begin;
   for (; g + 1 < g_end; g += 2) {
     issue(st1, g + 1);
     compute(st0);
     finish(st1);
-    __syncthreads();
+    dma_barrier();
     const bool more2 = g + 2 < g_end;
     if (more2) issue(st0, g + 2);
     compute(st1);
     if (more2) finish(st0);
-    __syncthreads();
+    dma_barrier();
   }
   if (g < g_end) compute(st0);
   __syncthreads();  // every wave is done with both stages before they are refilled

@@ -228,7 +228,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
     for (int t = 0; t < kSteps; ++t) {
       const int c = t / MI, mi = t % MI;
       if (t == kHalf) {
-        __syncthreads();  // stage g+1 has landed everywhere, stage g-1 is free
+        dma_barrier();  // stage g+1 has landed everywhere, stage g-1 is free
         issue_x(XD, min(g + S - 1, g_end - 1));
         load_codes(cq[S - 2], sq[S - 2], min(g + S - 1, g_end - 1));
       }
@@ -274,7 +274,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
     issue_x(xs[0], g_begin);
     issue_x(xs[1], min(g_begin + 1, g_end - 1));
   }
-  __syncthreads();  // first two stages and the first codes have arrived
+  dma_barrier();  // first two stages and the first codes have arrived
   if (g_begin < g_end) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
@@ -293,7 +293,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
 #pragma unroll
     for (int k = 0; k < S; ++k) step(xs[k], xs[(k + 1) % S], xs[(k + S - 1) % S], g + k);
   }
-  __syncthreads();  // every copy has landed and every stage is free
+  dma_barrier();  // the copies requested past the last group have landed; every stage is free
 }
 
 // Stores rows m0 .. m0 + 16*MI of a tile, times the row scales, into out

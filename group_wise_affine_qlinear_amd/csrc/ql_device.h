@@ -136,6 +136,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)voff, (int)soff, 0, 0);
 }
 
+// Block barrier that publishes LDS filled by dma16: a copy to LDS is a vector
+// memory load, counted by vmcnt until its bytes are in LDS, and the workgroup
+// fence of __syncthreads() waits only for LDS operations, so each wave first
+// waits for all of its own copies (and other loads) in flight.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // XCD-aware remap of a linear block id: the hardware deals consecutive block
 // ids round-robin over the 8 XCDs; renumber so that each XCD receives a
 // contiguous run of logical tiles (neighbouring tiles share one L2).

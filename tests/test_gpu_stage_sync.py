@@ -1,0 +1,67 @@
+"""Regression test: x stages copied into LDS by DMA must have landed before
+any wave reads them.
+
+A copy to LDS is a vector memory load; the workgroup barrier alone does not
+wait for it, so each wave has to wait for its own copies before the barrier
+that publishes a stage. Without that wait the result depends on timing: it
+shows as a few wrong outputs in some runs, mostly in the short row pieces that
+finish a tile grid (their groups take the least time between a copy and its
+use). The case here is the square projection at full size, whose last 32
+tiles run as 8 row pieces each, repeated; every run must give the same bits
+and match the oracle on the rows and columns of the pieces."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs
+from group_wise_affine_qlinear_amd import qlinear as ql
+
+from gpu_helpers import MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, dev, torch_or_skip
+
+pytestmark = pytest.mark.gpu
+
+REPS = 6
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_or_skip()
+    ql.load_library()
+    return t
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("mode", [ql.QL_MODE_FAST, ql.QL_MODE_EXACT])
+def test_repeated_runs_identical_and_correct(torch, bits, mode):
+    M, K, N = 4096, 4608, 4608
+    w = inputs.weights(N, K, 70 + bits)
+    x = inputs.activations_bf16(M, K, 70 + bits)
+    q, s16, b16 = oracle.quantize_rtn(w, bits)
+    packed = oracle.pack(q, bits)
+    del w, q
+    rng = np.random.default_rng(71)
+    # the 32 pieced tiles are row tile 14 from column tile 4 on and all of row
+    # tile 15: sample their rows 3584..4095 and columns 4096..4607 (inside
+    # both), plus random rows and columns
+    rows = np.unique(np.concatenate([np.arange(3584, 4096, 7), rng.integers(0, M, 40)]))
+    cols = np.unique(np.concatenate([np.arange(4096, 4608, 5), rng.integers(0, N, 40)]))
+    ref = oracle.forward_rows(x, packed, s16, b16, bits, K, rows, cols)
+    xd, pd, sd, bd = dev(torch, x), dev(torch, packed), dev(torch, s16), dev(torch, b16)
+    tq, tsb = ql.qlinear_repack(pd, sd, bd, bits, 64, N, K)
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    first = None
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for rep in range(REPS):
+        out.fill_(float("nan"))
+        ql.qlinear_forward_ex(xd, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED, mode=mode)
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.clone()
+            blk = out.index_select(0, ri).index_select(1, ci).cpu().numpy()
+            e = oracle.error_metrics(blk, ref)
+            assert e["relF"] <= RELF_TOL and e["maxabs_over_rms"] <= MAXABS_RMS_TOL, (ql.qlinear_last_path(), e)
+            if mode == ql.QL_MODE_EXACT:
+                assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, e
+        else:
+            diff = (out != first).nonzero()
+            assert diff.shape[0] == 0, (rep, ql.qlinear_last_path(), diff[:8].tolist())
