@@ -136,6 +136,38 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
             del sets
             log(f"skinny M={M} {lname}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
 
+    # SwiGLU MLP gate/up projection at 1024x1024: plain FAST GEMM (fp32 y, [M, 2F])
+    # against the fused epilogue (bf16 silu(gate) * up, [M, F])
+    M, K, N = 4608, 4608, 2 * 12288
+    w = torch.from_numpy(inputs.weights(N, K, 3)).cuda()
+    p = torch.empty((N, K // 8), dtype=torch.int32, device="cuda")
+    s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    ql.qlinear_quantize_rtn(w, 4, 64, N, K, p, s, b)
+    del w
+    tq, tsb = ql.qlinear_repack(p, s, b, 4, 64, N, K)
+    gq, gsb = ql.qlinear_repack_glu(p, s, b, 4, 64, N, K)
+    del p, s, b
+    x = torch.from_numpy(inputs.activations_bf16(M, K, 3).view("int16")).cuda()
+    x16, rs = ql.qlinear_fast_activations(x, M, K)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    yg = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
+    ms_plain = time_calls(torch, lambda: ql.qlinear_forward_ex(
+        x, tq, tsb, None, 4, M, N, K, y, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs), 10, 3)
+    path_plain = ql.qlinear_last_path()
+    ms_glu = time_calls(torch, lambda: ql.qlinear_forward_ex(
+        x, gq, gsb, None, 4, M, N, K, yg, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs,
+        epilogue=ql.QL_EPI_SWIGLU), 10, 3)
+    tf = 2 * M * N * K / 1e12
+    rows["mlp_gateup_M4608_K4608_N24576_q4_fast"] = {
+        "path": path_plain, "us": round(ms_plain * 1e3, 1), "TFLOP/s": round(tf / (ms_plain * 1e-3), 1),
+        "out_bytes": M * N * 4}
+    rows["mlp_gateup_M4608_K4608_N24576_q4_swiglu_fused"] = {
+        "path": ql.qlinear_last_path(), "us": round(ms_glu * 1e3, 1), "TFLOP/s": round(tf / (ms_glu * 1e-3), 1),
+        "out_bytes": M * (N // 2) * 2}
+    log(f"gate/up plain {ms_plain*1e3:.1f} us, fused SwiGLU {ms_glu*1e3:.1f} us")
+    del tq, tsb, gq, gsb, x, x16, rs, y, yg
+
     M, K, N = 512, 53248, 4608
     copies = 4
     x = torch.from_numpy(inputs.activations_bf16(M, K, 4, "slices").view("int16")).cuda()

@@ -296,8 +296,16 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   dma_barrier();  // the copies requested past the last group have landed; every stage is free
 }
 
+// silu(g) * u: g / (1 + e^-g) with the hardware exponential and reciprocal;
+// e^-g overflows to +inf for g < -88 and the quotient is then -0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Stores rows m0 .. m0 + 16*MI of a tile, times the row scales, into out
-// ([M, N] fp32 or bf16).
+// ([M, N] fp32 or bf16). With GLU-ordered weights subtile ni = 0 of a wave
+// holds gate outputs and ni = 1 the up outputs of the same 16 columns
+// f = 16*strip + r16 of the [M, N/2] result, which gets silu(gate) * up.
 template <bool OUT_BF16, int MI>
 __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64_t m0, int64_t n0,
                                             const f32x4 (&acc)[MI][kNI]) {
@@ -306,6 +314,23 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, h = lane >> 4;
   const int64_t row0 = m0 + 4 * h;
+  if (a.glu) {
+    const int64_t F = a.N / 2;
+    const int64_t f = (n0 / 32 + wave) * 16 + r16;
+    if (f >= F) return;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = row0 + mi * 16 + i;
+        if (m >= a.M) continue;
+        const float rs = a.rowscale[m];
+        const float v = swiglu(acc[mi][0][i] * rs, acc[mi][1][i] * rs);
+        if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * F + f] = f32_to_bf16_rne3(v);
+        else reinterpret_cast<float *>(out)[m * F + f] = v;
+      }
+    return;
+  }
   const int64_t col0 = n0 + wave * kWN + r16;
   const bool full = (m0 + 16 * MI <= a.M) && (n0 + kBN <= a.N);
 #pragma unroll

@@ -263,6 +263,13 @@ int validate_forward(const ql_forward_args *a) {
   if (a->layout != QL_LAYOUT_CANONICAL && a->layout != QL_LAYOUT_TILED) return QL_EINVAL;
   if (a->mode != QL_MODE_AUTO && a->mode != QL_MODE_EXACT && a->mode != QL_MODE_FAST) return QL_EINVAL;
   if ((a->x16 == nullptr) != (a->rowscale == nullptr)) return QL_EINVAL;
+  if (a->epilogue != QL_EPI_NONE && a->epilogue != QL_EPI_SWIGLU) return QL_EINVAL;
+  if (a->epilogue == QL_EPI_SWIGLU) {
+    if (a->layout != QL_LAYOUT_TILED || a->mode == QL_MODE_EXACT || a->path == QL_PATH_SKINNY ||
+        a->path == QL_PATH_SPLITK || a->split_k > 1)
+      return QL_EUNSUPPORTED;
+    if (a->N % 32) return QL_EINVAL;
+  }
   if (a->M == 0 || a->N == 0) return QL_OK;
   if (!a->out) return QL_EINVAL;
   if (!aligned16(a->out)) return QL_EALIGN;
@@ -330,14 +337,19 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     set_last_path("noop");
     return QL_OK;
   }
+  const bool glu = a->epilogue == QL_EPI_SWIGLU;
+  const int64_t n_out = glu ? a->N / 2 : a->N;
   if (a->K == 0) {
     set_last_path("fill_zero");
-    return ql::launch_fill_zero(a->out, a->M * a->N, a->out_dtype == QL_OUT_BF16, stream) == hipSuccess ? QL_OK
-                                                                                                       : QL_EHIP;
+    return ql::launch_fill_zero(a->out, a->M * n_out, a->out_dtype == QL_OUT_BF16, stream) == hipSuccess ? QL_OK
+                                                                                                        : QL_EHIP;
   }
   Plan p;
-  st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, a->layout == QL_LAYOUT_TILED, a->mode,
-                 &p);
+  // the fused gate/up epilogue runs on the FAST GEMM without a K split (it
+  // needs finished sums), at any M
+  st = glu ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, true, QL_MODE_FAST, &p)
+           : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, a->layout == QL_LAYOUT_TILED,
+                       a->mode, &p);
   if (st != QL_OK) return st;
   const int G = (int)(a->K / kGroup);
   const int out_bf16 = a->out_dtype == QL_OUT_BF16;
@@ -382,8 +394,11 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales),
                      split ? static_cast<void *>(partial) : a->out,
                      a->M, a->N, a->K, G, split ? 0 : out_bf16,
-                     p.g3.dp_tiles, p.g3.tail_tiles, p.g3.tail_mi, p.g3.splits, p.g3.grid_x};
-    if (split)
+                     p.g3.dp_tiles, p.g3.tail_tiles, p.g3.tail_mi, p.g3.splits, p.g3.grid_x, glu ? 1 : 0};
+    if (glu)
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_swiglu_tiled", a->bits,
+                    p.g3.tail_tiles > 0 ? "_tail" : "");
+    else if (split)
       std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_split%d_tiled", a->bits, p.g3.splits);
     else if (p.g3.tail_tiles > 0)
       std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_tiled", a->bits, p.g3.tail_tiles,
@@ -602,7 +617,22 @@ QL_API int qlinear_repack(const uint32_t *packed_q, const void *scales, const vo
   if (!aligned16(packed_q) || !aligned16(tiled_q) || (reinterpret_cast<uintptr_t>(tiled_sb) & 3u)) return QL_EALIGN;
   set_last_path("repack");
   return ql::launch_repack(bits, packed_q, static_cast<const uint16_t *>(scales),
-                           static_cast<const uint16_t *>(biases), N, K, tiled_q, tiled_sb,
+                           static_cast<const uint16_t *>(biases), N, K, 0, tiled_q, tiled_sb,
+                           reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
+QL_API int qlinear_repack_glu(const uint32_t *packed_q, const void *scales, const void *biases, int bits, int group,
+                              int64_t N, int64_t K, uint32_t *tiled_q, uint32_t *tiled_sb, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup || N % 32) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!packed_q || !scales || !biases || !tiled_q || !tiled_sb) return QL_EINVAL;
+  if (!aligned16(packed_q) || !aligned16(tiled_q) || (reinterpret_cast<uintptr_t>(tiled_sb) & 3u)) return QL_EALIGN;
+  set_last_path("repack_glu");
+  return ql::launch_repack(bits, packed_q, static_cast<const uint16_t *>(scales),
+                           static_cast<const uint16_t *>(biases), N, K, N / 2, tiled_q, tiled_sb,
                            reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? QL_OK
              : QL_EHIP;
@@ -616,7 +646,21 @@ QL_API int qlinear_unrepack(const uint32_t *tiled_q, const uint32_t *tiled_sb, i
   if (!packed_q || !scales || !biases || !tiled_q || !tiled_sb) return QL_EINVAL;
   if (!aligned16(packed_q) || !aligned16(tiled_q) || (reinterpret_cast<uintptr_t>(tiled_sb) & 3u)) return QL_EALIGN;
   set_last_path("unrepack");
-  return ql::launch_unrepack(bits, tiled_q, tiled_sb, N, K, packed_q, static_cast<uint16_t *>(scales),
+  return ql::launch_unrepack(bits, tiled_q, tiled_sb, N, K, 0, packed_q, static_cast<uint16_t *>(scales),
+                             static_cast<uint16_t *>(biases), reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
+QL_API int qlinear_unrepack_glu(const uint32_t *tiled_q, const uint32_t *tiled_sb, int bits, int group, int64_t N,
+                                int64_t K, uint32_t *packed_q, void *scales, void *biases, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup || N % 32) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!packed_q || !scales || !biases || !tiled_q || !tiled_sb) return QL_EINVAL;
+  if (!aligned16(packed_q) || !aligned16(tiled_q) || (reinterpret_cast<uintptr_t>(tiled_sb) & 3u)) return QL_EALIGN;
+  set_last_path("unrepack_glu");
+  return ql::launch_unrepack(bits, tiled_q, tiled_sb, N, K, N / 2, packed_q, static_cast<uint16_t *>(scales),
                              static_cast<uint16_t *>(biases), reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? QL_OK
              : QL_EHIP;

@@ -18,6 +18,11 @@
 // pair of bf16 operands. 8-bit words keep little-endian byte order.
 // Scale and bias become one uint32 per (strip, group, column): s | b << 16,
 // ordered [strip][group][col]. Columns past N in the last strip are zero.
+//
+// GLU order (for a fused gate/up projection, rows [gate (F); up (F)], N = 2F,
+// F a multiple of 16): strip j holds gate rows 16j .. 16j+15 in its columns
+// 0..15 and up rows 16j .. 16j+15 in columns 16..31, so one lane of the GEMM
+// ends with a gate output and the matching up output in its registers.
 #include "ql_device.h"
 #include "ql_kernels.h"
 
@@ -67,11 +72,13 @@ __device__ __forceinline__ uint32_t from_pair_b2(uint32_t r) {
 
 // One thread per (strip, group, column): moves that column's codes of the group
 // (2*BITS words) and its scale/bias between the layouts.
+// glu_f > 0: GLU order with F = glu_f (tiled column col of strip `strip`
+// holds canonical row 16*strip + col, or F + 16*strip + col - 16).
 template <int BITS, bool TO_TILED>
 __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32_t *dst,
                                                      const uint16_t *s, const uint16_t *b,
                                                      uint32_t *sb, uint16_t *s_out,
-                                                     uint16_t *b_out, int64_t N, int64_t K) {
+                                                     uint16_t *b_out, int64_t N, int64_t K, int64_t glu_f) {
   constexpr int WPG = 2 * BITS;  // words of one column per group
   const int64_t G = K / 64;
   const int64_t N32 = (N + 31) / 32;
@@ -80,8 +87,8 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32
   const int col = (int)(idx % 32);
   const int64_t g = (idx / 32) % G;
   const int64_t strip = idx / (32 * G);
-  const int64_t n = strip * 32 + col;
-  const bool real = n < N;
+  const int64_t n = glu_f > 0 ? (col < 16 ? strip * 16 + col : glu_f + strip * 16 + (col - 16)) : strip * 32 + col;
+  const bool real = glu_f > 0 ? strip * 16 < glu_f : n < N;
   uint32_t *tile = TO_TILED ? dst : const_cast<uint32_t *>(src);
   uint32_t *blk = tile + (strip * G + g) * (32 * WPG);
   // tiled position of canonical word j (0..WPG-1) of this column
@@ -118,31 +125,31 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32
 
 template <int BITS, bool TO_TILED>
 hipError_t repack_bits(const uint32_t *src, uint32_t *dst, const uint16_t *s, const uint16_t *b,
-                       uint32_t *sb, uint16_t *s_out, uint16_t *b_out, int64_t N, int64_t K,
+                       uint32_t *sb, uint16_t *s_out, uint16_t *b_out, int64_t N, int64_t K, int64_t glu_f,
                        hipStream_t stream) {
   const int64_t threads = ((N + 31) / 32) * (K / 64) * 32;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((repack_kernel<BITS, TO_TILED>), dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, s,
-                     b, sb, s_out, b_out, N, K);
+                     b, sb, s_out, b_out, N, K, glu_f);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_repack(int bits, const uint32_t *canon, const uint16_t *s, const uint16_t *b, int64_t N,
-                         int64_t K, uint32_t *tiled, uint32_t *sb, hipStream_t stream) {
-  if (bits == 4) return repack_bits<4, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, stream);
-  if (bits == 8) return repack_bits<8, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, stream);
-  if (bits == 2) return repack_bits<2, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, stream);
+                         int64_t K, int64_t glu_f, uint32_t *tiled, uint32_t *sb, hipStream_t stream) {
+  if (bits == 4) return repack_bits<4, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
+  if (bits == 8) return repack_bits<8, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
+  if (bits == 2) return repack_bits<2, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, int64_t N, int64_t K,
+hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, int64_t N, int64_t K, int64_t glu_f,
                            uint32_t *canon, uint16_t *s, uint16_t *b, hipStream_t stream) {
   uint32_t *sbm = const_cast<uint32_t *>(sb);
-  if (bits == 4) return repack_bits<4, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, stream);
-  if (bits == 8) return repack_bits<8, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, stream);
-  if (bits == 2) return repack_bits<2, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, stream);
+  if (bits == 4) return repack_bits<4, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
+  if (bits == 8) return repack_bits<8, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
+  if (bits == 2) return repack_bits<2, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
   return hipErrorInvalidValue;
 }
 

@@ -72,6 +72,7 @@ struct Gemm3Args {
   int tail_mi;            // 16-row subtiles per piece: 2, 4 or 8
   int splits;             // K ranges (grid y)
   int grid_x;
+  int glu;                // 1: GLU-ordered weights, out = silu(gate) * up, [M, N/2]
 };
 struct Gemm3Plan {
   int64_t tiles;
@@ -104,9 +105,10 @@ struct SkinnyArgs {
 hipError_t launch_skinny(int bits, const SkinnyArgs &a, hipStream_t stream);
 
 // Tiled layout (see layout.hip): codes [N32][G][32 * 2*bits words], scale|bias [N32][G][32].
+// glu_f > 0: GLU row order for a [gate (glu_f); up (glu_f)] weight (see layout.hip).
 hipError_t launch_repack(int bits, const uint32_t *canon, const uint16_t *s, const uint16_t *b, int64_t N,
-                         int64_t K, uint32_t *tiled, uint32_t *sb, hipStream_t stream);
-hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, int64_t N, int64_t K,
+                         int64_t K, int64_t glu_f, uint32_t *tiled, uint32_t *sb, hipStream_t stream);
+hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, int64_t N, int64_t K, int64_t glu_f,
                            uint32_t *canon, uint16_t *s, uint16_t *b, hipStream_t stream);
 
 hipError_t launch_dequant(int bits, const uint32_t *w, const uint16_t *s, const uint16_t *b,

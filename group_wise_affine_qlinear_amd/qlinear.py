@@ -22,13 +22,15 @@ QL_OUT_F32, QL_OUT_BF16 = 0, 1
 QL_PATH_AUTO, QL_PATH_SKINNY, QL_PATH_GEMM, QL_PATH_SPLITK = 0, 1, 2, 3
 QL_LAYOUT_CANONICAL, QL_LAYOUT_TILED = 0, 1
 QL_MODE_AUTO, QL_MODE_EXACT, QL_MODE_FAST = 0, 1, 2
+QL_EPI_NONE, QL_EPI_SWIGLU = 0, 1
 
 EXPORTED = (
     "qlinear_forward", "qlinear_forward_ex", "qlinear_workspace_bytes", "qlinear_packed_words",
     "qlinear_pack_host", "qlinear_unpack_host", "qlinear_quantize_rtn_host", "qlinear_quantize_rtn",
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
     "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
-    "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations",
+    "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations", "qlinear_repack_glu",
+    "qlinear_unrepack_glu",
 )
 
 
@@ -62,6 +64,7 @@ class ql_forward_args(ctypes.Structure):
         ("mode", ctypes.c_int),
         ("x16", ctypes.c_void_p),
         ("rowscale", ctypes.c_void_p),
+        ("epilogue", ctypes.c_int),
     ]
 
 
@@ -106,6 +109,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_tiled_sb_words": ([i64, i64], sz),
         "qlinear_repack": ([vp, vp, vp, i32, i32, i64, i64, vp, vp, vp], i32),
         "qlinear_unrepack": ([vp, vp, i32, i32, i64, i64, vp, vp, vp, vp], i32),
+        "qlinear_repack_glu": ([vp, vp, vp, i32, i32, i64, i64, vp, vp, vp], i32),
+        "qlinear_unrepack_glu": ([vp, vp, i32, i32, i64, i64, vp, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -177,7 +182,7 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
                        workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
                        xsum=None, layout=QL_LAYOUT_CANONICAL, mode=QL_MODE_AUTO, x16=None,
-                       rowscale=None):
+                       rowscale=None, epilogue=QL_EPI_NONE):
     """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout, numerics mode
     and forced path.
 
@@ -185,6 +190,8 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
     ``qlinear_repack`` (tiled codes, tiled scale|bias words) and ``biases`` is ignored.
     ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights);
     ``x16``/``rowscale`` are optional FAST-mode activations from ``qlinear_fast_activations``.
+    ``epilogue=QL_EPI_SWIGLU`` takes GLU-ordered tiled weights (``qlinear_repack_glu``) and
+    writes ``out`` [M, N/2] = silu(gate) * up.
     """
     torch = _torch()
     u16 = _u16(torch)
@@ -208,7 +215,8 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
         a.out_dtype = QL_OUT_BF16
     else:
         raise TypeError("out must be float32 or bfloat16")
-    a.out = _dev_ptr(out, "out", (out.dtype,), (M, N))
+    a.epilogue = epilogue
+    a.out = _dev_ptr(out, "out", (out.dtype,), (M, N // 2 if epilogue == QL_EPI_SWIGLU else N))
     if workspace is not None:
         a.workspace = _dev_ptr(workspace, "workspace", (workspace.dtype,))
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -287,6 +295,42 @@ def qlinear_repack(packed_q, scales, biases, bits, group, N, K, tiled_q=None, ti
         _stream_handle(stream))
     _check(st, "qlinear_repack")
     return tiled_q, tiled_sb
+
+
+def qlinear_repack_glu(packed_q, scales, biases, bits, group, N, K, tiled_q=None, tiled_sb=None, stream=None):
+    """C ``qlinear_repack_glu``: stacked [gate; up] canonical weight -> tiled GLU order."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    dev = packed_q.device
+    if tiled_q is None:
+        tiled_q = torch.empty(qlinear_tiled_words(bits, N, K), dtype=torch.int32, device=dev)
+    if tiled_sb is None:
+        tiled_sb = torch.empty(qlinear_tiled_sb_words(N, K), dtype=torch.int32, device=dev)
+    st = lib.qlinear_repack_glu(
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)), bits, group, N, K,
+        _dev_ptr(tiled_q, "tiled_q", (torch.int32, torch.uint32), (qlinear_tiled_words(bits, N, K),)),
+        _dev_ptr(tiled_sb, "tiled_sb", (torch.int32, torch.uint32), (qlinear_tiled_sb_words(N, K),)),
+        _stream_handle(stream))
+    _check(st, "qlinear_repack_glu")
+    return tiled_q, tiled_sb
+
+
+def qlinear_unrepack_glu(tiled_q, tiled_sb, bits, group, N, K, packed_q, scales, biases, stream=None):
+    """C ``qlinear_unrepack_glu``: tiled GLU order -> stacked [gate; up] canonical, into the given tensors."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    st = lib.qlinear_unrepack_glu(
+        _dev_ptr(tiled_q, "tiled_q", (torch.int32, torch.uint32), (qlinear_tiled_words(bits, N, K),)),
+        _dev_ptr(tiled_sb, "tiled_sb", (torch.int32, torch.uint32), (qlinear_tiled_sb_words(N, K),)),
+        bits, group, N, K,
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)), _stream_handle(stream))
+    _check(st, "qlinear_unrepack_glu")
 
 
 def qlinear_unrepack(tiled_q, tiled_sb, bits, group, N, K, packed_q, scales, biases, stream=None):

@@ -86,6 +86,21 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  */
 typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
 
+/*
+ * Fused epilogues.
+ * SWIGLU: the weight is a gate projection stacked on an up projection, rows
+ *   [gate (F); up (F)], N = 2F with F a multiple of 16, repacked with
+ *   qlinear_repack_glu. The call writes out[m, f] = silu(g) * u for
+ *   f < F, where g = y[m, f], u = y[m, F + f] of the product y = x W^T and
+ *   silu(g) = g / (1 + exp(-g)), in fp32 (bf16 out: one RNE rounding of that
+ *   value); out is [M, F]. This is the SwiGLU MLP of the DiT block
+ *   (Ideogram 4 paper notes, section 2.1 pipeline and section 2.8 table).
+ *   Runs the FAST GEMM without a K split at any M; needs QL_LAYOUT_TILED,
+ *   mode AUTO or FAST and path AUTO or GEMM, else QL_EUNSUPPORTED; N not a
+ *   multiple of 32 is QL_EINVAL.
+ */
+typedef enum { QL_EPI_NONE = 0, QL_EPI_SWIGLU = 1 } ql_epilogue;
+
 typedef enum {
   QL_PATH_AUTO = 0,      /* dispatch table decides                            */
   QL_PATH_SKINNY = 1,    /* wavefront GEMV kernel, M <= 16                    */
@@ -102,7 +117,7 @@ typedef struct ql_forward_args {
   int bits;                  /* 2, 4 or 8                                    */
   int group;                 /* 64                                           */
   int64_t M, N, K;
-  void *out;                 /* [M, N], dtype per out_dtype                  */
+  void *out;                 /* [M, N] ([M, N/2] with QL_EPI_SWIGLU), dtype per out_dtype */
   int out_dtype;             /* ql_out_dtype                                 */
   void *workspace;           /* device scratch, may be NULL if ws_bytes==0   */
   size_t workspace_bytes;    /* >= qlinear_workspace_bytes(...)              */
@@ -125,6 +140,7 @@ typedef struct ql_forward_args {
   const float *rowscale;     /* [M] row scales from qlinear_fast_activations
                                 for this x; both NULL = computed inside the
                                 call (both or neither must be given)        */
+  int epilogue;              /* ql_epilogue; QL_EPI_NONE = plain y           */
 } ql_forward_args;
 
 /*
@@ -237,6 +253,21 @@ size_t qlinear_tiled_sb_words(int64_t N, int64_t K);
 int qlinear_repack(const uint32_t *packed_q, const void *scales, const void *biases, int bits,
                    int group, int64_t N, int64_t K, uint32_t *tiled_q, uint32_t *tiled_sb,
                    void *stream);
+
+/*
+ * Device repack of a stacked gate/up weight, rows [gate (N/2); up (N/2)],
+ * canonical -> tiled in GLU order (strip j holds gate rows 16j .. 16j+15,
+ * then up rows 16j .. 16j+15), for QL_EPI_SWIGLU. Same array sizes as
+ * qlinear_repack; N must be a multiple of 32 (QL_EINVAL otherwise).
+ */
+int qlinear_repack_glu(const uint32_t *packed_q, const void *scales, const void *biases, int bits,
+                       int group, int64_t N, int64_t K, uint32_t *tiled_q, uint32_t *tiled_sb,
+                       void *stream);
+
+/* Inverse of qlinear_repack_glu. */
+int qlinear_unrepack_glu(const uint32_t *tiled_q, const uint32_t *tiled_sb, int bits, int group,
+                         int64_t N, int64_t K, uint32_t *packed_q, void *scales, void *biases,
+                         void *stream);
 
 /* Device unrepack, tiled -> canonical (inverse of qlinear_repack). */
 int qlinear_unrepack(const uint32_t *tiled_q, const uint32_t *tiled_sb, int bits, int group,

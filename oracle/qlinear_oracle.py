@@ -37,6 +37,12 @@ pages do not describe; ``forward_fast`` writes out its definition (weights
 rounded once to fp16, activations scaled per row by a power of two into
 fp16) so the GPU path can be compared with it to fp32-accumulation accuracy,
 while ``forward`` remains the reference for the error budget.
+
+SwiGLU (the DiT block's MLP: Ideogram 4 paper notes, section 2.1 pipeline,
+section 2.8 table "SwiGLU MLP"; the notes print no formula). Reading taken:
+the standard gated form silu(x W_gate^T) * (x W_up^T) with silu(v) =
+v / (1 + e^-v), the gate and up weights stacked as rows [gate; up] of one
+projection. ``swiglu`` applies it to an exact product in float64.
 """
 from __future__ import annotations
 
@@ -50,7 +56,7 @@ __all__ = [
     "f16_bits_to_f32", "f32_to_f16_bits", "bf16_bits_to_f64",
     "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
     "forward_rows", "error_metrics", "timed_forward",
-    "fast_weights_f16", "fast_activations_f16", "forward_fast",
+    "fast_weights_f16", "fast_activations_f16", "forward_fast", "forward_fast_rows", "silu", "swiglu",
 ]
 
 GROUP = 64
@@ -267,6 +273,31 @@ def forward_fast(x_bf16, packed, s16, b16, bits, k, group: int = GROUP) -> np.nd
     w16 = fast_weights_f16(q, s16, b16, group).astype(np.float64)
     x16, scale = fast_activations_f16(x_bf16)
     return scale[:, None] * (x16.astype(np.float64) @ w16.T)
+
+
+def forward_fast_rows(x_bf16, packed, s16, b16, bits, k, rows, cols=None, group: int = GROUP):
+    """``forward_fast`` restricted to selected output rows (and columns): the
+    row scales depend only on their row and the fp16 weights only on theirs."""
+    x_sel = np.asarray(x_bf16)[np.asarray(rows)]
+    if cols is not None:
+        cols = np.asarray(cols)
+        packed, s16, b16 = packed[cols], s16[cols], b16[cols]
+    return forward_fast(x_sel, packed, s16, b16, bits, k, group)
+
+
+def silu(v) -> np.ndarray:
+    """silu(v) = v * sigmoid(v) = v / (1 + exp(-v)), float64; exp overflow for
+    v < -709 gives v / inf = -0, the limit."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu(y: np.ndarray, f: int) -> np.ndarray:
+    """Gated output of a stacked [gate; up] product y [M, 2f]: silu(y[:, :f]) * y[:, f:]."""
+    y = np.asarray(y, dtype=np.float64)
+    assert y.shape[1] == 2 * f
+    return silu(y[:, :f]) * y[:, f:]
 
 
 def error_metrics(y: np.ndarray, y_ref: np.ndarray) -> dict:

@@ -1,0 +1,163 @@
+"""GPU tests of the fused SwiGLU epilogue on a stacked [gate; up] projection.
+
+The weight's rows are [gate (F); up (F)]; ``qlinear_repack_glu`` stores them
+in GLU order and ``qlinear_forward_ex(..., epilogue=QL_EPI_SWIGLU)`` writes
+silu(gate) * up, [M, F].
+
+Bounds. The gate and up sums are the FAST GEMM's, so the kernel is compared
+with ``oracle.swiglu`` of the oracle's FAST definition at the FAST design
+tolerance (only fp32 accumulation and the fp32 exponential and reciprocal
+differ), and with ``oracle.swiglu`` of the exact product by relative
+Frobenius error at the FAST budget. A max-abs bound against the exact product
+is not used: silu(g) * u multiplies two fields that each carry the fp16
+weight rounding, so its largest errors sit on the largest |g u| products,
+far out in a product distribution's tail relative to its rms."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs
+from group_wise_affine_qlinear_amd import qlinear as ql
+
+from gpu_helpers import (MAXABS_RMS_DESIGN, RELF_DESIGN, RELF_TOL, Case, dev, host_u16, host_u32,
+                         torch_or_skip)
+
+pytestmark = pytest.mark.gpu
+
+RELF_FAST = 5e-4
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_or_skip()
+    ql.load_library()
+    return t
+
+
+def glu_rows(N):
+    """Canonical row held by each tiled row position in GLU order (the layout's definition)."""
+    F = N // 2
+    t = np.arange(N)
+    strip, col = t // 32, t % 32
+    return np.where(col < 16, strip * 16 + col, F + strip * 16 + col - 16)
+
+
+def run_glu(torch, c, out_dtype="f32", **kw):
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack_glu(p, s, b, c.bits, 64, c.N, c.K)
+    F = c.N // 2
+    if out_dtype == "f32":
+        out = torch.full((c.M, F), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        out = torch.zeros((c.M, F), dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward_ex(x, tq, tsb, None, c.bits, c.M, c.N, c.K, out, layout=ql.QL_LAYOUT_TILED,
+                          epilogue=ql.QL_EPI_SWIGLU, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(y, c, rows=None, fs=None):
+    """y: the kernel's [rows, fs] block of silu(gate) * up for case c."""
+    y = np.asarray(y, dtype=np.float64)
+    assert np.all(np.isfinite(y)), "non-finite output"
+    F = c.N // 2
+    rows = np.arange(c.M) if rows is None else rows
+    fs = np.arange(F) if fs is None else fs
+    cols = np.concatenate([fs, F + fs])
+    ref_fast = oracle.swiglu(oracle.forward_fast_rows(c.x, c.packed, c.s16, c.b16, c.bits, c.K, rows, cols), len(fs))
+    e = oracle.error_metrics(y, ref_fast)
+    assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, ("vs FAST definition", e)
+    ref = oracle.swiglu(oracle.forward_rows(c.x, c.packed, c.s16, c.b16, c.bits, c.K, rows, cols), len(fs))
+    e2 = oracle.error_metrics(y, ref)
+    assert e2["relF"] <= RELF_FAST <= RELF_TOL, ("vs exact product", e2)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_glu_repack_is_a_row_permutation_and_round_trips(torch, bits):
+    N, K = 96 * 2, 320
+    c = Case(8, N, K, bits, wid=500 + bits)
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack_glu(p, s, b, bits, 64, N, K)
+    # same bytes as the plain tiled repack of the weight with its rows permuted
+    perm = glu_rows(N)
+    pp, sp, bp = dev(torch, c.packed[perm]), dev(torch, c.s16[perm]), dev(torch, c.b16[perm])
+    tq2, tsb2 = ql.qlinear_repack(pp, sp, bp, bits, 64, N, K)
+    assert np.array_equal(host_u32(tq), host_u32(tq2)) and np.array_equal(host_u32(tsb), host_u32(tsb2))
+    p3, s3, b3 = torch.zeros_like(p), torch.zeros_like(s), torch.zeros_like(b)
+    ql.qlinear_unrepack_glu(tq, tsb, bits, 64, N, K, p3, s3, b3)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u32(p3), c.packed) and np.array_equal(host_u16(s3), c.s16)
+    assert np.array_equal(host_u16(b3), c.b16)
+
+
+GLU_SHAPES = [(520, 800, 320), (300, 2080, 448), (64, 32, 128), (5, 512, 640), (17, 1056, 256)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("shape", GLU_SHAPES)
+def test_swiglu_parity(torch, shape, bits):
+    M, N, K = shape
+    c = Case(M, N, K, bits, wid=510 + bits, x_structure="outlier")
+    y = run_glu(torch, c).cpu().numpy()
+    assert "swiglu" in ql.qlinear_last_path(), ql.qlinear_last_path()
+    check(y, c)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_swiglu_bf16_out_is_rounded_fp32_out(torch, bits):
+    c = Case(300, 640, 384, bits, wid=520 + bits)
+    y = run_glu(torch, c).cpu().numpy()
+    yb = run_glu(torch, c, out_dtype="bf16")
+    got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(y))
+
+
+# (slots, shape): 9 tiles over 8 blocks (1 tail tile x 8 pieces of 32 rows),
+# 12 over 10 (2 x 4 pieces, last tile row ragged), 9 over 7 (2 x 2 pieces)
+@pytest.mark.parametrize("slots,shape", [(8, (256, 2304, 320)), (10, (520, 1024, 448)), (7, (700, 768, 320))])
+def test_swiglu_with_tail_pieces(torch, monkeypatch, slots, shape):
+    M, N, K = shape
+    monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
+    c = Case(M, N, K, 4, wid=530)
+    y = run_glu(torch, c).cpu().numpy()
+    assert "_tail" in ql.qlinear_last_path(), ql.qlinear_last_path()
+    check(y, c)
+
+
+def test_swiglu_rejects_unsupported_requests(torch):
+    c = Case(64, 256, 256, 4, wid=540)
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack_glu(p, s, b, 4, 64, 256, 256)
+    out = torch.empty((64, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(ql.QLinearError):   # canonical layout
+        ql.qlinear_forward_ex(x, p, s, b, 4, 64, 256, 256, out, epilogue=ql.QL_EPI_SWIGLU)
+    with pytest.raises(ql.QLinearError):   # EXACT numerics
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
+                              mode=ql.QL_MODE_EXACT, epilogue=ql.QL_EPI_SWIGLU)
+    with pytest.raises(ql.QLinearError):   # K split
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
+                              path=ql.QL_PATH_SPLITK, epilogue=ql.QL_EPI_SWIGLU)
+    with pytest.raises(ql.QLinearError):   # N not a multiple of 32
+        c2 = Case(8, 48, 128, 4, wid=541)
+        x2, p2, s2, b2 = c2.device(torch)
+        t2, sb2 = ql.qlinear_repack(p2, s2, b2, 4, 64, 48, 128)
+        ql.qlinear_forward_ex(x2, t2, sb2, None, 4, 8, 48, 128, torch.empty((8, 24), device="cuda"),
+                              layout=ql.QL_LAYOUT_TILED, epilogue=ql.QL_EPI_SWIGLU)
+    with pytest.raises(ql.QLinearError):   # GLU repack needs N a multiple of 32
+        ql.qlinear_repack_glu(p2, s2, b2, 4, 64, 48, 128)
+
+
+def test_swiglu_full_size_mlp_gate_up_sampled(torch):
+    """The SwiGLU MLP's gate/up projection at 1024x1024 (M=4608, K=4608,
+    F=12288, 4-bit), on sampled outputs."""
+    wl = inputs.WORKLOADS["mlp_gateup_1024"]
+    M, K, N = wl["M"], wl["K"], wl["N"]
+    F = N // 2
+    c = Case(M, N, K, 4, wid=wl["id"])
+    rng = np.random.default_rng(550)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 60)]))
+    fs = np.unique(np.concatenate([[0, 15, 16, 127, 128, F - 1], rng.integers(0, F, 60)]))
+    out = run_glu(torch, c)
+    assert bool(torch.isfinite(out).all())
+    blk = out.index_select(0, torch.from_numpy(rows).cuda()).index_select(1, torch.from_numpy(fs).cuda())
+    check(blk.cpu().numpy(), c, rows, fs)

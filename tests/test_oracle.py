@@ -482,3 +482,57 @@ def test_fast_error_budget_on_normal_weights():
     e = oracle.error_metrics(oracle.forward_fast(xb, packed, s16, b16, 4, 512),
                              oracle.forward(xb, packed, s16, b16, 4, 512))
     assert 5e-5 < e["relF"] < 5e-4 and e["maxabs_over_rms"] < 3e-3, e
+
+
+# ---- SwiGLU (stacked gate/up projection) ------------------------------------
+
+def test_silu_closed_forms():
+    # sigmoid(ln 3) = 3/4, sigmoid(0) = 1/2, sigmoid(-ln 3) = 1/4
+    ln3 = math.log(3.0)
+    got = oracle.silu(np.array([0.0, ln3, -ln3, 1000.0, -1000.0]))
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.75 * ln3) < 1e-15 and abs(got[2] + 0.25 * ln3) < 1e-15
+    assert got[3] == 1000.0 and got[4] == 0.0 and math.copysign(1.0, got[4]) < 0
+
+
+def test_silu_matches_library_logistic():
+    from scipy.special import expit
+    v = np.linspace(-40, 40, 2001)
+    np.testing.assert_allclose(oracle.silu(v), v * expit(v), rtol=1e-14, atol=1e-300)
+    # odd part: silu(v) - silu(-v) = v
+    np.testing.assert_allclose(oracle.silu(v) - oracle.silu(-v), v, rtol=0, atol=1e-13)
+
+
+def test_swiglu_pairs_gate_with_up_of_the_same_column():
+    y = np.array([[1.0, 2.0, 3.0, 10.0, 20.0, 30.0]])
+    got = oracle.swiglu(y, 3)
+    expect = np.array([[10.0 / (1 + math.exp(-1.0)), 20.0 * 2 / (1 + math.exp(-2.0)), 30.0 * 3 / (1 + math.exp(-3.0))]])
+    np.testing.assert_allclose(got, expect, rtol=1e-15)
+
+
+def test_forward_fast_rows_is_a_restriction_of_forward_fast():
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((40, 192)) * 0.02).astype(np.float32)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    packed = oracle.pack(q, 4)
+    x = rng.standard_normal((30, 192)).astype(np.float32)
+    x[4] *= 1e5
+    xb = inputs.f32_to_bf16_bits(x)
+    full = oracle.forward_fast(xb, packed, s16, b16, 4, 192)
+    rows, cols = np.array([0, 4, 29]), np.array([3, 17, 39])
+    assert np.array_equal(oracle.forward_fast_rows(xb, packed, s16, b16, 4, 192, rows, cols), full[rows][:, cols])
+
+
+def test_swiglu_fast_definition_error_budget():
+    # the FAST numerics (fp16 weights) carried through silu(g) * u stay within
+    # the FAST budget of relative Frobenius error against the exact product
+    rng = np.random.default_rng(13)
+    F, K = 64, 512
+    w = (rng.standard_normal((2 * F, K)) * 0.02).astype(np.float32)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    packed = oracle.pack(q, 4)
+    xb = inputs.f32_to_bf16_bits(rng.standard_normal((48, K)).astype(np.float32))
+    fast = oracle.swiglu(oracle.forward_fast(xb, packed, s16, b16, 4, K), F)
+    exact = oracle.swiglu(oracle.forward(xb, packed, s16, b16, 4, K), F)
+    e = oracle.error_metrics(fast, exact)
+    assert 1e-5 < e["relF"] < 5e-4, e
