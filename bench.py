@@ -168,6 +168,48 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     log(f"gate/up plain {ms_plain*1e3:.1f} us, fused SwiGLU {ms_glu*1e3:.1f} us")
     del tq, tsb, gq, gsb, x, x16, rs, y, yg
 
+    # 2048x2048 canvas: per-bit layer sweep, and one pass over the 34 blocks'
+    # attention projections (QKV N=13824 then out N=4608) with 34 distinct
+    # weight sets per width (every launch streams its weights)
+    M, K = 16896, 4608
+    x = torch.from_numpy(inputs.activations_bf16(M, K, 5).view("int16")).cuda()
+    x16, rs = ql.qlinear_fast_activations(x, M, K)
+    for bits in (2, 4, 8):
+        layers = []
+        for N in (13824, 4608):
+            w = torch.from_numpy(inputs.weights(N, K, 5 if N == 4608 else 50)).cuda()
+            p = torch.empty((N, K * bits // 32), dtype=torch.int32, device="cuda")
+            s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+            b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+            ql.qlinear_quantize_rtn(w, bits, 64, N, K, p, s, b)
+            del w
+            sets = [ql.qlinear_repack(p, s, b, bits, 64, N, K) for _ in range(34)]
+            del p, s, b
+            out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            layers.append((N, sets, out))
+            tq, tsb = sets[0]
+            ms = time_calls(torch, lambda: ql.qlinear_forward_ex(
+                x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs), 10, 3)
+            rows[f"sweep_2048_M{M}_K{K}_N{N}_q{bits}"] = {
+                "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1),
+                "TFLOP/s": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+
+        def one_pass():
+            for i in range(34):
+                for N, sets, out in layers:
+                    tq, tsb = sets[i]
+                    ql.qlinear_forward_ex(x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
+                                          x16=x16, rowscale=rs)
+
+        ms = time_calls(torch, one_pass, 3, 1)
+        flop = 34 * sum(2 * M * N * K for N, _, _ in layers)
+        rows[f"sweep_2048_34_layer_qkv_out_pass_q{bits}"] = {
+            "ms": round(ms, 2), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1), "weight_sets": 34,
+            "note": "34 x (QKV 16896x4608->13824 + out 16896x4608->4608), shared fp16 activations"}
+        log(f"2048 sweep q{bits}: 34-layer pass {ms:.2f} ms")
+        del layers
+    del x, x16, rs
+
     M, K, N = 512, 53248, 4608
     copies = 4
     x = torch.from_numpy(inputs.activations_bf16(M, K, 4, "slices").view("int16")).cuda()
