@@ -57,6 +57,7 @@ __all__ = [
     "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
     "forward_rows", "error_metrics", "timed_forward",
     "fast_weights_f16", "fast_activations_f16", "forward_fast", "forward_fast_rows", "silu", "swiglu",
+    "IMATRIX_DELTAS", "quantize_imatrix", "weighted_error",
 ]
 
 GROUP = 64
@@ -156,6 +157,137 @@ def quantize_rtn(w: np.ndarray, bits: int, group: int = GROUP):
     q = np.clip(q, 0, qmax)
     q = np.where(zero[:, :, None], np.float32(0), q)
     return q.astype(np.uint8).reshape(n, k), s16, b16
+
+
+# ------------------------------------------------- importance-weighted fit
+
+# Level-count offsets of the scale search: candidate t starts from codes
+# l = rint((w - min) * (Q + d_t) / (max - min)), d_t = (t - 7.5) / 10.
+IMATRIX_DELTAS = tuple((t - 7.5) / 10.0 for t in range(16))
+
+
+def _f32(v):
+    return np.float32(v)
+
+
+def _group_error(w, a, s_f, b_f, q):
+    """sum_j a_j * e_j * e_j, e_j = w_j - (s*q_j + b), fp32, j in order; the
+    product s*q_j is exact in fp32 (f16 scale, code < 256), so s*q + b rounds once."""
+    err = np.zeros(w.shape[:-1], dtype=np.float32)
+    for j in range(w.shape[-1]):
+        dq = s_f * q[..., j] + b_f
+        e = w[..., j] - dq
+        err = err + a[..., j] * (e * e)
+    return err
+
+
+def _codes(w, s_f, b_f, qmax):
+    """clamp(rint_half_even((w - b) / s), 0, Q) in fp32, 0 where s == 0."""
+    zero = s_f == 0
+    safe = np.where(zero, np.float32(1), s_f)
+    q = np.clip(np.rint((w - b_f[..., None]) / safe[..., None]), 0, qmax).astype(np.float32)
+    return np.where(zero[..., None], np.float32(0), q)
+
+
+def quantize_imatrix(w: np.ndarray, importance: np.ndarray, bits: int, group: int = GROUP):
+    """Importance-weighted affine fit per (row, 64-group), same storage as ``quantize_rtn``.
+
+    Objective (Ideogram-4-IQ4_M card, section on what "IQ4" means): an error
+    dW_j in input channel j adds dW_j^2 * E[x_j^2] to the output, so each group
+    minimises E(s, b) = sum_j E[x_j^2] (w_j - W_hat_j)^2 over its f16 scale and
+    bias; the min/max round-to-nearest fit is candidate 0, so the result is
+    never worse than RTN by this objective. The pages do not give the other
+    candidates; reading taken (this oracle's own search): starting codes l are
+    (1) the RTN codes, (2) for each offset d in ``IMATRIX_DELTAS``
+    l_j = clamp(rint((w_j - lo) * (Q + d) / (hi - lo)), 0, Q) with [lo, hi] the
+    group's [min, max], then (3) the same 16 with [lo, hi] the min and max over
+    the channels of nonzero importance (so an outlier in an unweighted channel
+    does not set the step). For each, solve the weighted least-squares line
+    w ~ s*l + b, round s and b to f16, recompute the codes from the stored s
+    and b as RTN does, and keep the candidate with the smallest E (strictly
+    smaller: earlier candidates win ties). Candidates whose f16 scale is not a
+    positive finite number, or whose bias is not finite, are skipped, as are
+    ranges with hi <= lo; a group whose RTN scale is zero keeps RTN.
+
+    Arithmetic: fp32 with one IEEE rounding per operation, no fused
+    multiply-add, sums over j = 0..63 in order:
+      S0 = sum a_j, S1 = sum a_j*l_j, S2 = sum (a_j*l_j)*l_j,
+      T0 = sum a_j*w_j, T1 = sum (a_j*l_j)*w_j,
+      D = S0*S2 - S1*S1 (skip unless D > 0),
+      s = (S0*T1 - S1*T0) / D, b = (S2*T0 - S1*T1) / D,
+      E = sum a_j * (e_j * e_j), e_j = w_j - (s*q_j + b).
+    ``importance`` is [K], finite and >= 0. Returns (q uint8 [N, K], s16, b16).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    imp = np.asarray(importance, dtype=np.float32)
+    n, k = w.shape
+    if imp.shape != (k,):
+        raise ValueError("importance must be [K]")
+    if not (np.all(np.isfinite(imp)) and np.all(imp >= 0)):
+        raise ValueError("importance must be finite and >= 0")
+    q0, s16, b16 = quantize_rtn(w, bits, group)
+    qmax = np.float32(2 ** bits - 1)
+    g = k // group
+    wg = w.reshape(n, g, group)
+    a = np.broadcast_to(imp.reshape(1, g, group), wg.shape)
+    q_best = q0.reshape(n, g, group).astype(np.float32)
+    s_best, b_best = s16.copy(), b16.copy()
+    err_best = _group_error(wg, a, f16_bits_to_f32(s16), f16_bits_to_f32(b16), q_best)
+    live0 = f16_bits_to_f32(s16) != 0
+    weighted = a > 0
+    ranges = [(wg.min(axis=2), wg.max(axis=2)),
+              (np.where(weighted, wg, np.float32(np.inf)).min(axis=2),
+               np.where(weighted, wg, np.float32(-np.inf)).max(axis=2))]
+    q_rtn = q_best.copy()
+    cands = [(None, None)] + [(r, d) for r in range(2) for d in IMATRIX_DELTAS]
+    for r, d in cands:
+        live = live0.copy()
+        if d is None:
+            l = q_rtn   # the RTN codes
+        else:
+            lo, hi = ranges[r]
+            live &= hi > lo
+            width = np.where(live, hi - lo, np.float32(1))
+            lo = np.where(live, lo, np.float32(0))
+            inv = (qmax + _f32(d)) / width
+            l = np.clip(np.rint((wg - lo[..., None]) * inv[..., None]), 0, qmax).astype(np.float32)
+        S0 = np.zeros((n, g), np.float32); S1 = np.zeros((n, g), np.float32); S2 = np.zeros((n, g), np.float32)
+        T0 = np.zeros((n, g), np.float32); T1 = np.zeros((n, g), np.float32)
+        for j in range(group):
+            al = a[..., j] * l[..., j]
+            S0 = S0 + a[..., j]
+            S1 = S1 + al
+            S2 = S2 + al * l[..., j]
+            T0 = T0 + a[..., j] * wg[..., j]
+            T1 = T1 + al * wg[..., j]
+        D = S0 * S2 - S1 * S1
+        ok = live & (D > 0)
+        safe_d = np.where(ok, D, np.float32(1))
+        with np.errstate(over="ignore", invalid="ignore"):
+            sc = (S0 * T1 - S1 * T0) / safe_d
+            bc = (S2 * T0 - S1 * T1) / safe_d
+        sc16, bc16 = f32_to_f16_bits(sc), f32_to_f16_bits(bc)
+        sf, bf = f16_bits_to_f32(sc16), f16_bits_to_f32(bc16)
+        ok &= np.isfinite(sf) & (sf > 0) & np.isfinite(bf)
+        sf = np.where(ok, sf, np.float32(1))
+        bf = np.where(ok, bf, np.float32(0))
+        qc = _codes(wg, sf, bf, qmax)
+        ec = _group_error(wg, a, sf, bf, qc)
+        better = ok & (ec < err_best)
+        err_best = np.where(better, ec, err_best)
+        s_best = np.where(better, sc16, s_best)
+        b_best = np.where(better, bc16, b_best)
+        q_best = np.where(better[..., None], qc, q_best)
+    return q_best.astype(np.uint8).reshape(n, k), s_best.astype(np.uint16), b_best.astype(np.uint16)
+
+
+def weighted_error(w, importance, q, s16, b16, group: int = GROUP) -> np.ndarray:
+    """The fit objective in float64: per (row, group) sum_j E[x_j^2] (w_j - W_hat_j)^2."""
+    w = np.asarray(w, dtype=np.float64)
+    n, k = w.shape
+    wh = dequantize(q, s16, b16, group).astype(np.float64)
+    e2 = (w - wh) ** 2 * np.asarray(importance, dtype=np.float64)[None, :]
+    return e2.reshape(n, k // group, group).sum(axis=2)
 
 
 # ---------------------------------------------------------------- packing

@@ -536,3 +536,71 @@ def test_swiglu_fast_definition_error_budget():
     exact = oracle.swiglu(oracle.forward(xb, packed, s16, b16, 4, K), F)
     e = oracle.error_metrics(fast, exact)
     assert 1e-5 < e["relF"] < 5e-4, e
+
+
+# ---- importance-weighted fit (the pages' imatrix objective) ---------------
+
+def _outlier_importance(k, wid):
+    x = inputs.activations_f32(64, k, wid, "outlier").astype(np.float64)
+    return (x * x).mean(axis=0).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_imatrix_never_worse_than_rtn(bits):
+    # candidate 0 is the min/max RTN fit, so the objective never increases
+    w = inputs.weights(96, 512, 60 + bits)
+    imp = _outlier_importance(512, 60 + bits)
+    q, s16, b16 = oracle.quantize_imatrix(w, imp, bits)
+    q0, s0, b0 = oracle.quantize_rtn(w, bits)
+    e = oracle.weighted_error(w, imp, q, s16, b16)
+    e0 = oracle.weighted_error(w, imp, q0, s0, b0)
+    assert np.all(e <= e0 * (1 + 1e-6) + 1e-30)
+    assert e.sum() < 0.6 * e0.sum()   # and it helps on outlier-channel importance
+    assert q.max() <= 2 ** bits - 1
+
+
+def test_imatrix_keeps_rtn_when_rtn_is_exact():
+    # weights exactly on an f16 affine grid: RTN has zero error, every later
+    # candidate can at best tie, and ties keep candidate 0
+    q = np.tile(np.arange(16, dtype=np.float32), 4)[None, :]
+    w = (np.float32(0.125) * q + np.float32(-1.0)).astype(np.float32)
+    imp = np.linspace(0.5, 2.0, 64).astype(np.float32)
+    got = oracle.quantize_imatrix(w, imp, 4)
+    ref = oracle.quantize_rtn(w, 4)
+    for a_, b_ in zip(got, ref):
+        assert np.array_equal(a_, b_)
+
+
+def test_imatrix_ignores_an_outlier_in_an_unweighted_channel():
+    # 63 weighted values spread over [0, 0.3] and one value 10 whose channel
+    # has zero importance: RTN's step (10/15) maps every weighted value to
+    # code 0; the fit over the weighted range reproduces them closely
+    w = np.concatenate([np.linspace(0, 0.3, 63), [10.0]]).astype(np.float32)[None, :]
+    imp = np.ones(64, np.float32)
+    imp[63] = 0
+    q, s16, b16 = oracle.quantize_imatrix(w, imp, 4)
+    q0, s0, b0 = oracle.quantize_rtn(w, 4)
+    e = oracle.weighted_error(w, imp, q, s16, b16)[0, 0]
+    e0 = oracle.weighted_error(w, imp, q0, s0, b0)[0, 0]
+    assert e0 > 1.0 and e < 0.01 * e0
+    # the half-step bound of a uniform grid over [0, 0.3] with 15 steps
+    wh = oracle.dequantize(q, s16, b16)[0, :63].astype(np.float64)
+    assert np.max(np.abs(wh - w[0, :63])) <= 0.3 / 15 / 2 * 1.1
+
+
+def test_imatrix_is_invariant_to_scaling_importance_by_two():
+    # the objective scales by exactly 2 in fp32, so every comparison, and so
+    # the chosen fit, is unchanged bit for bit
+    w = inputs.weights(32, 256, 64)
+    imp = _outlier_importance(256, 64)
+    a = oracle.quantize_imatrix(w, imp, 4)
+    b = oracle.quantize_imatrix(w, imp * np.float32(2), 4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_imatrix_rejects_bad_importance():
+    w = inputs.weights(4, 64, 65)
+    for bad in (np.full(64, -1.0, np.float32), np.full(64, np.nan, np.float32), np.ones(32, np.float32)):
+        with pytest.raises(ValueError):
+            oracle.quantize_imatrix(w, bad, 4)
