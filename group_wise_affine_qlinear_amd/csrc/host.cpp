@@ -598,6 +598,21 @@ QL_API int qlinear_quantize_rtn(const float *w, int bits, int group, int64_t N, 
              : QL_EHIP;
 }
 
+QL_API int qlinear_quantize_imatrix(const float *w, const float *importance, int bits, int group, int64_t N,
+                                    int64_t K, uint32_t *packed_q, uint16_t *scales, uint16_t *biases,
+                                    int *status_dev, void *stream) {
+  if (!bits_ok(bits) || group != kGroup) return QL_EUNSUPPORTED;
+  if (N < 0 || K < 0 || K % kGroup) return QL_EINVAL;
+  if (N == 0 || K == 0) return QL_OK;
+  if (!w || !importance || !packed_q || !scales || !biases) return QL_EINVAL;
+  if (!aligned16(w) || !aligned16(importance) || !aligned16(packed_q)) return QL_EALIGN;
+  set_last_path("quantize_imatrix");
+  return ql::launch_quantize_imatrix(bits, w, importance, N, K, packed_q, scales, biases, status_dev,
+                                     reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
 QL_API size_t qlinear_tiled_words(int bits, int64_t N, int64_t K) {
   if (!bits_ok(bits) || N < 0 || K < 0 || K % kGroup) return 0;
   return (size_t)round_up(N, 32) * (size_t)K * (size_t)bits / 32u;

@@ -115,5 +115,7 @@ hipError_t launch_dequant(int bits, const uint32_t *w, const uint16_t *s, const 
                           int64_t N, int64_t K, float *out, hipStream_t stream);
 hipError_t launch_quantize(int bits, const float *w, int64_t N, int64_t K, uint32_t *packed,
                            uint16_t *s, uint16_t *b, int *status, hipStream_t stream);
+hipError_t launch_quantize_imatrix(int bits, const float *w, const float *imp, int64_t N, int64_t K,
+                                  uint32_t *packed, uint16_t *s, uint16_t *b, int *status, hipStream_t stream);
 
 }  // namespace ql

@@ -30,7 +30,7 @@ EXPORTED = (
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
     "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
     "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations", "qlinear_repack_glu",
-    "qlinear_unrepack_glu",
+    "qlinear_unrepack_glu", "qlinear_quantize_imatrix",
 )
 
 
@@ -98,6 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_unpack_host": ([vp, i32, i64, i64, vp], i32),
         "qlinear_quantize_rtn_host": ([vp, i32, i32, i64, i64, vp, vp, vp], i32),
         "qlinear_quantize_rtn": ([vp, i32, i32, i64, i64, vp, vp, vp, vp, vp], i32),
+        "qlinear_quantize_imatrix": ([vp, vp, i32, i32, i64, i64, vp, vp, vp, vp, vp], i32),
         "qlinear_dequantize": ([vp, vp, vp, i32, i32, i64, i64, vp, vp], i32),
         "qlinear_status_string": ([i32], ctypes.c_char_p),
         "qlinear_last_path": ([ctypes.c_char_p, sz], i32),
@@ -362,6 +363,22 @@ def qlinear_quantize_rtn(w, bits, group, N, K, packed_q, scales, biases, status=
         _dev_ptr(status, "status", (torch.int32,)) if status is not None else None,
         _stream_handle(stream))
     _check(st, "qlinear_quantize_rtn")
+
+
+def qlinear_quantize_imatrix(w, importance, bits, group, N, K, packed_q, scales, biases, status=None, stream=None):
+    """C ``qlinear_quantize_imatrix``: device importance-weighted fit + pack (importance fp32 [K])."""
+    torch = _torch()
+    u16 = _u16(torch)
+    lib = load_library()
+    st = lib.qlinear_quantize_imatrix(
+        _dev_ptr(w, "w", (torch.float32,), (N, K)),
+        _dev_ptr(importance, "importance", (torch.float32,), (K,)), bits, group, N, K,
+        _dev_ptr(packed_q, "packed_q", (torch.int32, torch.uint32), (N, K * bits // 32)),
+        _dev_ptr(scales, "scales", u16, (N, K // group)),
+        _dev_ptr(biases, "biases", u16, (N, K // group)),
+        _dev_ptr(status, "status", (torch.int32,)) if status is not None else None,
+        _stream_handle(stream))
+    _check(st, "qlinear_quantize_imatrix")
 
 
 def qlinear_dequantize(packed_q, scales, biases, bits, group, N, K, w_out, stream=None):

@@ -231,6 +231,24 @@ int qlinear_quantize_rtn(const float *w, int bits, int group, int64_t N, int64_t
                          uint32_t *packed_q, uint16_t *scales, uint16_t *biases,
                          int *status_dev, void *stream);
 
+/*
+ * Device importance-weighted fit ("imatrix"), same storage as
+ * qlinear_quantize_rtn. Per (row, 64-group) it minimises
+ * sum_j importance[k_j] * (w_j - W_hat_j)^2, the error weighting of the
+ * Ideogram-4-IQ4_M card (section on what "IQ4" means: importance is the
+ * per-input-channel mean squared activation E[x^2]); the min/max RTN fit is
+ * candidate 0 and is kept unless another candidate is strictly better, so
+ * the fit is never worse than RTN by that objective. The other candidates
+ * (weighted least-squares lines from 33 starting code sets) are this
+ * library's search, decided in fp32 with one rounding per operation.
+ * importance fp32 [K], finite and >= 0 (16-byte aligned), else
+ * *status_dev = QL_EINVAL; non-finite weights or f16 overflow of the RTN fit
+ * set QL_ERANGE, as for qlinear_quantize_rtn. *status_dev is never cleared.
+ */
+int qlinear_quantize_imatrix(const float *w, const float *importance, int bits, int group,
+                             int64_t N, int64_t K, uint32_t *packed_q, uint16_t *scales,
+                             uint16_t *biases, int *status_dev, void *stream);
+
 /* Device dequantize (check path): W_hat fp32 [N, K], one rounding per value,
  * bit-identical to fp32(scale)*q + fp32(bias). */
 int qlinear_dequantize(const uint32_t *packed_q, const void *scales, const void *biases,
