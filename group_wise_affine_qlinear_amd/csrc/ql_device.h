@@ -29,12 +29,18 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// (a & mask) | bits in one v_and_or_b32 (the compiler splits it into two ops
-// when both constants would need the scalar bus). Pure ALU, no memory access.
+// (a & mask) | bits in one v_and_or_b32. With both constants as literals the
+// compiler emits a v_and_b32 and a v_or_b32 (a VOP3 op takes no literal), so
+// the empty asm statements pin the mask to an SGPR and `bits` to a VGPR
+// (loop-invariant, hoisted) and leave the compiler free to select
+// v_and_or_b32 itself. The instruction must stay visible to the compiler: its
+// result often feeds an MFMA directly, and the wait states required between a
+// VALU write of a VGPR and an MFMA read of it are only inserted for
+// instructions the compiler knows are VALU, never for an asm statement.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
-  uint32_t r;
-  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(bits));
-  return r;
+  asm("" : "+s"(mask));
+  asm("" : "+v"(bits));
+  return (a & mask) | bits;
 }
 
 // 4-bit: word w holds codes c0..c7 (nibble i = code i). Returns four bf16
