@@ -43,6 +43,15 @@ section 2.8 table "SwiGLU MLP"; the notes print no formula). Reading taken:
 the standard gated form silu(x W_gate^T) * (x W_up^T) with silu(v) =
 v / (1 + e^-v), the gate and up weights stacked as rows [gate; up] of one
 projection. ``swiglu`` applies it to an exact product in float64.
+
+AdaLN gate (Ideogram 4 paper notes, section 2.1 pipeline: each block takes an
+AdaLN scale and gate from the timestep embedding; Ideogram-4-IQ4_M card,
+Conversion section: the modulation projection emits a per-layer scale and a
+tanh gate whose error multiplies the whole residual stream). Reading taken:
+the gate (already through tanh) multiplies a branch's output projection
+feature-wise, per sample, before it is added to the residual stream:
+out[m, n] = residual[m, n] + gate[m // rows_per_sample, n] * y[m, n].
+``gate_residual`` writes that out in float64.
 """
 from __future__ import annotations
 
@@ -57,6 +66,7 @@ __all__ = [
     "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
     "forward_rows", "error_metrics", "timed_forward",
     "fast_weights_f16", "fast_activations_f16", "forward_fast", "forward_fast_rows", "silu", "swiglu",
+    "gate_residual",
     "IMATRIX_DELTAS", "quantize_imatrix", "weighted_error",
 ]
 
@@ -430,6 +440,19 @@ def swiglu(y: np.ndarray, f: int) -> np.ndarray:
     y = np.asarray(y, dtype=np.float64)
     assert y.shape[1] == 2 * f
     return silu(y[:, :f]) * y[:, f:]
+
+
+def gate_residual(y: np.ndarray, residual: np.ndarray, gate: np.ndarray, gate_rows: int) -> np.ndarray:
+    """Gated residual update of a branch output y [M, N]: every output row m
+    belongs to sample m // gate_rows and adds that sample's gate row times y[m]
+    to residual[m]: out = residual + gate[m // gate_rows] * y, in float64."""
+    y = np.asarray(y, dtype=np.float64)
+    residual = np.asarray(residual, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    assert gate_rows >= 1 and y.shape == residual.shape and gate.shape[1] == y.shape[1]
+    sample = np.arange(y.shape[0]) // gate_rows
+    assert gate.shape[0] > (sample[-1] if len(sample) else -1)
+    return residual + gate[sample] * y
 
 
 def error_metrics(y: np.ndarray, y_ref: np.ndarray) -> dict:

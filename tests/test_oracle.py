@@ -538,6 +538,32 @@ def test_swiglu_fast_definition_error_budget():
     assert 1e-5 < e["relF"] < 5e-4, e
 
 
+# ---- AdaLN gated residual update ---------------------------------------------
+
+def test_gate_residual_hand_worked():
+    # 3 rows, 2 rows per sample: rows 0 and 1 take gate row 0, row 2 gate row 1
+    y = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    res = np.array([[10.0, 20.0], [30.0, 40.0], [50.0, 60.0]])
+    gate = np.array([[2.0, -1.0], [0.5, 3.0]])
+    got = oracle.gate_residual(y, res, gate, 2)
+    assert np.array_equal(got, np.array([[12.0, 18.0], [36.0, 36.0], [52.5, 78.0]]))
+
+
+def test_gate_residual_special_cases():
+    rng = np.random.default_rng(14)
+    y, res = rng.standard_normal((7, 5)), rng.standard_normal((7, 5))
+    # a closed gate leaves the residual stream untouched
+    assert np.array_equal(oracle.gate_residual(y, res, np.zeros((4, 5)), 2), res)
+    # an open gate on an empty stream is the branch output itself
+    assert np.array_equal(oracle.gate_residual(y, np.zeros_like(y), np.ones((1, 5)), 7), y)
+    # one sample: every row uses gate row 0, which scales columns
+    g = rng.standard_normal((1, 5))
+    np.testing.assert_allclose(oracle.gate_residual(y, res, g, 100), res + y @ np.diag(g[0]), rtol=1e-15)
+    # per-row gates (one row per sample) equal the elementwise product
+    g7 = rng.standard_normal((7, 5))
+    np.testing.assert_allclose(oracle.gate_residual(y, res, g7, 1), res + g7 * y, rtol=1e-15)
+
+
 # ---- importance-weighted fit (the pages' imatrix objective) ---------------
 
 def _outlier_importance(k, wid):
