@@ -168,6 +168,50 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     log(f"gate/up plain {ms_plain*1e3:.1f} us, fused SwiGLU {ms_glu*1e3:.1f} us")
     del tq, tsb, gq, gsb, x, x16, rs, y, yg
 
+    # attention-out projection at 1024x1024 (2 samples of 2304 tokens) with the
+    # AdaLN gated residual update: plain FAST GEMM, GEMM + a separate torch
+    # update of the residual stream, and the update fused into the GEMM store
+    M, K, N, L = 4608, 4608, 4608, 2304
+    w = torch.from_numpy(inputs.weights(N, K, 7)).cuda()
+    p = torch.empty((N, K // 8), dtype=torch.int32, device="cuda")
+    s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    ql.qlinear_quantize_rtn(w, 4, 64, N, K, p, s, b)
+    del w
+    tq, tsb = ql.qlinear_repack(p, s, b, 4, 64, N, K)
+    del p, s, b
+    x = torch.from_numpy(inputs.activations_bf16(M, K, 7).view("int16")).cuda()
+    x16, rs = ql.qlinear_fast_activations(x, M, K)
+    res = torch.from_numpy(inputs.residual_stream(M, N, 7)).cuda()
+    gate = torch.from_numpy(inputs.adaln_gate(M // L, N, 7)).cuda()
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def plain():
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, y, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs)
+
+    def unfused():
+        plain()
+        res.view(M // L, L, N).addcmul_(gate[:, None, :], y.view(M // L, L, N))
+
+    def fused():
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, res, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs,
+                              epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=gate, gate_rows=L)
+
+    ms_plain = time_calls(torch, plain, 20, 5)
+    ms_unf = time_calls(torch, unfused, 20, 5)
+    ms_fused = time_calls(torch, fused, 20, 5)
+    tf = 2 * M * N * K / 1e12
+    rows["attn_out_M4608_K4608_N4608_q4_fast"] = {
+        "path": "gemm3 (plain y)", "us": round(ms_plain * 1e3, 1), "TFLOP/s": round(tf / (ms_plain * 1e-3), 1)}
+    rows["attn_out_M4608_K4608_N4608_q4_gate_unfused"] = {
+        "path": "gemm3 + torch addcmul_ on the residual", "us": round(ms_unf * 1e3, 1),
+        "TFLOP/s": round(tf / (ms_unf * 1e-3), 1)}
+    rows["attn_out_M4608_K4608_N4608_q4_gate_fused"] = {
+        "path": ql.qlinear_last_path(), "us": round(ms_fused * 1e3, 1), "TFLOP/s": round(tf / (ms_fused * 1e-3), 1),
+        "note": "residual updated in place: out = residual + gate[sample] * y"}
+    log(f"attn-out plain {ms_plain*1e3:.1f} us, unfused gate {ms_unf*1e3:.1f} us, fused gate {ms_fused*1e3:.1f} us")
+    del tq, tsb, x, x16, rs, res, gate, y
+
     # 2048x2048 canvas: per-bit layer sweep, and one pass over the 34 blocks'
     # attention projections (QKV N=13824 then out N=4608) with 34 distinct
     # weight sets per width (every launch streams its weights)

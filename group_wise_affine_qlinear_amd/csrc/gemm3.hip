@@ -333,6 +333,34 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
   }
   const int64_t col0 = n0 + wave * kWN + r16;
   const bool full = (m0 + 16 * MI <= a.M) && (n0 + kBN <= a.N);
+  if (a.gate) {
+    // gated residual update: out = residual + gate[m / gate_rows] * y, one
+    // fused multiply-add in fp32; each element is read and written by the
+    // same lane, so residual may be out itself
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = row0 + mi * 16 + i;
+        if (!full && m >= a.M) continue;
+        const float rs = a.rowscale[m];
+        const float *grow = a.gate + (int64_t)((uint32_t)m / (uint32_t)a.gate_rows) * a.N;
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni) {
+          const int64_t n = col0 + ni * 16;
+          if (!full && n >= a.N) continue;
+          const float v = acc[mi][ni][i] * rs;
+          if constexpr (OUT_BF16) {
+            const float r = bf16_lo(reinterpret_cast<const uint16_t *>(a.residual)[m * a.N + n]);
+            reinterpret_cast<uint16_t *>(out)[m * a.N + n] = f32_to_bf16_rne3(__builtin_fmaf(grow[n], v, r));
+          } else {
+            const float r = reinterpret_cast<const float *>(a.residual)[m * a.N + n];
+            reinterpret_cast<float *>(out)[m * a.N + n] = __builtin_fmaf(grow[n], v, r);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll

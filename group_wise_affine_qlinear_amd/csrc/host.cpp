@@ -2,6 +2,7 @@
 // and host RTN quantizer. Kernels live in gemm.hip, skinny.hip and misc.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -263,12 +264,19 @@ int validate_forward(const ql_forward_args *a) {
   if (a->layout != QL_LAYOUT_CANONICAL && a->layout != QL_LAYOUT_TILED) return QL_EINVAL;
   if (a->mode != QL_MODE_AUTO && a->mode != QL_MODE_EXACT && a->mode != QL_MODE_FAST) return QL_EINVAL;
   if ((a->x16 == nullptr) != (a->rowscale == nullptr)) return QL_EINVAL;
-  if (a->epilogue != QL_EPI_NONE && a->epilogue != QL_EPI_SWIGLU) return QL_EINVAL;
-  if (a->epilogue == QL_EPI_SWIGLU) {
+  if (a->epilogue != QL_EPI_NONE && a->epilogue != QL_EPI_SWIGLU && a->epilogue != QL_EPI_GATE_RESIDUAL)
+    return QL_EINVAL;
+  if (a->epilogue != QL_EPI_NONE) {
     if (a->layout != QL_LAYOUT_TILED || a->mode == QL_MODE_EXACT || a->path == QL_PATH_SKINNY ||
         a->path == QL_PATH_SPLITK || a->split_k > 1)
       return QL_EUNSUPPORTED;
-    if (a->N % 32) return QL_EINVAL;
+  }
+  if (a->epilogue == QL_EPI_SWIGLU && a->N % 32) return QL_EINVAL;
+  if (a->epilogue == QL_EPI_GATE_RESIDUAL) {
+    if (a->gate_rows < 1) return QL_EINVAL;
+    if (a->M > 0 && a->N > 0 && (!a->residual || !a->gate)) return QL_EINVAL;
+    if (reinterpret_cast<uintptr_t>(a->gate) & 3u) return QL_EALIGN;
+    if (reinterpret_cast<uintptr_t>(a->residual) & (a->out_dtype == QL_OUT_BF16 ? 1u : 3u)) return QL_EALIGN;
   }
   if (a->M == 0 || a->N == 0) return QL_OK;
   if (!a->out) return QL_EINVAL;
@@ -338,16 +346,25 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     return QL_OK;
   }
   const bool glu = a->epilogue == QL_EPI_SWIGLU;
+  const bool gated = a->epilogue == QL_EPI_GATE_RESIDUAL;
   const int64_t n_out = glu ? a->N / 2 : a->N;
+  if (a->K == 0 && gated) {
+    // y = 0: the gated update leaves the residual stream as it is
+    set_last_path("copy_residual");
+    if (a->residual == a->out) return QL_OK;
+    const size_t bytes = (size_t)(a->M * a->N) * (a->out_dtype == QL_OUT_BF16 ? 2 : 4);
+    return hipMemcpyAsync(a->out, a->residual, bytes, hipMemcpyDeviceToDevice, stream) == hipSuccess ? QL_OK
+                                                                                                   : QL_EHIP;
+  }
   if (a->K == 0) {
     set_last_path("fill_zero");
     return ql::launch_fill_zero(a->out, a->M * n_out, a->out_dtype == QL_OUT_BF16, stream) == hipSuccess ? QL_OK
                                                                                                         : QL_EHIP;
   }
   Plan p;
-  // the fused gate/up epilogue runs on the FAST GEMM without a K split (it
-  // needs finished sums), at any M
-  st = glu ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, true, QL_MODE_FAST, &p)
+  // the fused epilogues run on the FAST GEMM without a K split (they need
+  // finished sums), at any M
+  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, true, QL_MODE_FAST, &p)
            : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, a->layout == QL_LAYOUT_TILED,
                        a->mode, &p);
   if (st != QL_OK) return st;
@@ -394,8 +411,13 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales),
                      split ? static_cast<void *>(partial) : a->out,
                      a->M, a->N, a->K, G, split ? 0 : out_bf16,
-                     p.g3.dp_tiles, p.g3.tail_tiles, p.g3.tail_mi, p.g3.splits, p.g3.grid_x, glu ? 1 : 0};
-    if (glu)
+                     p.g3.dp_tiles, p.g3.tail_tiles, p.g3.tail_mi, p.g3.splits, p.g3.grid_x, glu ? 1 : 0,
+                     gated ? a->residual : nullptr, gated ? a->gate : nullptr,
+                     gated ? (int)std::min<int64_t>(a->gate_rows, a->M) : 0};
+    if (gated)
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_gate_tiled", a->bits,
+                    p.g3.tail_tiles > 0 ? "_tail" : "");
+    else if (glu)
       std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_swiglu_tiled", a->bits,
                     p.g3.tail_tiles > 0 ? "_tail" : "");
     else if (split)

@@ -73,6 +73,9 @@ struct Gemm3Args {
   int splits;             // K ranges (grid y)
   int grid_x;
   int glu;                // 1: GLU-ordered weights, out = silu(gate) * up, [M, N/2]
+  const void *residual;   // non-null with gate: out = residual + gate[m / gate_rows] * y
+  const float *gate;      // fp32 [ceil(M / gate_rows), N]
+  int gate_rows;          // 1 .. M (callers clamp larger values to M)
 };
 struct Gemm3Plan {
   int64_t tiles;

@@ -13,6 +13,8 @@ Distributions: weights N(0, 0.02^2) in fp32; activations N(0, 1) in fp32 then
 rounded to bf16 (round-half-to-even). Optional structure: a seeded 1% of input
 channels scaled by 20 before the bf16 cast (outlier channels), or per-4096-slice
 standard deviations drawn from U[0.5, 4] (13 concatenated encoder layers).
+AdaLN-gated residual updates: residual stream N(0, 1) in fp32; per-sample gate
+values uniform in (-1, 1), the range of a tanh gate.
 Every tensor has its own stream: SeedSequence([0, workload_id, role]).
 """
 from __future__ import annotations
@@ -26,6 +28,8 @@ ROLE_SLICE = 4
 ROLE_CODES = 5
 ROLE_SCALE = 6
 ROLE_BIAS = 7
+ROLE_RESIDUAL = 8
+ROLE_GATE = 9
 
 # id, M, K, N, bits, x structure
 WORKLOADS = {
@@ -89,6 +93,16 @@ def random_f16_bits(n: int, g: int, lo: float, hi: float, workload_id: int = 0, 
     rng = rng_for(workload_id, role)
     v = rng.uniform(lo, hi, size=(n, g)).astype(np.float32)
     return v.astype(np.float16).view(np.uint16)
+
+
+def residual_stream(m: int, n: int, workload_id: int = 0) -> np.ndarray:
+    """Residual stream [m, n], N(0, 1) in fp32."""
+    return rng_for(workload_id, ROLE_RESIDUAL).standard_normal((m, n), dtype=np.float32)
+
+
+def adaln_gate(samples: int, n: int, workload_id: int = 0) -> np.ndarray:
+    """Per-sample gate rows [samples, n], uniform in (-1, 1) in fp32."""
+    return rng_for(workload_id, ROLE_GATE).uniform(-1.0, 1.0, size=(samples, n)).astype(np.float32)
 
 
 def workload_inputs(name: str, m: int | None = None):

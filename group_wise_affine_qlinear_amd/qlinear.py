@@ -22,7 +22,7 @@ QL_OUT_F32, QL_OUT_BF16 = 0, 1
 QL_PATH_AUTO, QL_PATH_SKINNY, QL_PATH_GEMM, QL_PATH_SPLITK = 0, 1, 2, 3
 QL_LAYOUT_CANONICAL, QL_LAYOUT_TILED = 0, 1
 QL_MODE_AUTO, QL_MODE_EXACT, QL_MODE_FAST = 0, 1, 2
-QL_EPI_NONE, QL_EPI_SWIGLU = 0, 1
+QL_EPI_NONE, QL_EPI_SWIGLU, QL_EPI_GATE_RESIDUAL = 0, 1, 2
 
 EXPORTED = (
     "qlinear_forward", "qlinear_forward_ex", "qlinear_workspace_bytes", "qlinear_packed_words",
@@ -65,6 +65,9 @@ class ql_forward_args(ctypes.Structure):
         ("x16", ctypes.c_void_p),
         ("rowscale", ctypes.c_void_p),
         ("epilogue", ctypes.c_int),
+        ("residual", ctypes.c_void_p),
+        ("gate", ctypes.c_void_p),
+        ("gate_rows", ctypes.c_int64),
     ]
 
 
@@ -183,7 +186,7 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
                        workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
                        xsum=None, layout=QL_LAYOUT_CANONICAL, mode=QL_MODE_AUTO, x16=None,
-                       rowscale=None, epilogue=QL_EPI_NONE):
+                       rowscale=None, epilogue=QL_EPI_NONE, residual=None, gate=None, gate_rows=0):
     """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout, numerics mode
     and forced path.
 
@@ -192,7 +195,9 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
     ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights);
     ``x16``/``rowscale`` are optional FAST-mode activations from ``qlinear_fast_activations``.
     ``epilogue=QL_EPI_SWIGLU`` takes GLU-ordered tiled weights (``qlinear_repack_glu``) and
-    writes ``out`` [M, N/2] = silu(gate) * up.
+    writes ``out`` [M, N/2] = silu(gate) * up. ``epilogue=QL_EPI_GATE_RESIDUAL`` writes
+    ``out`` = ``residual`` + ``gate``[m // ``gate_rows``] * y (``residual`` [M, N] of out's
+    dtype, may be ``out``; ``gate`` fp32 [ceil(M / gate_rows), N]).
     """
     torch = _torch()
     u16 = _u16(torch)
@@ -227,6 +232,12 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
         a.ld_xsum = xsum.shape[1]
         if xsum.dim() != 2 or xsum.shape[0] != K // group:
             raise ValueError("xsum must be [K/64, ld_xsum]")
+    if epilogue == QL_EPI_GATE_RESIDUAL:
+        a.gate_rows = gate_rows
+        if residual is not None:
+            a.residual = _dev_ptr(residual, "residual", (out.dtype,), (M, N))
+        if gate is not None and gate_rows >= 1:
+            a.gate = _dev_ptr(gate, "gate", (torch.float32,), (-(-M // gate_rows), N))
     if x16 is not None:
         a.x16 = _dev_ptr(x16, "x16", (torch.float16, torch.int16), (M, K))
         a.rowscale = _dev_ptr(rowscale, "rowscale", (torch.float32,), (M,))

@@ -98,8 +98,22 @@ typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
  *   Runs the FAST GEMM without a K split at any M; needs QL_LAYOUT_TILED,
  *   mode AUTO or FAST and path AUTO or GEMM, else QL_EUNSUPPORTED; N not a
  *   multiple of 32 is QL_EINVAL.
+ * GATE_RESIDUAL: the gated residual update of a DiT block branch. The call
+ *   writes out[m, n] = residual[m, n] + gate[m / gate_rows, n] * y[m, n]
+ *   (integer division: rows m of one sample share its gate row), computed
+ *   in fp32 as one fused multiply-add (bf16 out: one RNE rounding of it).
+ *   residual is [M, N] with the dtype of out and may be out itself (in-place
+ *   update of the residual stream); gate is fp32 [ceil(M / gate_rows), N],
+ *   the tanh gate as the modulation projection emits it; gate_rows >= 1.
+ *   This is the AdaLN gate of each DiT block, taken from the timestep
+ *   embedding and applied to the attention-out and MLP-down projections
+ *   (Ideogram 4 paper notes, section 2.1 pipeline; Ideogram-4-IQ4_M card,
+ *   Conversion section: a per-layer scale and a tanh gate). Same path rules
+ *   as SWIGLU (FAST GEMM, no K split, any M, QL_LAYOUT_TILED); a missing
+ *   residual or gate or gate_rows < 1 is QL_EINVAL. With K == 0 the call
+ *   copies residual to out.
  */
-typedef enum { QL_EPI_NONE = 0, QL_EPI_SWIGLU = 1 } ql_epilogue;
+typedef enum { QL_EPI_NONE = 0, QL_EPI_SWIGLU = 1, QL_EPI_GATE_RESIDUAL = 2 } ql_epilogue;
 
 typedef enum {
   QL_PATH_AUTO = 0,      /* dispatch table decides                            */
@@ -141,6 +155,9 @@ typedef struct ql_forward_args {
                                 for this x; both NULL = computed inside the
                                 call (both or neither must be given)        */
   int epilogue;              /* ql_epilogue; QL_EPI_NONE = plain y           */
+  const void *residual;      /* QL_EPI_GATE_RESIDUAL: [M, N], dtype of out   */
+  const float *gate;         /* QL_EPI_GATE_RESIDUAL: fp32 [ceil(M/gate_rows), N] */
+  int64_t gate_rows;         /* QL_EPI_GATE_RESIDUAL: output rows per gate row */
 } ql_forward_args;
 
 /*

@@ -1,0 +1,168 @@
+"""GPU tests of the fused AdaLN gated residual update on the FAST GEMM:
+``qlinear_forward_ex(..., epilogue=QL_EPI_GATE_RESIDUAL)`` writes
+out = residual + gate[m // gate_rows] * y.
+
+Bounds. The branch output y is the FAST GEMM's, so the kernel is compared with
+``oracle.gate_residual`` of the oracle's FAST definition. The error the GEMM
+carries is scaled by the gate, so it is measured against the gated branch
+g * y: max|out - ref| <= MAXABS_RMS_DESIGN * rms(g * y_ref) and
+||out - ref|| <= RELF_DESIGN * ||g * y_ref||, plus the fp32 rounding of the
+residual add (half an ulp of |out|, far below these bounds at these sizes)."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs
+from group_wise_affine_qlinear_amd import qlinear as ql
+
+from gpu_helpers import MAXABS_RMS_DESIGN, RELF_DESIGN, Case, dev, torch_or_skip
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_or_skip()
+    ql.load_library()
+    return t
+
+
+def gate_inputs(c, gate_rows, wid):
+    samples = -(-c.M // gate_rows)
+    return inputs.residual_stream(c.M, c.N, wid), inputs.adaln_gate(samples, c.N, wid)
+
+
+def run_gate(torch, c, gate_rows, res, gate, out_dtype="f32", inplace=False, **kw):
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack(p, s, b, c.bits, 64, c.N, c.K)
+    if out_dtype == "f32":
+        rd = dev(torch, res)
+    else:
+        rd = dev(torch, inputs.f32_to_bf16_bits(res)).view(torch.bfloat16)
+    if inplace:
+        out = rd
+    elif out_dtype == "f32":
+        out = torch.full((c.M, c.N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        out = torch.zeros((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+    ql.qlinear_forward_ex(x, tq, tsb, None, c.bits, c.M, c.N, c.K, out, layout=ql.QL_LAYOUT_TILED,
+                          epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=rd, gate=dev(torch, gate),
+                          gate_rows=gate_rows, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(out, c, res, gate, gate_rows, rows=None, cols=None):
+    out = np.asarray(out, dtype=np.float64)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    rows = np.arange(c.M) if rows is None else rows
+    cols = np.arange(c.N) if cols is None else cols
+    y = oracle.forward_fast_rows(c.x, c.packed, c.s16, c.b16, c.bits, c.K, rows, cols)
+    g = np.asarray(gate, dtype=np.float64)[rows // gate_rows][:, cols]   # each sampled row's gate row
+    ref = oracle.gate_residual(y, np.asarray(res, dtype=np.float64)[rows][:, cols], g, 1)
+    gy = g * y
+    d = out - ref
+    rms = float(np.sqrt(np.mean(gy * gy)))
+    assert float(np.max(np.abs(d))) <= MAXABS_RMS_DESIGN * rms, float(np.max(np.abs(d))) / rms
+    assert float(np.linalg.norm(d)) <= RELF_DESIGN * float(np.linalg.norm(gy)), \
+        float(np.linalg.norm(d) / np.linalg.norm(gy))
+
+
+GATE_SHAPES = [(520, 800, 320, 260), (300, 2080, 448, 7), (64, 256, 128, 64), (5, 512, 640, 2),
+               (17, 1056, 256, 1000), (1, 384, 192, 1)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("shape", GATE_SHAPES)
+def test_gate_residual_parity(torch, shape, bits):
+    M, N, K, gate_rows = shape
+    c = Case(M, N, K, bits, wid=560 + bits, x_structure="outlier")
+    res, gate = gate_inputs(c, gate_rows, 560 + bits)
+    out = run_gate(torch, c, gate_rows, res, gate).cpu().numpy()
+    assert "_gate" in ql.qlinear_last_path(), ql.qlinear_last_path()
+    check(out, c, res, gate, gate_rows)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gate_residual_in_place(torch, bits):
+    c = Case(300, 640, 384, bits, wid=570 + bits)
+    res, gate = gate_inputs(c, 100, 570 + bits)
+    out = run_gate(torch, c, 100, res, gate, inplace=True).cpu().numpy()
+    check(out, c, res, gate, 100)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gate_residual_bf16_is_rounded_fp32_update(torch, bits):
+    """bf16 out with a bf16 residual = RNE of the fp32 update of that residual."""
+    c = Case(300, 640, 384, bits, wid=575 + bits)
+    res, gate = gate_inputs(c, 64, 575 + bits)
+    res_b = oracle.bf16_bits_to_f64(inputs.f32_to_bf16_bits(res)).astype(np.float32)
+    y32 = run_gate(torch, c, 64, res_b, gate).cpu().numpy()
+    yb = run_gate(torch, c, 64, res, gate, out_dtype="bf16")
+    got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, inputs.f32_to_bf16_bits(y32))
+
+
+# (slots, shape): row pieces of the last tiles, gate rows not aligned to them
+@pytest.mark.parametrize("slots,shape", [(8, (256, 2304, 320)), (10, (520, 1024, 448)), (7, (700, 768, 320))])
+def test_gate_residual_with_tail_pieces(torch, monkeypatch, slots, shape):
+    M, N, K = shape
+    monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
+    c = Case(M, N, K, 4, wid=580)
+    res, gate = gate_inputs(c, 37, 580)
+    out = run_gate(torch, c, 37, res, gate).cpu().numpy()
+    assert "_tail" in ql.qlinear_last_path(), ql.qlinear_last_path()
+    check(out, c, res, gate, 37)
+
+
+def test_gate_residual_k0_copies_residual(torch):
+    c = Case(16, 64, 64, 4, wid=585)
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack(p, s, b, 4, 64, 64, 64)
+    res = dev(torch, inputs.residual_stream(16, 64, 585))
+    gate = dev(torch, inputs.adaln_gate(2, 64, 585))
+    out = torch.full((16, 64), float("nan"), dtype=torch.float32, device="cuda")
+    ql.qlinear_forward_ex(x[:, :0].contiguous(), tq[:0], tsb[:0], None, 4, 16, 64, 0, out,
+                          layout=ql.QL_LAYOUT_TILED, epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=gate,
+                          gate_rows=8)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(out, res))
+
+
+def test_gate_residual_rejects_bad_requests(torch):
+    c = Case(64, 256, 256, 4, wid=590)
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack(p, s, b, 4, 64, 256, 256)
+    out = torch.empty((64, 256), dtype=torch.float32, device="cuda")
+    res = torch.zeros_like(out)
+    gate = torch.zeros((1, 256), dtype=torch.float32, device="cuda")
+    kw = dict(epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=gate, gate_rows=64)
+    with pytest.raises(ql.QLinearError):   # canonical layout
+        ql.qlinear_forward_ex(x, p, s, b, 4, 64, 256, 256, out, **kw)
+    with pytest.raises(ql.QLinearError):   # EXACT numerics
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
+                              mode=ql.QL_MODE_EXACT, **kw)
+    with pytest.raises(ql.QLinearError):   # K split
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
+                              path=ql.QL_PATH_SPLITK, **kw)
+    with pytest.raises(ql.QLinearError):   # no gate
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
+                              epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate_rows=64)
+    with pytest.raises(ql.QLinearError):   # gate_rows < 1
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
+                              epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate_rows=0)
+
+
+def test_gate_residual_full_size_attention_out_sampled(torch):
+    """The attention-out projection at 1024x1024 (M=4608, K=N=4608, 4-bit) over
+    a batch of 2 samples of 2304 rows, on sampled outputs."""
+    M, N, K, gate_rows = 4608, 4608, 4608, 2304
+    c = Case(M, N, K, 4, wid=6)
+    res, gate = gate_inputs(c, gate_rows, 595)
+    out = run_gate(torch, c, gate_rows, res, gate)
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(596)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2303, 2304, M - 1], rng.integers(0, M, 60)]))
+    cols = np.unique(np.concatenate([[0, 15, 16, 255, 256, N - 1], rng.integers(0, N, 60)]))
+    blk = out.index_select(0, torch.from_numpy(rows).cuda()).index_select(1, torch.from_numpy(cols).cuda())
+    check(blk.cpu().numpy(), c, res, gate, gate_rows, rows, cols)
