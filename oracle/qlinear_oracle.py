@@ -16,9 +16,14 @@ What it computes (sources are the pages' titles and sections):
 * Fit. Round-to-nearest from the group's min/max ("candidate 0", the card's
   section on what "IQ4" means; the OrbitQuant W2A4 card's quantization manifest
   names the same int4 RTN group-64 policy).
-* Packing. The pages say only "packed". Reading taken: codes are stored
-  little-endian along K in uint32 words, 32/bits codes per word, code k in bits
-  [bits*(k % (32/bits)), +bits) of word k // (32/bits).
+* Packing. The pages say only "packed". Reading taken: each row's codes form
+  one little-endian bit stream along K, code k in stream bits
+  [bits*k, bits*k + bits), stream bit i being bit i % 32 of uint32 word
+  i // 32. For 2, 4 and 8 bits this puts 32/bits whole codes in each word
+  (code k in bits [bits*(k % (32/bits)), +bits) of word k // (32/bits)); for
+  3 bits (the 3-bit DiT bulk of the IQ4_M card's previous pack, section
+  "Against the pack this replaces"; its layout is not given) a code may
+  straddle two words, and every 64-wide group fills exactly 6 words.
 * Product. y = x @ W_hat^T, x given as bf16, accumulated in float64.
 
 Readings where the pages are silent (each also listed in the design notes):
@@ -61,7 +66,8 @@ import time
 import numpy as np
 
 __all__ = [
-    "GROUP", "SUPPORTED_BITS", "codes_per_word", "bits_per_weight", "storage_bytes",
+    "GROUP", "SUPPORTED_BITS", "check_bits", "codes_per_word", "words_per_row", "bits_per_weight",
+    "storage_bytes",
     "f16_bits_to_f32", "f32_to_f16_bits", "bf16_bits_to_f64",
     "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
     "forward_rows", "error_metrics", "timed_forward",
@@ -71,13 +77,28 @@ __all__ = [
 ]
 
 GROUP = 64
-SUPPORTED_BITS = (2, 4, 8)
+SUPPORTED_BITS = (2, 3, 4, 8)
+
+
+def check_bits(bits: int) -> None:
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"bits must be one of {SUPPORTED_BITS}, got {bits}")
 
 
 def codes_per_word(bits: int) -> int:
-    if bits not in SUPPORTED_BITS:
-        raise ValueError(f"bits must be one of {SUPPORTED_BITS}, got {bits}")
+    """Whole codes per uint32 word (widths that divide 32 only)."""
+    check_bits(bits)
+    if 32 % bits:
+        raise ValueError(f"{bits}-bit codes do not tile a 32-bit word")
     return 32 // bits
+
+
+def words_per_row(bits: int, k: int) -> int:
+    """uint32 words of one row's packed codes: k * bits / 32 (k * bits a multiple of 32)."""
+    check_bits(bits)
+    if (k * bits) % 32:
+        raise ValueError("K * bits must be a multiple of 32")
+    return k * bits // 32
 
 
 def bits_per_weight(bits: int, group: int = GROUP) -> float:
@@ -91,7 +112,7 @@ def bits_per_weight(bits: int, group: int = GROUP) -> float:
 
 def storage_bytes(bits: int, n: int, k: int, group: int = GROUP) -> int:
     """Bytes of packed codes + f16 scales + f16 biases for an [n, k] weight."""
-    words = n * k // codes_per_word(bits)
+    words = n * words_per_row(bits, k)
     groups = n * (k // group)
     return 4 * words + 2 * groups + 2 * groups
 
@@ -141,7 +162,7 @@ def quantize_rtn(w: np.ndarray, bits: int, group: int = GROUP):
     if not np.all(np.isfinite(w)):
         raise ValueError("non-finite weight")
     qmax = np.float32(2 ** bits - 1)
-    codes_per_word(bits)  # validates bits
+    check_bits(bits)
     g = k // group
     wg = w.reshape(n, g, group)
     mn = wg.min(axis=2)
@@ -305,35 +326,39 @@ def weighted_error(w, importance, q, s16, b16, group: int = GROUP) -> np.ndarray
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
     """q uint8 [N, K] (values < 2**bits) -> uint32 [N, K*bits/32].
 
-    Code k sits in bits [bits*(k % c), bits*(k % c) + bits) of word k // c,
-    c = 32 // bits (little-endian along K).
+    Bit j of code k goes to bit p % 32 of word p // 32, p = bits*k + j (one
+    little-endian bit stream per row). Written bit by bit: for a fixed bit j
+    and a fixed k % 32 the codes k land in distinct words, so each step is a
+    plain vectorised OR.
     """
     q = np.asarray(q)
-    c = codes_per_word(bits)
     n, k = q.shape
-    if k % c:
-        raise ValueError("K must be a multiple of codes per word")
+    nw = words_per_row(bits, k)
     if q.size and int(q.max()) >= (1 << bits):
         raise ValueError("code out of range")
-    q32 = q.astype(np.uint32).reshape(n, k // c, c)
-    words = np.zeros((n, k // c), dtype=np.uint32)
-    for j in range(c):
-        words |= q32[:, :, j] << np.uint32(bits * j)
+    q32 = q.astype(np.uint32)
+    words = np.zeros((n, nw), dtype=np.uint32)
+    for j in range(bits):
+        for r in range(min(32, k)):
+            ks = np.arange(r, k, 32)
+            p = bits * ks + j
+            words[:, p // 32] |= ((q32[:, ks] >> np.uint32(j)) & np.uint32(1)) << (p % 32).astype(np.uint32)
     return words
 
 
 def unpack(words: np.ndarray, bits: int, k: int) -> np.ndarray:
     """Inverse of ``pack``: uint32 [N, K*bits/32] -> uint8 [N, K]."""
-    c = codes_per_word(bits)
     words = np.asarray(words, dtype=np.uint32)
     n = words.shape[0]
-    if words.shape[1] * c != k:
+    if words.shape[1] != words_per_row(bits, k):
         raise ValueError("word count does not match K")
-    mask = np.uint32((1 << bits) - 1)
-    out = np.empty((n, k // c, c), dtype=np.uint8)
-    for j in range(c):
-        out[:, :, j] = ((words >> np.uint32(bits * j)) & mask).astype(np.uint8)
-    return out.reshape(n, k)
+    q = np.zeros((n, k), dtype=np.uint32)
+    for j in range(bits):
+        for r in range(min(32, k)):
+            ks = np.arange(r, k, 32)
+            p = bits * ks + j
+            q[:, ks] |= ((words[:, p // 32] >> (p % 32).astype(np.uint32)) & np.uint32(1)) << np.uint32(j)
+    return q.astype(np.uint8)
 
 
 # ---------------------------------------------------------------- dequantize

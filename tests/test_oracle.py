@@ -74,10 +74,10 @@ def test_bpw_closed_form_matches_page_overhead():
     fig = _golden("page_figures.json")
     over = fig["group_overhead_bits"]["value"]
     assert fig["group_overhead_bits"]["group"] == oracle.GROUP == fig["group_size"]["value"]
-    for b in (2, 4, 8):
+    for b in (2, 3, 4, 8):
         assert oracle.bits_per_weight(b) == b + over
     for (n, k) in [(256, 512), (13824, 4608), (4608, 53248), (3, 64)]:
-        for b in (2, 4, 8):
+        for b in (2, 3, 4, 8):
             assert oracle.storage_bytes(b, n, k) * 8 == n * k * (b + over)
 
 
@@ -105,7 +105,7 @@ def test_pack_hand_words():
         assert np.array_equal(oracle.unpack(packed, bits, codes.shape[1]), codes)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_pack_unpack_round_trip(bits):
     n, k = 7, 256
     q = inputs.random_codes(n, k, bits, workload_id=99)
@@ -114,10 +114,42 @@ def test_pack_unpack_round_trip(bits):
     for pat in (np.zeros((n, k)), np.full((n, k), qmax), np.tile([0, qmax], (n, k // 2))):
         pat = pat.astype(np.uint8)
         assert np.array_equal(oracle.unpack(oracle.pack(pat, bits), bits, k), pat)
-    all_q = oracle.pack(np.full((1, 32 // bits), qmax, dtype=np.uint8), bits)
-    assert int(all_q[0, 0]) == 0xFFFFFFFF
+    all_q = oracle.pack(np.full((1, 32), qmax, dtype=np.uint8), bits)
+    assert all_q.shape == (1, bits) and np.all(all_q == 0xFFFFFFFF)
     words = np.random.default_rng(5).integers(0, 2**32, size=(n, k * bits // 32), dtype=np.uint64).astype(np.uint32)
     assert np.array_equal(oracle.pack(oracle.unpack(words, bits, k), bits), words)
+
+
+def test_pack_3bit_hand_words():
+    """3-bit bit stream, hand-worked: code k at stream bits 3k .. 3k+2; codes 10
+    (bits 30-32) and 21 (bits 63-65) straddle words."""
+    def row(**codes):
+        q = np.zeros((1, 32), dtype=np.uint8)
+        for k, v in codes.items():
+            q[0, int(k[1:])] = v
+        return q
+    cases = [
+        (row(c10=7), [0xC0000000, 0x00000001, 0x00000000]),
+        (row(c21=5), [0x00000000, 0x80000000, 0x00000002]),
+        (row(c0=5, c31=6), [0x00000005, 0x00000000, 0xC0000000]),
+        (row(c1=1, c11=3, c22=4), [0x00000008, 0x00000003 << 1, 0x00000004 << 2]),
+    ]
+    for q, words in cases:
+        got = oracle.pack(q, 3)
+        assert got.tolist() == [words], (q, [hex(w) for w in got[0]])
+        assert np.array_equal(oracle.unpack(got, 3, 32), q)
+
+
+def test_pack_stream_matches_big_integer():
+    """Every width against an independent construction: the row's codes summed
+    into one Python integer at bit offsets bits*k, split into 32-bit words."""
+    for bits in (2, 3, 4, 8):
+        q = inputs.random_codes(5, 192, bits, workload_id=98)
+        got = oracle.pack(q, bits)
+        for n in range(q.shape[0]):
+            v = sum(int(c) << (bits * k) for k, c in enumerate(q[n]))
+            words = [(v >> (32 * i)) & 0xFFFFFFFF for i in range(192 * bits // 32)]
+            assert got[n].tolist() == words
 
 
 def test_pack_rejects_out_of_range_code():
@@ -212,7 +244,7 @@ def test_rtn_rejects_non_finite_and_overflow():
         oracle.quantize_rtn(w, 4)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_rtn_scale_bias_are_rounded_min_max(bits):
     """s and b equal exact-RNE f16 of (max-min)/Q (fp32 ops) and of min, group by group."""
     w = inputs.weights(6, 256, workload_id=21)
@@ -228,7 +260,7 @@ def test_rtn_scale_bias_are_rounded_min_max(bits):
     assert q.max() <= qmax
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_rtn_brute_force_nearest_code(bits):
     """q is the nearest grid point among all 2**bits codes (exact fp64 distances)."""
     w = inputs.weights(16, 512, workload_id=22)
@@ -253,7 +285,7 @@ def test_rtn_brute_force_nearest_code(bits):
 
 # ----------------------------------------------------------------- dequantize
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_dequant_equals_exact_then_round(bits):
     """fp32 mul+add equals the exactly computed s*q + b rounded once to fp32."""
     n, k = 32, 256
@@ -571,7 +603,7 @@ def _outlier_importance(k, wid):
     return (x * x).mean(axis=0).astype(np.float32)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_imatrix_never_worse_than_rtn(bits):
     # candidate 0 is the min/max RTN fit, so the objective never increases
     w = inputs.weights(96, 512, 60 + bits)
