@@ -94,6 +94,23 @@ template <> struct LaneCodes<2> {
   }
 };
 
+// 3-bit block: the 2-bit block of the low bits (word h%2 of half h/2, as
+// above), then the high-bit plane [h'2][col32][1 word] at byte 512 (code 2P
+// of the half at bit P, code 2P+1 at bit 16+P). w[0] is the low-bit word,
+// w[1] the high-bit word of half h/2 after prep(): the lane's pairs
+// 8(h%2) .. +7 moved to bits 2.. and 18.. (prep runs once per group, when
+// the codes have arrived).
+template <> struct LaneCodes<3> {
+  static constexpr int kWords = 2;
+  __device__ static constexpr uint32_t offset(int col, int h) { return (h >> 1) * 256 + col * 8 + (h & 1) * 4; }
+  __device__ static constexpr uint32_t hi_offset(int col, int h) { return 512 + (h >> 1) * 128 + col * 4; }
+  __device__ static uint32_t prep(uint32_t hw, int h) { return (hw >> (8 * (h & 1))) << 2; }
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    const uint32_t lo = and_or(w[0] >> (8 * c + 2 * p), 0x00030003u, 0x64006400u);
+    return dq_pair(and_or(w[1] >> (4 * c + p), 0x00040004u, lo), s2, b2);
+  }
+};
+
 // Chunk swizzle of an x stage: logical 16-byte chunk c of row r sits at
 // position c ^ xswz(r). With this function the 64 lanes of an MFMA fragment
 // read (16 rows, four k-blocks) spread over the banks best among the
@@ -154,6 +171,8 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, strip * G * BB, (int64_t)G * BB);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.sb, strip * G * 128, (int64_t)G * 128);
   const uint32_t wo = LC::offset(r16, h), so = (uint32_t)(r16 * 4);
+  uint32_t who = 0;  // 3-bit: the lane's high-bit word
+  if constexpr (BITS == 3) who = LC::hi_offset(r16, h);
   constexpr uint32_t kColStep = LC::offset(16, 0) - LC::offset(0, 0);  // bytes per 16 columns
 
   auto load_codes = [&](uint32_t (&w)[kNI][LC::kWords], uint32_t (&sb)[kNI], int gv) {
@@ -168,6 +187,9 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) w[ni][t] = v[t];
+      } else if constexpr (BITS == 3) {
+        w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
+        w[ni][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, who + ni * 64u, (uint32_t)g * BB, 0);
       } else {
         w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
       }
@@ -211,6 +233,12 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
     const uint32_t v = valid ? sq[0][ni] : 0u;
     const h2 s2 = __builtin_bit_cast(h2, (v & 0xFFFFu) * 0x10001u);
     const h2 b2 = __builtin_bit_cast(h2, (v >> 16) * 0x10001u);
+    if constexpr (BITS == 3) {
+      // the first piece of a column block (i = 8 ni) runs before its other
+      // pieces: in both placements below pieces run in increasing i within a
+      // column block
+      if (c == 0 && p == 0) cq[0][ni][1] = LC::prep(cq[0][ni][1], h);
+    }
     uint32_t r = LC::pair(cq[0][ni], c, p, s2, b2);
     asm volatile("" : "+v"(r));  // keeps the piece where it is placed, between MFMAs
     dst[ni][c][p] = r;
@@ -581,6 +609,7 @@ hipError_t launch_gemm3(int bits, const Gemm3Args &a, hipStream_t stream) {
   if (bits == 4) return launch3_bits<4>(a, stream);
   if (bits == 8) return launch3_bits<8>(a, stream);
   if (bits == 2) return launch3_bits<2>(a, stream);
+  if (bits == 3) return launch3_bits<3>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -26,7 +26,7 @@ void set_last_path(const char *s) {
   std::snprintf(g_last_path, sizeof(g_last_path), "%s", s);
 }
 
-bool bits_ok(int bits) { return bits == 2 || bits == 4 || bits == 8; }
+bool bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -174,6 +174,8 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
     if (envp > 0) path = envp;
   }
   if (path == QL_PATH_AUTO) path = (M <= kMaxSkinnyM) ? QL_PATH_SKINNY : QL_PATH_GEMM;
+  // 3-bit codes run on tiled weights only: the skinny kernel and the FAST GEMM
+  if (bits == 3 && !tiled) return QL_EUNSUPPORTED;
   if (path == QL_PATH_SKINNY) {
     if (M > kMaxSkinnyM || mode == QL_MODE_FAST) return QL_EUNSUPPORTED;
     p->path = QL_PATH_SKINNY;
@@ -210,6 +212,7 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
     return QL_OK;
   }
   if (forced && forced->gen == 3) return QL_EUNSUPPORTED;
+  if (bits == 3) return QL_EUNSUPPORTED;  // no exact-mode GEMM for 3-bit codes
   int splits = 0;
   if (tile <= 0) {
     for (const TableEntry &e : kTable) {
@@ -528,21 +531,26 @@ QL_API int qlinear_forward(const void *x, const uint32_t *packed_q, const void *
   return qlinear_forward_ex(&a, nullptr);
 }
 
+// Code k of a row sits in bits [bits*k, bits*k + bits) of the row's
+// little-endian bit stream (bit i of the stream = bit i % 32 of word i / 32);
+// 3-bit codes may straddle two words.
 QL_API int qlinear_pack_host(const uint8_t *q, int bits, int64_t N, int64_t K, uint32_t *packed) {
   if (!bits_ok(bits)) return QL_EUNSUPPORTED;
-  const int cpw = 32 / bits;
-  if (N < 0 || K < 0 || K % cpw) return QL_EINVAL;
+  if (N < 0 || K < 0 || (K * bits) % 32) return QL_EINVAL;
   if (N * K > 0 && (!q || !packed)) return QL_EINVAL;
   const uint32_t lim = 1u << bits;
   for (int64_t i = 0; i < N * K; ++i)
     if (q[i] >= lim) return QL_ERANGE;
-  const int64_t wr = K / cpw;
+  const int64_t wr = K * bits / 32;
   for (int64_t n = 0; n < N; ++n) {
-    for (int64_t j = 0; j < wr; ++j) {
-      uint32_t word = 0;
-      const uint8_t *src = q + n * K + j * cpw;
-      for (int i = 0; i < cpw; ++i) word |= (uint32_t)src[i] << (bits * i);
-      packed[n * wr + j] = word;
+    uint32_t *row = packed + n * wr;
+    for (int64_t j = 0; j < wr; ++j) row[j] = 0;
+    for (int64_t k = 0; k < K; ++k) {
+      const uint32_t v = q[n * K + k];
+      const int64_t p = k * bits;
+      const int sh = (int)(p % 32);
+      row[p / 32] |= v << sh;
+      if (sh + bits > 32) row[p / 32 + 1] |= v >> (32 - sh);
     }
   }
   return QL_OK;
@@ -550,16 +558,20 @@ QL_API int qlinear_pack_host(const uint8_t *q, int bits, int64_t N, int64_t K, u
 
 QL_API int qlinear_unpack_host(const uint32_t *packed, int bits, int64_t N, int64_t K, uint8_t *q) {
   if (!bits_ok(bits)) return QL_EUNSUPPORTED;
-  const int cpw = 32 / bits;
-  if (N < 0 || K < 0 || K % cpw) return QL_EINVAL;
+  if (N < 0 || K < 0 || (K * bits) % 32) return QL_EINVAL;
   if (N * K > 0 && (!q || !packed)) return QL_EINVAL;
   const uint32_t mask = (1u << bits) - 1u;
-  const int64_t wr = K / cpw;
-  for (int64_t n = 0; n < N; ++n)
-    for (int64_t j = 0; j < wr; ++j) {
-      const uint32_t word = packed[n * wr + j];
-      for (int i = 0; i < cpw; ++i) q[n * K + j * cpw + i] = (uint8_t)((word >> (bits * i)) & mask);
+  const int64_t wr = K * bits / 32;
+  for (int64_t n = 0; n < N; ++n) {
+    const uint32_t *row = packed + n * wr;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t p = k * bits;
+      const int sh = (int)(p % 32);
+      uint32_t v = row[p / 32] >> sh;
+      if (sh + bits > 32) v |= row[p / 32 + 1] << (32 - sh);
+      q[n * K + k] = (uint8_t)(v & mask);
     }
+  }
   return QL_OK;
 }
 

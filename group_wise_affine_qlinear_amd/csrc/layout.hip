@@ -9,6 +9,9 @@
 //   4-bit: 1 KB   = [h 2][col 32][4 words]   words t: codes 32h+8t .. +7
 //   8-bit: 2 KB   = [part 2][h 2][col 32][4 words]  part p: codes 32h+16p .. +15
 //   2-bit: 512 B  = [h 2][col 32][2 words]   words t: codes 32h+16t .. +15
+//   3-bit: 768 B  = the 2-bit block of the codes' low two bits, then
+//                   [h 2][col 32][1 word] of their high bits: code 32h+2P at
+//                   bit P and code 32h+2P+1 at bit 16+P (P = 0..15)
 //
 // so lane l = 32h + col of a wave reads its 16 (or 8) bytes at l*16 and one
 // load instruction covers whole cache lines. Blocks are ordered [strip][group].
@@ -97,6 +100,60 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32
     if (BITS == 8) return ((j >> 2) & 1) * 256 + (j >> 3) * 128 + col * 4 + (j & 3);  // h = j/8, part = (j/4)%2
     return (j >> 1) * 64 + col * 2 + (j & 1);                            // 2-bit: h = j/2, t = j%2
   };
+  if constexpr (BITS == 3) {
+    // low-bit plane words at [h][col][t] (2-bit block), high-bit plane at 128 + [h][col]
+    if (TO_TILED) {
+      uint32_t cw[WPG];
+      const uint32_t *crow = src + n * (K * 3 / 32) + g * WPG;
+#pragma unroll
+      for (int j = 0; j < WPG; ++j) cw[j] = real ? crow[j] : 0u;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t hi = 0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint32_t lo = 0;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            const uint32_t c0 = stream_code<3>(cw, 32 * hh + 16 * t + 2 * p);
+            const uint32_t c1 = stream_code<3>(cw, 32 * hh + 16 * t + 2 * p + 1);
+            lo |= ((c0 & 3u) << (2 * p)) | ((c1 & 3u) << (16 + 2 * p));
+            hi |= ((c0 >> 2) << (8 * t + p)) | ((c1 >> 2) << (16 + 8 * t + p));
+          }
+          blk[hh * 64 + col * 2 + t] = lo;
+        }
+        blk[128 + hh * 32 + col] = hi;
+      }
+      sb[(strip * G + g) * 32 + col] = real ? ((uint32_t)s[n * G + g] | ((uint32_t)b[n * G + g] << 16)) : 0u;
+    } else {
+      if (!real) return;
+      uint32_t cw[WPG];
+#pragma unroll
+      for (int j = 0; j < WPG; ++j) cw[j] = 0u;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t hi = blk[128 + hh * 32 + col];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t lo = blk[hh * 64 + col * 2 + t];
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            const uint32_t c0 = ((lo >> (2 * p)) & 3u) | (((hi >> (8 * t + p)) & 1u) << 2);
+            const uint32_t c1 = ((lo >> (16 + 2 * p)) & 3u) | (((hi >> (16 + 8 * t + p)) & 1u) << 2);
+            stream_put<3>(cw, 32 * hh + 16 * t + 2 * p, c0);
+            stream_put<3>(cw, 32 * hh + 16 * t + 2 * p + 1, c1);
+          }
+        }
+      }
+      uint32_t *crow = dst + n * (K * 3 / 32) + g * WPG;
+#pragma unroll
+      for (int j = 0; j < WPG; ++j) crow[j] = cw[j];
+      const uint32_t v = sb[(strip * G + g) * 32 + col];
+      s_out[n * G + g] = (uint16_t)(v & 0xFFFFu);
+      b_out[n * G + g] = (uint16_t)(v >> 16);
+    }
+    return;
+  }
   if (TO_TILED) {
     const uint32_t *crow = src + n * (K * BITS / 32) + g * WPG;
 #pragma unroll
@@ -141,6 +198,7 @@ hipError_t launch_repack(int bits, const uint32_t *canon, const uint16_t *s, con
   if (bits == 4) return repack_bits<4, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
   if (bits == 8) return repack_bits<8, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
   if (bits == 2) return repack_bits<2, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
+  if (bits == 3) return repack_bits<3, true>(canon, tiled, s, b, sb, nullptr, nullptr, N, K, glu_f, stream);
   return hipErrorInvalidValue;
 }
 
@@ -150,6 +208,7 @@ hipError_t launch_unrepack(int bits, const uint32_t *tiled, const uint32_t *sb, 
   if (bits == 4) return repack_bits<4, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
   if (bits == 8) return repack_bits<8, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
   if (bits == 2) return repack_bits<2, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
+  if (bits == 3) return repack_bits<3, false>(tiled, canon, nullptr, nullptr, sbm, s, b, N, K, glu_f, stream);
   return hipErrorInvalidValue;
 }
 

@@ -14,29 +14,31 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
 __device__ __forceinline__ bool f16_finite(uint16_t h) { return (h & 0x7C00u) != 0x7C00u; }
 
 // W_hat[n, k] = fp32(s) * q + fp32(b); s*q is exact in fp32 so the fused form
-// rounds exactly once, like the plain multiply-then-add definition.
+// rounds exactly once, like the plain multiply-then-add definition. One
+// thread per (row, group): the group's 2*BITS words of the row's code stream.
 template <int BITS>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *w, const uint16_t *s,
                                                       const uint16_t *b, int64_t N, int64_t K,
                                                       float *out) {
-  constexpr int CPW = 32 / BITS;
-  constexpr uint32_t Q = (1u << BITS) - 1u;
-  const int64_t wr = K / CPW;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= N * wr) return;
-  const int64_t n = idx / wr, wi = idx % wr;
-  const int64_t k0 = wi * CPW;
+  constexpr int WPG = 2 * BITS;
   const int64_t G = K / 64;
-  const int64_t g = k0 / 64;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * G) return;
+  const int64_t n = idx / G, g = idx % G;
   const float sf = f16_to_f32(s[n * G + g]);
   const float bf = f16_to_f32(b[n * G + g]);
-  const uint32_t word = w[idx];
-  float v[CPW];
+  uint32_t word[WPG];
+  const uint32_t *src = w + n * (K * BITS / 32) + g * WPG;
 #pragma unroll
-  for (int j = 0; j < CPW; ++j) v[j] = __builtin_fmaf(sf, (float)((word >> (BITS * j)) & Q), bf);
-  float *o = out + n * K + k0;
+  for (int j = 0; j < WPG; ++j) word[j] = src[j];
+  float *o = out + n * K + g * 64;
 #pragma unroll
-  for (int j = 0; j < CPW; j += 4) *reinterpret_cast<f32x4 *>(o + j) = f32x4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+  for (int k = 0; k < 64; k += 4) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(sf, (float)stream_code<BITS>(word, k + e), bf);
+    *reinterpret_cast<f32x4 *>(o + k) = v;
+  }
 }
 
 // One thread per (row, group): min/max, f16 scale and bias, codes from the
@@ -46,7 +48,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *w, int64_t N
                                                        uint32_t *packed, uint16_t *s, uint16_t *b,
                                                        int *status) {
 #pragma clang fp contract(off)
-  constexpr int CPW = 32 / BITS;
   constexpr int Q = (1 << BITS) - 1;
   const int64_t G = K / 64;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,22 +75,22 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *w, int64_t N
     if (status) *status = -6;  // QL_ERANGE
   }
   const float sf = f16_to_f32(s16), bf = f16_to_f32(b16);
-  uint32_t *pw = packed + n * (K / CPW) + g * (64 / CPW);
+  uint32_t word[2 * BITS];
 #pragma unroll
-  for (int j = 0; j < 64 / CPW; ++j) {
-    uint32_t word = 0;
+  for (int j = 0; j < 2 * BITS; ++j) word[j] = 0u;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      int q = 0;
-      if (sf != 0.f) {
-        float t = __builtin_rintf(__fdiv_rn(__fsub_rn(wp[j * CPW + i], bf), sf));
-        t = fminf(fmaxf(t, 0.f), (float)Q);
-        q = (int)t;
-      }
-      word |= (uint32_t)q << (BITS * i);
+  for (int i = 0; i < 64; ++i) {
+    int q = 0;
+    if (sf != 0.f) {
+      float t = __builtin_rintf(__fdiv_rn(__fsub_rn(wp[i], bf), sf));
+      t = fminf(fmaxf(t, 0.f), (float)Q);
+      q = (int)t;
     }
-    pw[j] = word;
+    stream_put<BITS>(word, i, (uint32_t)q);
   }
+  uint32_t *pw = packed + n * (K * BITS / 32) + g * (2 * BITS);
+#pragma unroll
+  for (int j = 0; j < 2 * BITS; ++j) pw[j] = word[j];
   s[n * G + g] = s16;
   b[n * G + g] = b16;
 }
@@ -112,7 +113,6 @@ __global__ __launch_bounds__(256) void quantize_imatrix_kernel(const float *w, c
                                                                int64_t K, uint32_t *packed, uint16_t *s, uint16_t *b,
                                                                int *status) {
 #pragma clang fp contract(off)
-  constexpr int CPW = 32 / BITS;
   constexpr float Q = (float)((1 << BITS) - 1);
   const int64_t G = K / 64;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -203,14 +203,14 @@ __global__ __launch_bounds__(256) void quantize_imatrix_kernel(const float *w, c
     }
   }
   const float sf = f16_to_f32(s_best), bf = f16_to_f32(b_best);
-  uint32_t *pw = packed + n * (K / CPW) + g * (64 / CPW);
+  uint32_t word[2 * BITS];
 #pragma unroll
-  for (int j = 0; j < 64 / CPW; ++j) {
-    uint32_t word = 0;
+  for (int j = 0; j < 2 * BITS; ++j) word[j] = 0u;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) word |= (uint32_t)(int)code(wv[j * CPW + i], sf, bf) << (BITS * i);
-    pw[j] = word;
-  }
+  for (int i = 0; i < 64; ++i) stream_put<BITS>(word, i, (uint32_t)(int)code(wv[i], sf, bf));
+  uint32_t *pw = packed + n * (K * BITS / 32) + g * (2 * BITS);
+#pragma unroll
+  for (int j = 0; j < 2 * BITS; ++j) pw[j] = word[j];
   s[n * G + g] = s_best;
   b[n * G + g] = b_best;
 }
@@ -228,7 +228,7 @@ hipError_t quantize_imatrix_bits(const float *w, const float *imp, int64_t N, in
 template <int BITS>
 hipError_t dequant_bits(const uint32_t *w, const uint16_t *s, const uint16_t *b, int64_t N, int64_t K,
                         float *out, hipStream_t stream) {
-  const int64_t threads = N * (K * BITS / 32);
+  const int64_t threads = N * (K / 64);
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(dequant_kernel<BITS>, dim3((unsigned)blocks), dim3(256), 0, stream, w, s, b, N, K, out);
   return hipGetLastError();
@@ -251,6 +251,7 @@ hipError_t launch_dequant(int bits, const uint32_t *w, const uint16_t *s, const 
   if (bits == 4) return dequant_bits<4>(w, s, b, N, K, out, stream);
   if (bits == 8) return dequant_bits<8>(w, s, b, N, K, out, stream);
   if (bits == 2) return dequant_bits<2>(w, s, b, N, K, out, stream);
+  if (bits == 3) return dequant_bits<3>(w, s, b, N, K, out, stream);
   return hipErrorInvalidValue;
 }
 
@@ -259,6 +260,7 @@ hipError_t launch_quantize_imatrix(int bits, const float *w, const float *imp, i
   if (bits == 4) return quantize_imatrix_bits<4>(w, imp, N, K, packed, s, b, status, stream);
   if (bits == 8) return quantize_imatrix_bits<8>(w, imp, N, K, packed, s, b, status, stream);
   if (bits == 2) return quantize_imatrix_bits<2>(w, imp, N, K, packed, s, b, status, stream);
+  if (bits == 3) return quantize_imatrix_bits<3>(w, imp, N, K, packed, s, b, status, stream);
   return hipErrorInvalidValue;
 }
 
@@ -267,6 +269,7 @@ hipError_t launch_quantize(int bits, const float *w, int64_t N, int64_t K, uint3
   if (bits == 4) return quantize_bits<4>(w, N, K, packed, s, b, status, stream);
   if (bits == 8) return quantize_bits<8>(w, N, K, packed, s, b, status, stream);
   if (bits == 2) return quantize_bits<2>(w, N, K, packed, s, b, status, stream);
+  if (bits == 3) return quantize_bits<3>(w, N, K, packed, s, b, status, stream);
   return hipErrorInvalidValue;
 }
 

@@ -22,7 +22,7 @@ constexpr int kGroup = 64;
 // removed per group with the row sums of x: sum_k x*(128+q) = P + 128*xsum.
 // 8-bit codes are converted exactly (integers <= 255 fit bf16's 8-bit
 // significand) and carry no offset.
-template <int BITS> struct CodeOffset { static constexpr float value = 128.0f; };
+template <int BITS> struct CodeOffset { static constexpr float value = 128.0f; };  // 2, 3, 4-bit
 template <> struct CodeOffset<8> { static constexpr float value = 0.0f; };
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -116,6 +116,29 @@ __device__ __forceinline__ u32x4 unpack8_b2_pair(uint32_t w, int half) {
   r[3] = and_or(v >> 6, 0x00030003u, hi);
   return r;
 }
+
+// Canonical code stream: a row's codes form one little-endian bit stream
+// along K, code k in stream bits [BITS*k, BITS*k + BITS), stream bit i being
+// bit i % 32 of word i / 32. One 64-wide group is 2*BITS words; 3-bit codes
+// 10, 21, 42 and 53 of a group straddle two words. With i a compile-time
+// constant (unrolled loops) both helpers reduce to shifts and masks.
+template <int BITS>
+__device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[2 * BITS], int i) {
+  const int p = BITS * i, j = p >> 5, sh = p & 31;
+  uint32_t v = w[j] >> sh;
+  if (sh + BITS > 32) v |= w[j + 1] << (32 - sh);
+  return v & ((1u << BITS) - 1u);
+}
+template <int BITS>
+__device__ __forceinline__ void stream_put(uint32_t (&w)[2 * BITS], int i, uint32_t q) {
+  const int p = BITS * i, j = p >> 5, sh = p & 31;
+  w[j] |= q << sh;
+  if (sh + BITS > 32) w[j + 1] |= q >> (32 - sh);
+}
+
+// x >> n for n >= 0, x << -n otherwise (n a compile-time constant after
+// unrolling).
+__device__ __forceinline__ uint32_t shift_right(uint32_t x, int n) { return n >= 0 ? x >> n : x << -n; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

@@ -36,8 +36,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne_s(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Per-lane codes of one group: 4-bit 16 B, 8-bit 32 B, 2-bit 8 B. `p` points
-// at the lane's first 16 (8) bytes; for 8-bit `p2` at its second 16 bytes.
+// Per-lane codes of one group: 4-bit 16 B, 8-bit 32 B, 2-bit 8 B, 3-bit 8 B
+// of low bits + 4 B of high bits (tiled only). `p` points at the lane's first
+// 16 (8) bytes; for 8-bit `p2` at its second 16 bytes, for 3-bit at its
+// high-bit word.
 template <int BITS> struct LaneCodes { u32x4 v[BITS == 8 ? 2 : 1]; };
 
 template <int BITS>
@@ -48,6 +50,9 @@ __device__ __forceinline__ LaneCodes<BITS> load_codes(const uint32_t *p, const u
   } else if constexpr (BITS == 8) {
     c.v[0] = *reinterpret_cast<const u32x4 *>(p);
     c.v[1] = *reinterpret_cast<const u32x4 *>(p2);
+  } else if constexpr (BITS == 3) {
+    const u32x2 t = *reinterpret_cast<const u32x2 *>(p);
+    c.v[0] = u32x4{t[0], t[1], *p2, 0u};
   } else {
     const u32x2 t = *reinterpret_cast<const u32x2 *>(p);
     c.v[0] = u32x4{t[0], t[1], 0u, 0u};
@@ -60,6 +65,14 @@ template <int BITS, bool TILED>
 __device__ __forceinline__ bf16x8 codes_step(const LaneCodes<BITS> &c, int t) {
   if constexpr (BITS == 4) return as_bf16x8(TILED ? unpack8_b4_pair(c.v[0][t]) : unpack8_b4(c.v[0][t]));
   else if constexpr (BITS == 8) return as_bf16x8(unpack8_b8(c.v[t >> 1][(t & 1) * 2], c.v[t >> 1][(t & 1) * 2 + 1]));
+  else if constexpr (BITS == 3) {
+    // low two bits as 2-bit codes, then the high bit of pair P = 4t + p (bits
+    // P and 16 + P of the high-bit word) into bits 2 and 18: 128 + q
+    u32x4 r = unpack8_b2_pair(c.v[0][t >> 1], t & 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = and_or(shift_right(c.v[0][2], 4 * t + p - 2), 0x00040004u, r[p]);
+    return as_bf16x8(r);
+  }
   else return as_bf16x8(TILED ? unpack8_b2_pair(c.v[0][t >> 1], t & 1) : unpack8_b2(c.v[0][t >> 1], t & 1));
 }
 
@@ -118,9 +131,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   if constexpr (TILED) {
     const int l = 32 * h + col;
     gstride = 64 * BITS;  // 32 columns x 2*BITS words
-    wbase = a.w + strip_c * G * gstride + (BITS == 2 ? 2 * l : 4 * l);
+    wbase = a.w + strip_c * G * gstride + (BITS == 2 || BITS == 3 ? 2 * l : 4 * l);
     sbbase = a.sb + strip_c * G * 32 + col;
-    off2 = 256;
+    off2 = BITS == 3 ? 128 - l : 256;  // 3-bit: high-bit word 128 + l of the block
   } else {
     gstride = 2 * BITS;
     wbase = a.w + n * (a.K * BITS / 32) + (BITS == 8 ? 8 * h : (BITS == 4 ? 4 * h : 2 * h));
@@ -394,6 +407,7 @@ hipError_t launch_skinny(int bits, const SkinnyArgs &a, hipStream_t stream) {
   if (bits == 4) return launch_bits<4>(a, stream);
   if (bits == 8) return launch_bits<8>(a, stream);
   if (bits == 2) return launch_bits<2>(a, stream);
+  if (bits == 3) return a.tiled ? launch_layout<3, true>(a, stream) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
 

@@ -5,12 +5,16 @@
  *   y[m, n] = sum_k x[m, k] * W_hat[n, k]
  *   W_hat[n, k] = scale[n, g] * q[n, k] + bias[n, g],   g = k / 64
  *
- * The format -- unsigned codes q of 2, 4 or 8 bits, one f16 scale and one f16
+ * The format -- unsigned codes q of 2, 3, 4 or 8 bits, one f16 scale and one f16
  * bias per 64 consecutive weights of a row, i.e. half a bit of overhead per
  * weight -- is the one described by the Ideogram-4-IQ4_M model card
  * (aimarketly.com; opening section and the section on what "IQ4" means) and
  * the SceneWorks/ideogram-4-mlx model card (huggingface.co; section
- * "Versions": group-wise affine Q4/Q8, group size 64, packed).
+ * "Versions": group-wise affine Q4/Q8, group size 64, packed). 3-bit codes
+ * serve the mixed-precision packs of the IQ4_M card (3-bit DiT bulk with
+ * 8-bit modulation and conditioning; sections "Against the pack this
+ * replaces" and "Conversion"); they run on the TILED layout only (the
+ * skinny kernel and the FAST GEMM), other requests are QL_EUNSUPPORTED.
  *
  * Conventions for every entry point:
  *  - Pointers whose name ends in _host are host memory; all others are device
@@ -18,10 +22,12 @@
  *    the library never frees caller memory.
  *  - Arrays are row-major and contiguous.
  *      x        bf16 bit patterns, [M, K]
- *      packed_q uint32, [N, K*bits/32]; code k of a row sits in bits
- *               [bits*(k % (32/bits)), +bits) of word k / (32/bits)
- *               (little-endian along K; the pages say only "packed", this is
- *               the layout this library fixes)
+ *      packed_q uint32, [N, K*bits/32]; each row is one little-endian bit
+ *               stream along K: code k sits in stream bits
+ *               [bits*k, bits*k + bits), stream bit i being bit i % 32 of
+ *               word i / 32 (so 2/4/8-bit words hold 32/bits whole codes
+ *               and 3-bit codes may straddle two words; the pages say only
+ *               "packed", this is the layout this library fixes)
  *      scales   f16 bit patterns, [N, K/64]
  *      biases   f16 bit patterns, [N, K/64]
  *      out      fp32 [M, N] (or bf16 with QL_OUT_BF16 in the _ex form)
@@ -46,8 +52,9 @@ typedef enum {
   QL_OK = 0,
   QL_EINVAL = -1,        /* bad size, null pointer, K not a multiple of 64  */
   QL_EALIGN = -2,        /* x / out / packed_q not 16-byte aligned            */
-  QL_EUNSUPPORTED = -3,  /* bits not in {2,4,8}, group != 64, forced path
-                            that cannot serve the shape                       */
+  QL_EUNSUPPORTED = -3,  /* bits not in {2,3,4,8}, group != 64, forced path
+                            that cannot serve the shape, 3-bit codes on a
+                            path other than the tiled skinny / FAST GEMM     */
   QL_EWORKSPACE = -4,    /* caller workspace missing or too small             */
   QL_EHIP = -5,          /* a HIP runtime call or kernel launch failed        */
   QL_ERANGE = -6         /* non-finite weight, or f16 overflow of scale/bias  */
@@ -59,7 +66,8 @@ typedef enum { QL_OUT_F32 = 0, QL_OUT_BF16 = 1 } ql_out_dtype;
  * Weight layouts. CANONICAL is the layout described at the top of this file.
  * TILED is this library's load-time repack into the kernels' lane order (see
  * qlinear_repack): for each strip of 32 output rows and each 64-wide group the
- * codes form one contiguous block (4-bit 1 KB, 8-bit 2 KB, 2-bit 512 B) and
+ * codes form one contiguous block (4-bit 1 KB, 8-bit 2 KB, 2-bit 512 B, 3-bit
+ * 768 B: the low two bits as a 2-bit block, then a plane of high bits) and
  * the scale and bias become one uint32 (s | b << 16) per row and group, so a
  * wave's loads cover whole cache lines.
  */
@@ -128,7 +136,7 @@ typedef struct ql_forward_args {
   const uint32_t *packed_q;  /* uint32 [N, K*bits/32]                        */
   const void *scales;        /* f16 [N, K/group]                             */
   const void *biases;        /* f16 [N, K/group]                             */
-  int bits;                  /* 2, 4 or 8                                    */
+  int bits;                  /* 2, 3, 4 or 8                                 */
   int group;                 /* 64                                           */
   int64_t M, N, K;
   void *out;                 /* [M, N] ([M, N/2] with QL_EPI_SWIGLU), dtype per out_dtype */

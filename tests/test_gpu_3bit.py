@@ -1,0 +1,103 @@
+"""GPU tests specific to 3-bit codes (the parity tests of the shared paths run
+3-bit alongside 2/4/8-bit): which requests the library serves, and the two
+3-bit paths at full size on sampled outputs.
+
+3-bit codes run on the tiled layout only: the FAST GEMM for M > 16 and the
+skinny kernel for M <= 16. The canonical layout and the exact-mode GEMM
+return QL_EUNSUPPORTED."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_qlinear_amd import inputs
+from group_wise_affine_qlinear_amd import qlinear as ql
+
+from gpu_helpers import (MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, Case, dev, run_forward,
+                         torch_or_skip)
+
+pytestmark = pytest.mark.gpu
+
+RELF_FAST = 5e-4
+MAXABS_RMS_FAST = 4e-3
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_or_skip()
+    ql.load_library()
+    return t
+
+
+def test_3bit_requests_served_and_rejected(torch):
+    c = Case(64, 256, 256, 3, wid=620)
+    with pytest.raises(ql.QLinearError) as e:      # canonical layout
+        run_forward(torch, c)
+    assert e.value.status == ql.QL_EUNSUPPORTED
+    with pytest.raises(ql.QLinearError) as e:      # canonical entry point
+        run_forward(torch, c, via_ex=False)
+    assert e.value.status == ql.QL_EUNSUPPORTED
+    with pytest.raises(ql.QLinearError) as e:      # exact-mode GEMM
+        run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
+    assert e.value.status == ql.QL_EUNSUPPORTED
+    run_forward(torch, c, layout=ql.QL_LAYOUT_TILED)
+    assert ql.qlinear_last_path().startswith("gemm3_f16_256x256_b3"), ql.qlinear_last_path()
+    c8 = Case(8, 256, 256, 3, wid=621)
+    run_forward(torch, c8, layout=ql.QL_LAYOUT_TILED)
+    assert ql.qlinear_last_path() == "skinny_b3_m8_tiled"
+    with pytest.raises(ql.QLinearError) as e:      # skinny M on the canonical layout
+        run_forward(torch, c8)
+    assert e.value.status == ql.QL_EUNSUPPORTED
+
+
+def sample(n, seed, extra=50):
+    edges = [0, 1, 15, 16, 31, 32, 255, 256, n // 2, n - 2, n - 1]
+    rng = np.random.default_rng(seed)
+    idx = set(i for i in edges if 0 <= i < n)
+    idx.update(rng.integers(0, n, size=min(extra, n)).tolist())
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["qkv_1024", "adaln_m8"])
+def test_3bit_full_size_sampled(torch, name):
+    """The QKV projection (FAST GEMM, outlier channels) and the M=8 AdaLN
+    projection (skinny kernel) at full size with 3-bit weights, quantized and
+    tiled on the device; the oracle quantizes the same weights on the CPU."""
+    wl = inputs.WORKLOADS[name]
+    M, K, N = wl["M"], wl["K"], wl["N"]
+    w = inputs.weights(N, K, wl["id"])
+    x = inputs.activations_bf16(M, K, wl["id"], wl["x"])
+    q, s16, b16 = oracle.quantize_rtn(w, 3)
+    packed = oracle.pack(q, 3)
+    rows, cols = sample(M, 3000 + wl["id"]), sample(N, 3100 + wl["id"])
+    ref = oracle.forward_rows(x, packed, s16, b16, 3, K, rows, cols)
+    # device quantizer: byte-equal to the oracle's fit
+    wd = dev(torch, w)
+    del w
+    p = torch.empty((N, K * 3 // 32), dtype=torch.int32, device="cuda")
+    s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ql.qlinear_quantize_rtn(wd, 3, 64, N, K, p, s, b, st)
+    torch.cuda.synchronize()
+    del wd
+    assert int(st.item()) == 0
+    assert np.array_equal(p.cpu().numpy().view(np.uint32), packed)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s16) and np.array_equal(b.cpu().numpy().view(np.uint16), b16)
+    tq, tsb = ql.qlinear_repack(p, s, b, 3, 64, N, K)
+    del p, s, b
+    xd = dev(torch, x)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ql.qlinear_forward_ex(xd, tq, tsb, None, 3, M, N, K, out, layout=ql.QL_LAYOUT_TILED)
+    torch.cuda.synchronize()
+    path = ql.qlinear_last_path()
+    assert bool(torch.isfinite(out).all())
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    blk = out.index_select(0, ri).index_select(1, ci).cpu().numpy()
+    e = oracle.error_metrics(blk, ref)
+    if M > 16:
+        assert path.startswith("gemm3"), path
+        assert e["relF"] <= RELF_TOL and e["maxabs_over_rms"] <= MAXABS_RMS_TOL, (path, e)
+        assert e["relF"] <= RELF_FAST and e["maxabs_over_rms"] <= MAXABS_RMS_FAST, (path, e)
+    else:
+        assert path.startswith("skinny_b3"), path
+        assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, (path, e)

@@ -44,7 +44,7 @@ def check_fast(y, c):
 FAST_SHAPES = [(520, 390, 320), (300, 520, 640), (17, 40, 64), (256, 256, 512), (777, 1000, 448)]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape", FAST_SHAPES)
 def test_fast_parity(torch, shape, bits):
     M, N, K = shape
@@ -104,7 +104,7 @@ def test_fast_one_hot_rows_give_fp16_weights_exactly(torch):
     assert np.array_equal(y, w16[:, cols].T)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_fast_bf16_out_is_rounded_fp32_out(torch, bits):
     c = Case(300, 260, 384, bits, wid=440 + bits)
     y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
@@ -133,7 +133,7 @@ FAST_TAIL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("slots,shape", FAST_TAIL_CASES)
 def test_fast_split_tail(torch, monkeypatch, slots, shape, bits):
     M, N, K = shape
@@ -206,7 +206,7 @@ FAST_SPLIT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape,splits", FAST_SPLIT_CASES)
 def test_fast_split_k(torch, shape, splits, bits):
     M, N, K = shape

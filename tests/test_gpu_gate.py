@@ -72,7 +72,7 @@ GATE_SHAPES = [(520, 800, 320, 260), (300, 2080, 448, 7), (64, 256, 128, 64), (5
                (17, 1056, 256, 1000), (1, 384, 192, 1)]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape", GATE_SHAPES)
 def test_gate_residual_parity(torch, shape, bits):
     M, N, K, gate_rows = shape

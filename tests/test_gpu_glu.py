@@ -72,7 +72,7 @@ def check(y, c, rows=None, fs=None):
     assert e2["relF"] <= RELF_FAST <= RELF_TOL, ("vs exact product", e2)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_glu_repack_is_a_row_permutation_and_round_trips(torch, bits):
     N, K = 96 * 2, 320
     c = Case(8, N, K, bits, wid=500 + bits)
@@ -93,7 +93,7 @@ def test_glu_repack_is_a_row_permutation_and_round_trips(torch, bits):
 GLU_SHAPES = [(520, 800, 320), (300, 2080, 448), (64, 32, 128), (5, 512, 640), (17, 1056, 256)]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape", GLU_SHAPES)
 def test_swiglu_parity(torch, shape, bits):
     M, N, K = shape

@@ -49,7 +49,7 @@ def run(torch, w, imp, bits):
     return host_u32(p), host_u16(s), host_u16(b), int(st.item())
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("kind", ["outlier", "sparse", "wide", "uniform"])
 def test_imatrix_byte_equal_to_oracle(torch, bits, kind):
     N, K = 130, 640

@@ -46,17 +46,29 @@ def reference_tiling(q, s16, b16, bits):
                                 e = c[32 * h + 16 * part + 4 * t:32 * h + 16 * part + 4 * t + 4]
                                 word = sum(int(e[i]) << (8 * i) for i in range(4))
                                 tiled[base + part * 256 + h * 128 + col * 4 + t] = word
-                else:
+                elif bits == 2:
                     for h in range(2):
                         for t in range(2):
                             e = c[32 * h + 16 * t:32 * h + 16 * t + 16]
                             word = sum(int(e[2 * p]) << (2 * p) | int(e[2 * p + 1]) << (16 + 2 * p) for p in range(8))
                             tiled[base + h * 64 + col * 2 + t] = word
+                else:
+                    # 3-bit: the low two bits as the 2-bit block, then one word
+                    # of high bits per (half, column): code 32h + 2P at bit P,
+                    # code 32h + 2P + 1 at bit 16 + P
+                    for h in range(2):
+                        for t in range(2):
+                            e = c[32 * h + 16 * t:32 * h + 16 * t + 16] & 3
+                            word = sum(int(e[2 * p]) << (2 * p) | int(e[2 * p + 1]) << (16 + 2 * p) for p in range(8))
+                            tiled[base + h * 64 + col * 2 + t] = word
+                        e = c[32 * h:32 * h + 32] >> 2
+                        tiled[base + 128 + h * 32 + col] = sum(int(e[2 * p]) << p | int(e[2 * p + 1]) << (16 + p)
+                                                               for p in range(16))
                 sb[(st * G + g) * 32 + col] = int(s16[n, g]) | (int(b16[n, g]) << 16)
     return tiled, sb
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_repack_matches_definition_and_round_trips(torch, bits):
     c = Case(1, 70, 256, bits, wid=301)   # 70 rows: a ragged last strip
     _, p, s, b = c.device(torch)
@@ -74,7 +86,7 @@ def test_repack_matches_definition_and_round_trips(torch, bits):
     assert np.array_equal(host_u16(s2), c.s16) and np.array_equal(host_u16(b2), c.b16)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 16])
 def test_skinny_tiled_parity(torch, bits, M):
     c = Case(M, 300, 1536, bits, wid=310 + M)

@@ -27,7 +27,7 @@ def torch():
 
 # ------------------------------------------------------------------ dequantize / quantize
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_dequantize_bit_exact(torch, bits):
     c = Case(1, 300, 512, bits, wid=201)
     _, p, s, b = c.device(torch)
@@ -39,7 +39,7 @@ def test_dequantize_bit_exact(torch, bits):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_device_quantizer_byte_equal(torch, bits):
     w = inputs.weights(257, 1024, workload_id=202)
     # adversarial rows: exact grid, ties, constant, signed zeros, tiny scales

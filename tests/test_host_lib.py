@@ -48,7 +48,9 @@ def test_sizes(lib):
     assert ql.qlinear_packed_words(4, 4608, 4608) == 4608 * 4608 // 8
     assert ql.qlinear_packed_words(2, 3, 64) == 3 * 4
     assert ql.qlinear_packed_words(8, 3, 64) == 3 * 16
-    assert ql.qlinear_packed_words(3, 3, 64) == 0
+    assert ql.qlinear_packed_words(3, 3, 64) == 3 * 6
+    assert ql.qlinear_packed_words(5, 3, 64) == 0
+    assert ql.qlinear_tiled_words(3, 40, 128) == 64 * 128 * 3 // 32
     # skinny path needs no workspace; the GEMM path needs per-group row sums of x
     assert ql.qlinear_workspace_bytes(4, 1, 27648, 4608) == 0
     ws = ql.qlinear_workspace_bytes(4, 4096, 4608, 4608)
@@ -56,6 +58,24 @@ def test_sizes(lib):
     # long K with few output tiles uses split K partials
     assert ql.qlinear_workspace_bytes(4, 512, 4608, 53248) > 512 * 4608 * 4
     assert ql.qlinear_workspace_bytes(4, 64, 256, 100) == 0
+
+
+def test_host_pack_3bit_hand_words(lib):
+    # code 10 of a row straddles words 0 and 1, code 21 words 1 and 2
+    q = np.zeros((2, 32), np.uint8)
+    q[0, 10] = 7
+    q[1, 21] = 5
+    p = ql.qlinear_pack_host(q, 3)
+    assert p.tolist() == [[0xC0000000, 0x1, 0x0], [0x0, 0x80000000, 0x2]]
+    assert np.array_equal(ql.qlinear_unpack_host(p, 3, 32), q)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_host_pack_matches_oracle_stream(lib, bits):
+    q = inputs.random_codes(19, 448, bits, workload_id=102)
+    p = ql.qlinear_pack_host(q, bits)
+    assert np.array_equal(p, oracle.pack(q, bits))
+    assert np.array_equal(ql.qlinear_unpack_host(p, bits, 448), q)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
@@ -76,7 +96,7 @@ def test_host_pack_rejects_bad_code(lib):
     assert e.value.status == ql.QL_ERANGE
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_host_quantize_matches_oracle_random(lib, bits):
     w = inputs.weights(64, 1024, workload_id=102)
     qh, sh, bh = ql.qlinear_quantize_rtn_host(w, bits)
@@ -102,7 +122,7 @@ def adversarial_weights():
     return np.stack(rows).astype(np.float32)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_host_quantize_matches_oracle_adversarial(lib, bits):
     w = adversarial_weights()
     qh, sh, bh = ql.qlinear_quantize_rtn_host(w, bits)
@@ -138,7 +158,7 @@ def test_host_quantize_errors(lib):
         ql.qlinear_quantize_rtn_host(w, 4)
     assert e.value.status == ql.QL_ERANGE
     with pytest.raises(ql.QLinearError) as e:
-        ql.qlinear_quantize_rtn_host(np.zeros((1, 64), np.float32), 3)
+        ql.qlinear_quantize_rtn_host(np.zeros((1, 64), np.float32), 5)
     assert e.value.status == ql.QL_EUNSUPPORTED
     with pytest.raises(ql.QLinearError) as e:
         ql.qlinear_quantize_rtn_host(np.zeros((1, 96), np.float32), 4)
@@ -156,7 +176,9 @@ def _args(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=3), ql.QL_EUNSUPPORTED),
+    (dict(bits=3), ql.QL_EUNSUPPORTED),              # 3-bit: tiled layout only
+    (dict(bits=3, layout=1, mode=1, M=64), ql.QL_EUNSUPPORTED),   # no exact-mode 3-bit GEMM
+    (dict(bits=5), ql.QL_EUNSUPPORTED),
     (dict(bits=16), ql.QL_EUNSUPPORTED),
     (dict(group=32), ql.QL_EUNSUPPORTED),
     (dict(K=100), ql.QL_EINVAL),
@@ -210,7 +232,7 @@ def test_tiled_sizes_and_repack_validation(lib):
     assert ql.qlinear_tiled_sb_words(70, 256) == 96 * 4
     assert ql.qlinear_tiled_words(4, 10, 100) == 0
     vp = 0x1000
-    assert lib.qlinear_repack(vp, vp, vp, 3, 64, 8, 64, vp, vp, None) == ql.QL_EUNSUPPORTED
+    assert lib.qlinear_repack(vp, vp, vp, 5, 64, 8, 64, vp, vp, None) == ql.QL_EUNSUPPORTED
     assert lib.qlinear_repack(vp, vp, vp, 4, 64, 8, 96, vp, vp, None) == ql.QL_EINVAL
     assert lib.qlinear_repack(vp + 4, vp, vp, 4, 64, 8, 64, vp, vp, None) == ql.QL_EALIGN
     assert lib.qlinear_repack(0, vp, vp, 4, 64, 8, 64, vp, vp, None) == ql.QL_EINVAL
