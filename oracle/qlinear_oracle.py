@@ -323,26 +323,29 @@ def weighted_error(w, importance, q, s16, b16, group: int = GROUP) -> np.ndarray
 
 # ---------------------------------------------------------------- packing
 
+_PACK_ROWS = 512   # rows per chunk: bounds the one-byte-per-bit temporaries
+
+
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
     """q uint8 [N, K] (values < 2**bits) -> uint32 [N, K*bits/32].
 
-    Bit j of code k goes to bit p % 32 of word p // 32, p = bits*k + j (one
-    little-endian bit stream per row). Written bit by bit: for a fixed bit j
-    and a fixed k % 32 the codes k land in distinct words, so each step is a
-    plain vectorised OR.
+    Each row becomes one bit stream: code k contributes its bits, least
+    significant first, as stream bits bits*k .. bits*k + bits - 1; the stream
+    is then cut into bytes (stream bit i = bit i % 8 of byte i // 8) and the
+    bytes into little-endian uint32 words.
     """
     q = np.asarray(q)
     n, k = q.shape
     nw = words_per_row(bits, k)
     if q.size and int(q.max()) >= (1 << bits):
         raise ValueError("code out of range")
-    q32 = q.astype(np.uint32)
-    words = np.zeros((n, nw), dtype=np.uint32)
-    for j in range(bits):
-        for r in range(min(32, k)):
-            ks = np.arange(r, k, 32)
-            p = bits * ks + j
-            words[:, p // 32] |= ((q32[:, ks] >> np.uint32(j)) & np.uint32(1)) << (p % 32).astype(np.uint32)
+    words = np.empty((n, nw), dtype=np.uint32)
+    for r0 in range(0, n, _PACK_ROWS):
+        qs = q[r0:r0 + _PACK_ROWS].astype(np.uint8)
+        code_bits = np.unpackbits(qs[:, :, None], axis=2, bitorder="little")[:, :, :bits]   # [r, k, bits]
+        stream = code_bits.reshape(qs.shape[0], k * bits)
+        stream_bytes = np.packbits(stream, axis=1, bitorder="little")
+        words[r0:r0 + qs.shape[0]] = stream_bytes.view("<u4")
     return words
 
 
@@ -352,13 +355,13 @@ def unpack(words: np.ndarray, bits: int, k: int) -> np.ndarray:
     n = words.shape[0]
     if words.shape[1] != words_per_row(bits, k):
         raise ValueError("word count does not match K")
-    q = np.zeros((n, k), dtype=np.uint32)
-    for j in range(bits):
-        for r in range(min(32, k)):
-            ks = np.arange(r, k, 32)
-            p = bits * ks + j
-            q[:, ks] |= ((words[:, p // 32] >> (p % 32).astype(np.uint32)) & np.uint32(1)) << np.uint32(j)
-    return q.astype(np.uint8)
+    q = np.empty((n, k), dtype=np.uint8)
+    for r0 in range(0, n, _PACK_ROWS):
+        ws = np.ascontiguousarray(words[r0:r0 + _PACK_ROWS], dtype="<u4")
+        stream = np.unpackbits(ws.view(np.uint8), axis=1, bitorder="little")               # [r, k*bits]
+        code_bits = stream.reshape(ws.shape[0], k, bits)
+        q[r0:r0 + ws.shape[0]] = np.packbits(code_bits, axis=2, bitorder="little")[:, :, 0]
+    return q
 
 
 # ---------------------------------------------------------------- dequantize
