@@ -112,29 +112,28 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     del out
 
     K, N = 4608, 27648
-    for M in (1, 8):
-        for tiled in (False, True):
-            copies = 8  # 8 x 71.7 MB of distinct weights > 256 MB Infinity Cache
-            sets = make_weights(torch, ql, inputs, N, K, 4, 40 + (M > 1), copies, tiled=tiled)
-            x = torch.from_numpy(inputs.activations_bf16(M, K, 40 + (M > 1)).view("int16")).cuda()
-            out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-            layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
-            i = [0]
+    for M, bits, tiled in ((1, 4, False), (1, 4, True), (8, 4, False), (8, 4, True), (1, 8, True), (1, 3, True)):
+        copies = 8  # 8 x >= 56 MB of distinct weights > 256 MB Infinity Cache
+        sets = make_weights(torch, ql, inputs, N, K, bits, 40 + (M > 1), copies, tiled=tiled)
+        x = torch.from_numpy(inputs.activations_bf16(M, K, 40 + (M > 1)).view("int16")).cuda()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
+        i = [0]
 
-            def fn():
-                p, s, b = sets[i[0] % copies]
-                i[0] += 1
-                ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out, layout=layout)
+        def fn():
+            p, s, b = sets[i[0] % copies]
+            i[0] += 1
+            ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=layout)
 
-            ms = time_calls(torch, fn, 64, 16)
-            by = algorithmic_bytes(M, N, K, 4)
-            gbs = by / (ms * 1e-3) / 1e9
-            lname = "tiled" if tiled else "canonical"
-            rows[f"adaln_skinny_M{M}_K{K}_N{N}_q4_{lname}"] = {
-                "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies_rotated": copies}
-            del sets
-            log(f"skinny M={M} {lname}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
+        ms = time_calls(torch, fn, 64, 16)
+        by = algorithmic_bytes(M, N, K, bits)
+        gbs = by / (ms * 1e-3) / 1e9
+        lname = "tiled" if tiled else "canonical"
+        rows[f"adaln_skinny_M{M}_K{K}_N{N}_q{bits}_{lname}"] = {
+            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies_rotated": copies}
+        del sets
+        log(f"skinny M={M} q{bits} {lname}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
 
     # SwiGLU MLP gate/up projection at 1024x1024: plain FAST GEMM (fp32 y, [M, 2F])
     # against the fused epilogue (bf16 silu(gate) * up, [M, F])
@@ -212,13 +211,72 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     log(f"attn-out plain {ms_plain*1e3:.1f} us, unfused gate {ms_unf*1e3:.1f} us, fused gate {ms_fused*1e3:.1f} us")
     del tq, tsb, x, x16, rs, res, gate, y
 
+    # one DiT block at 1024x1024 (4608 tokens) under the mixed-precision plans:
+    # modulation (skinny, M=1, 8-bit), QKV, attention-out + gated residual,
+    # gate/up + fused SwiGLU (bf16), down (fed by the SwiGLU output) + gated
+    # residual, at the plan's bulk width; fp16 activations made per projection
+    from group_wise_affine_qlinear_amd import plan as qplan
+    M = 4608
+    projs = {p.role: p for p in qplan.block_projections("mixed_4_8")}
+    wf = {r: torch.from_numpy(inputs.weights(p.N, p.K, 80 + i)).cuda() for i, (r, p) in enumerate(projs.items())}
+    x = torch.from_numpy(inputs.activations_bf16(M, 4608, 81).view("int16")).cuda()
+    att = torch.from_numpy(inputs.activations_bf16(M, 4608, 82).view("int16")).cuda()
+    temb = torch.from_numpy(inputs.activations_bf16(1, qplan.ADALN, 83).view("int16")).cuda()
+    res = torch.from_numpy(inputs.residual_stream(M, 4608, 84)).cuda()
+    gates = torch.from_numpy(inputs.adaln_gate(2, 4608, 85)).cuda()
+    g_attn, g_mlp = gates[0:1].contiguous(), gates[1:2].contiguous()
+    qkv = torch.empty((M, 3 * 4608), dtype=torch.bfloat16, device="cuda")
+    hmid = torch.empty((M, 12288), dtype=torch.bfloat16, device="cuda")
+    mod = torch.empty((1, 6 * 4608), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for policy in ("mixed_3_8", "mixed_4_8"):
+        wts = {}
+        for p in qplan.block_projections(policy):
+            pq = torch.empty((p.N, p.K * p.bits // 32), dtype=torch.int32, device="cuda")
+            ps = torch.empty((p.N, p.K // 64), dtype=torch.int16, device="cuda")
+            pb = torch.empty((p.N, p.K // 64), dtype=torch.int16, device="cuda")
+            ql.qlinear_quantize_rtn(wf[p.role], p.bits, 64, p.N, p.K, pq, ps, pb, status)
+            if p.role == "mlp_gate_up":
+                tq, tsb = ql.qlinear_repack_glu(pq, ps, pb, p.bits, 64, p.N, p.K)
+            else:
+                tq, tsb = ql.qlinear_repack(pq, ps, pb, p.bits, 64, p.N, p.K)
+            wts[p.role] = (tq, tsb, p)
+            del pq, ps, pb
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError("quantizer reported a range error")
+
+        def proj(role, xin, out, **kw):
+            tq, tsb, p = wts[role]
+            ql.qlinear_forward_ex(xin, tq, tsb, None, p.bits, xin.shape[0], p.N, p.K, out,
+                                  layout=ql.QL_LAYOUT_TILED, **kw)
+
+        def block():
+            proj("adaln_modulation", temb, mod)
+            proj("attn_qkv", x, qkv)
+            proj("attn_out", att, res, epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=g_attn, gate_rows=M)
+            proj("mlp_gate_up", x, hmid, epilogue=ql.QL_EPI_SWIGLU)
+            proj("mlp_down", hmid, res, epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=g_mlp, gate_rows=M)
+
+        ms = time_calls(torch, block, 10, 3)
+        blk = qplan.block_projections(policy)
+        flops = sum(2 * (1 if p.role == "adaln_modulation" else M) * p.N * p.K for p in blk)
+        rows[f"dit_block_1024_{policy}"] = {
+            "us": round(ms * 1e3, 1), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+            "weight_MB": round(sum(p.storage_bytes for p in blk) / 1e6, 1),
+            "bits_per_weight_model": round(qplan.bits_per_weight(qplan.model_plan(policy)), 3),
+            "note": "modulation M=1 8-bit skinny; QKV, out+gate, gate/up+SwiGLU, down+gate at the bulk width"}
+        log(f"DiT block {policy}: {ms*1e3:.1f} us")
+        del wts
+    del wf, x, att, temb, res, gates, qkv, hmid, mod
+
     # 2048x2048 canvas: per-bit layer sweep, and one pass over the 34 blocks'
     # attention projections (QKV N=13824 then out N=4608) with 34 distinct
     # weight sets per width (every launch streams its weights)
     M, K = 16896, 4608
     x = torch.from_numpy(inputs.activations_bf16(M, K, 5).view("int16")).cuda()
     x16, rs = ql.qlinear_fast_activations(x, M, K)
-    for bits in (2, 4, 8):
+    for bits in (2, 3, 4, 8):
         layers = []
         for N in (13824, 4608):
             w = torch.from_numpy(inputs.weights(N, K, 5 if N == 4608 else 50)).cuda()
