@@ -71,7 +71,7 @@ def test_full_size_sampled(torch, name, bits):
         assert bool(torch.isfinite(y).all()), "non-finite output"
         return y.index_select(0, ri).index_select(1, ci).cpu().numpy()
 
-    # canonical layout, the spec entry point (EXACT numerics)
+    # canonical layout, the primary entry point (EXACT numerics)
     out.fill_(float("nan"))
     ql.qlinear_forward(xd, pd, sd, bd, bits, 64, M, N, K, out)
     torch.cuda.synchronize()
