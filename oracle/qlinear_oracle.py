@@ -421,17 +421,22 @@ def fast_weights_f16(q: np.ndarray, s16: np.ndarray, b16: np.ndarray, group: int
 
 
 def fast_activations_f16(x_bf16: np.ndarray):
-    """FAST-mode activations: per row the smallest e >= 0 with max|x|*2^-e < 2^15,
-    then x*2^-e rounded to fp16 (exact for |x*2^-e| >= 2^-14). Returns
-    (x16 as float16 [M, K], 2^e as float64 [M])."""
+    """FAST-mode activations: each row is scaled by the power of two 2^-e that
+    brings its largest magnitude into [2^14, 2^15) (e = floor(log2 max|x|) - 14,
+    clamped to [-126, 120]; e = 0 for an all-zero row), then rounded to fp16
+    (exact for every scaled magnitude >= 2^-14, i.e. down to 2^-28 of the row's
+    largest value). Returns (x16 as float16 [M, K], 2^e as float64 [M])."""
     x = bf16_bits_to_f64(x_bf16)
     m = x.shape[0]
     scale = np.ones(m, dtype=np.float64)
     for r in range(m):
         mx = float(np.max(np.abs(x[r]))) if x.shape[1] else 0.0
-        e = 0
-        while mx * 2.0 ** -e >= 32768.0 and e < 120:
-            e += 1
+        if mx == 0.0:
+            e = 0
+        elif not math.isfinite(mx):
+            e = 120
+        else:
+            e = min(max(math.frexp(mx)[1] - 1 - 14, -126), 120)   # frexp: mx = f * 2^k, f in [0.5, 1)
         scale[r] = 2.0 ** e
     x16 = (x / scale[:, None]).astype(np.float16)
     return x16, scale

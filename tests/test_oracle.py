@@ -479,28 +479,55 @@ def test_fast_equals_exact_when_everything_is_representable():
 
 def test_fast_row_scaling_is_a_power_of_two():
     k = 64
-    x = np.zeros((4, k), np.float32)
-    x[0, :3] = [65536.0, -3.0, 0.5]     # max 2^16 -> e = 2 (2^16 / 4 = 2^14 < 2^15)
-    x[1, 0] = 32768.0                   # exactly 2^15 is not below 2^15 -> e = 1
+    x = np.zeros((8, k), np.float32)
+    x[0, :3] = [65536.0, -3.0, 0.5]     # max 2^16 -> e = 2 (2^16 / 4 = 2^14)
+    x[1, 0] = 32768.0                   # exactly 2^15 -> e = 1
     x[2, 0] = 32512.0                   # largest bf16 below 2^15 -> e = 0
     x[3, 0] = -3.0e38                   # near the top of the bf16 range
+    x[4, :2] = [3.0, 1.0]               # max 3 = 1.5 * 2^1 -> e = 1 - 14 = -13 (3 * 2^13 = 24576)
+    x[5, 0] = 2.0 ** -30                # tiny row -> e = -44, scaled up to 2^14
+    # row 6 stays all zero -> e = 0
+    x[7, 0] = 2.0 ** -126               # smallest normal fp32: e = -140 clamps to -126
     xb = inputs.f32_to_bf16_bits(x)
     x16, scale = oracle.fast_activations_f16(xb)
     assert list(scale[:3]) == [4.0, 2.0, 1.0]
+    assert scale[4] == 2.0 ** -13 and scale[5] == 2.0 ** -44 and scale[6] == 1.0 and scale[7] == 2.0 ** -126
     e3 = int(round(math.log2(scale[3])))
     xmax = float(oracle.bf16_bits_to_f64(xb[3:4, :1])[0, 0])
-    assert abs(xmax) * 2.0 ** -e3 < 32768 <= abs(xmax) * 2.0 ** -(e3 - 1)
+    assert 16384 <= abs(xmax) * 2.0 ** -e3 < 32768
     # scaled values that are powers of two or small integers stay exact
     assert float(x16[0, 0]) * 4 == 65536.0 and float(x16[0, 1]) * 4 == -3.0 and float(x16[0, 2]) * 4 == 0.5
+    assert float(x16[4, 0]) == 24576.0 and float(x16[4, 1]) == 8192.0
+    assert float(x16[5, 0]) == 16384.0 and float(x16[7, 0]) == 1.0
 
 
 def test_fast_activation_subnormals_round_to_nearest():
-    vals = [2.0 ** -20, 1.5 * 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 * (1 + 2.0 ** -7)]
+    # a row whose largest value is 2^14 keeps e = 0, so its small values land
+    # in the fp16 subnormal range and round to nearest-even there
+    vals = [2.0 ** 14, 2.0 ** -20, 1.5 * 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 * (1 + 2.0 ** -7)]
     xb = inputs.f32_to_bf16_bits(np.array([vals], np.float32))
     x16, scale = oracle.fast_activations_f16(xb)
     assert scale[0] == 1.0
     for v, got in zip(oracle.bf16_bits_to_f64(xb)[0], x16.view(np.uint16)[0]):
         assert int(got) == exact_f16_rne(Fraction(float(v))), v
+
+
+def test_fast_tiny_rows_keep_their_accuracy():
+    # a row of activations around 1e-9 loses nothing to the fp16 range: its
+    # FAST product meets the acceptance bar like a row of unit scale
+    rng = np.random.default_rng(15)
+    w = (rng.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    packed = oracle.pack(q, 4)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    x[1] *= np.float32(2.0 ** -30)
+    x[2] *= np.float32(2.0 ** 20)
+    xb = inputs.f32_to_bf16_bits(x)
+    fast = oracle.forward_fast(xb, packed, s16, b16, 4, 256)
+    exact = oracle.forward(xb, packed, s16, b16, 4, 256)
+    for r in range(3):
+        e = oracle.error_metrics(fast[r:r + 1], exact[r:r + 1])
+        assert e["relF"] < 5e-4, (r, e)
 
 
 def test_fast_error_budget_on_normal_weights():
