@@ -7,11 +7,11 @@
 // weight is instead dequantized once per block tile and group:
 //     W16[n,k] = fp16( s[n,g]*q[n,k] + b[n,g] )        (one rounding, packed
 //                                                        fp16 fused multiply-add)
-// and x enters as fp16 from a prepass that scales each row by a power of two
-// 2^-e (e >= 0, the smallest that keeps the row below 2^15; e = 0 for any
-// row already in range) so the conversion from bf16 is exact for every
-// value of magnitude >= 2^-14 after scaling. The output row is multiplied back
-// by 2^e. fp16 keeps 11 significant bits where bf16 keeps 8, so the only
+// and x enters as fp16 from a prepass that scales each row by the power of
+// two 2^-e bringing its largest magnitude into [2^14, 2^15), so the
+// conversion from bf16 is exact for every value within 2^28 of the row's
+// largest (scaled magnitude >= 2^-14). The output row is multiplied back by
+// 2^e. fp16 keeps 11 significant bits where bf16 keeps 8, so the only
 // rounding beyond fp32 accumulation is the half-ulp (2^-11 relative) of W16:
 // relative Frobenius error ~2e-4 on the pages' shapes, against 1.7e-3 for
 // weights rounded to bf16. The mode requires |W| < 65504 (true for weights
@@ -449,9 +449,18 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   }
 }
 
+// Row exponent of the fp16 activations: the power of two 2^-e that brings the
+// row's largest magnitude mx into [2^14, 2^15), e = floor(log2 mx) - 14,
+// clamped to [-126, 120] so 2^e and 2^-e are normal fp32 (e = 0 for mx = 0).
+__device__ __forceinline__ int row_exponent(float mx) {
+  if (!(mx > 0.f)) return 0;
+  const int ex = ilogbf(mx);  // exact for fp32 subnormals; INT_MAX for inf
+  return ex > 134 ? 120 : min(max(ex - 14, -126), 120);
+}
+
 // x (bf16) -> x16 (fp16) with a power-of-two scale per row. One block per
-// row: the row's max magnitude picks e (the smallest e >= 0 with max*2^-e <
-// 2^15); every value is multiplied by 2^-e (exact) and rounded to fp16.
+// row: the row's max magnitude picks e (row_exponent); every value is
+// multiplied by 2^-e (exact) and rounded to fp16.
 __global__ __launch_bounds__(256) void x16_kernel(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t K) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
@@ -471,8 +480,7 @@ __global__ __launch_bounds__(256) void x16_kernel(const uint16_t *x, uint16_t *x
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int e = 0;
-  while (e < 120 && mx * __uint_as_float((uint32_t)(127 - e) << 23) >= 32768.0f) ++e;  // mx * 2^-e
+  const int e = row_exponent(mx);
   const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
   if (threadIdx.x == 0) rowscale[m] = __uint_as_float((uint32_t)(127 + e) << 23);
   for (int i = threadIdx.x; i < nv; i += 256) {
@@ -509,8 +517,7 @@ __global__ __launch_bounds__(256) void x16_row_kernel(const uint16_t *x, uint16_
     for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[j][t])), fabsf(bf16_hi(v[j][t]))));
   }
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  int e = 0;
-  while (e < 120 && mx * __uint_as_float((uint32_t)(127 - e) << 23) >= 32768.0f) ++e;
+  const int e = row_exponent(mx);
   const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
   if (lane == 0) rowscale[m] = __uint_as_float((uint32_t)(127 + e) << 23);
 #pragma unroll

@@ -80,9 +80,10 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  *   accumulation (relative Frobenius error ~1e-6 against an fp64 product).
  * FAST: each weight is dequantized once per block tile to fp16 with a single
  *   rounding, W16 = fp16(s*q + b), and x enters as fp16 after scaling each
- *   row by a power of two 2^-e (e >= 0, the smallest keeping the row below
- *   2^15), exact for every scaled value of magnitude >= 2^-14; outputs are
- *   scaled back by 2^e and accumulated in fp32 on fp16 MFMA. The added error
+ *   row by the power of two 2^-e that brings its largest magnitude into
+ *   [2^14, 2^15), exact for every scaled value of magnitude >= 2^-14 (every
+ *   value within 2^28 of the row's largest); outputs are scaled back by 2^e
+ *   and accumulated in fp32 on fp16 MFMA. The added error
  *   is the half-ulp of fp16 on W (relative Frobenius error ~2e-4 on normal
  *   weights). Requires the TILED layout and |W| < 65504, which holds for
  *   weights quantized from fp16-range values (W lies between b and
@@ -202,9 +203,10 @@ int64_t qlinear_group_sums_ld(int64_t M);
 
 /*
  * FAST-mode activations (see ql_mode): for each row m of the bf16 [M, K]
- * input, e = the smallest integer >= 0 with max_k |x[m,k]| * 2^-e < 2^15;
- * x16[m, k] = fp16(x[m, k] * 2^-e) (round to nearest even; exact for scaled
- * magnitudes >= 2^-14) and rowscale[m] = 2^e. x16 is [M, K] fp16 (16-byte
+ * input with largest magnitude mx = max_k |x[m,k]|, e = floor(log2 mx) - 14
+ * clamped to [-126, 120] (e = 0 when mx = 0), so mx * 2^-e lies in
+ * [2^14, 2^15); x16[m, k] = fp16(x[m, k] * 2^-e) (round to nearest even;
+ * exact for scaled magnitudes >= 2^-14) and rowscale[m] = 2^e. x16 is [M, K] fp16 (16-byte
  * aligned), rowscale [M] fp32. Several projections of the same x (Q/K/V,
  * gate/up) can share one call by passing the results in ql_forward_args.
  * Returns QL_EINVAL for bad sizes or null pointers, QL_EALIGN for misaligned

@@ -228,3 +228,58 @@ def test_caller_workspace_and_stream(torch):
     with pytest.raises(ql.QLinearError) as e:
         ql.qlinear_forward_ex(x, p, s, b, 4, c.M, c.N, c.K, out, workspace=small)
     assert e.value.status == ql.QL_EWORKSPACE
+
+
+# ------------------------------------------------------------------ degenerate groups and rows
+
+def degenerate_case(M, N, K, bits, wid):
+    """Weights with the method's degenerate groups: constant groups (scale 0),
+    groups of +0/-0, groups whose range is a few f16 subnormal steps, a row of
+    exact grid points and a row spanning +-1e3; activations with an all-zero
+    row, a row of large values (2^20 range, scaled per row by the FAST
+    prepass) and a row of tiny values."""
+    w = inputs.weights(N, K, wid)
+    k = np.arange(K, dtype=np.float32)
+    w[0] = 0.25                        # constant: scale 0, W_hat = b
+    w[1] = 0.0
+    w[1, 1::2] = -0.0                  # signed zeros
+    w[2] = (k % 64) * np.float32(3e-9)    # range below the smallest normal f16 step
+    w[3] = -1 + np.float32(0.125) * (k % 16)  # exact grid points
+    w[4] = np.where(k % 2 == 0, 1e3, -1e3).astype(np.float32)
+    w[5, :64] = 7.0                    # one constant group in an otherwise normal row
+    x = inputs.activations_f32(M, K, wid)
+    x[0] = 0.0
+    x[1] *= np.float32(2.0 ** 20)
+    x[2] *= np.float32(2.0 ** -30)
+    return Case(M, N, K, bits, wid=wid, w=w, x=inputs.f32_to_bf16_bits(x))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_degenerate_groups_every_path(torch, bits):
+    c = degenerate_case(40, 96, 256, bits, wid=260 + bits)
+    ref = c.reference()
+    runs = []
+    if bits != 3:   # 3-bit runs on the tiled layout only
+        runs += [dict(path=ql.QL_PATH_GEMM), dict(path=ql.QL_PATH_SPLITK), dict(path=ql.QL_PATH_SKINNY, m=16),
+                 dict(path=ql.QL_PATH_GEMM, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)]
+    runs += [dict(path=ql.QL_PATH_SKINNY, layout=ql.QL_LAYOUT_TILED, m=16)]
+    for kw in runs:
+        m = kw.pop("m", c.M)
+        cc = c if m == c.M else Case(m, c.N, c.K, bits, wid=0, w=c.w, x=c.x[:m])
+        y = run_forward(torch, cc, **kw).cpu().numpy()
+        # acceptance bar: the exact mode's affine fold s*P + (b - 128 s)*sum(x)
+        # cancels large terms when a row of x is huge and a weight group spans
+        # +-1e3, so its fp32 rounding exceeds the design bound here
+        assert_parity(y, ref[:m], design=False, what=(ql.qlinear_last_path(), kw))
+        # the zero row of x gives exactly zero
+        assert np.all(y[0] == 0.0), ql.qlinear_last_path()
+    # FAST: against its definition (the large row is scaled by a power of two
+    # on the way to fp16, so its products keep their relative accuracy)
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
+    ref_fast = oracle.forward_fast(c.x, c.packed, c.s16, c.b16, bits, c.K)
+    assert_parity(y, ref_fast, what=ql.qlinear_last_path())   # fp32 accumulation only: design bound
+    assert np.all(y[0] == 0.0)
+    # every row of the FAST result also meets the acceptance bar row by row
+    for r in (1, 2, 3):
+        e = oracle.error_metrics(y[r:r + 1], ref[r:r + 1])
+        assert e["relF"] <= 2e-3, (r, e)
