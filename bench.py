@@ -109,7 +109,20 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
         "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
         "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
     log(f"exact mode: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
-    del out
+
+    # the plain entry point on canonical weights (EXACT numerics, library-owned workspace)
+    (pc, sc, bc), = make_weights(torch, ql, inputs, N, K, bits, WORKLOAD["wid"])
+
+    def fc():
+        ql.qlinear_forward(x_main, pc, sc, bc, bits, 64, M, N, K, out)
+
+    ms = time_calls(torch, fc, 20, 5)
+    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+    rows[f"canonical_entry_M{M}_K{K}_N{N}_q{bits}"] = {
+        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+        "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4), "note": "qlinear_forward, canonical layout"}
+    log(f"canonical qlinear_forward: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
+    del out, pc, sc, bc
 
     K, N = 4608, 27648
     for M, bits, tiled in ((1, 4, False), (1, 4, True), (8, 4, False), (8, 4, True), (1, 8, True), (1, 3, True)):

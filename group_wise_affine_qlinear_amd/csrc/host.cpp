@@ -147,9 +147,19 @@ struct TableEntry {
   int64_t m_lo, m_hi, n_lo, n_hi, k_lo, k_hi;
   int tile, splits;
 };
+// Exact-mode large-M tiles for canonical codes, from a sweep of tiles 1, 2, 3,
+// 5, 10, 11 over the DiT projection shapes on one MI355X (first match wins):
+//  - 8-bit: the 128 x 128 first-generation tile (gate/up 4608x24576: 1.80 ms
+//    against 2.30 ms for tile 10; down 12288->4608: 0.97 against 1.21 ms);
+//  - M <= 383: the 64 x 128 tile (M=256, N=K=4608: 48 us against 52 us);
+//  - larger M: the second-generation 256 x 128 tile, which stages codes and x
+//    by LDS DMA (QKV 4608x13824: 0.82 ms against 0.99 ms for tile 1; 2048^2
+//    2-bit sweep 16896x13824: 2.85 against 3.40 ms; llm_cond_proj with its
+//    8-way K split: 0.49 against 0.60 ms).
 const TableEntry kTable[] = {
-    // placeholder defaults; refined by measurement
-    {0, 17, 1LL << 40, 1, 1LL << 40, 1, 1LL << 40, 1, 0},
+    {8, 17, 1LL << 40, 1, 1LL << 40, 1, 1LL << 40, 1, 0},
+    {0, 17, 383, 1, 1LL << 40, 1, 1LL << 40, 5, 0},
+    {0, 384, 1LL << 40, 1, 1LL << 40, 1, 1LL << 40, 10, 0},
 };
 
 int choose_splits(int64_t tiles, int G) {
@@ -310,7 +320,7 @@ QL_API const char *qlinear_status_string(int status) {
     case QL_OK: return "ok";
     case QL_EINVAL: return "invalid argument (size, null pointer or K not a multiple of 64)";
     case QL_EALIGN: return "misaligned pointer (x, out and packed_q need 16-byte alignment)";
-    case QL_EUNSUPPORTED: return "unsupported (bits must be 2, 4 or 8; group 64; or forced path cannot serve shape)";
+    case QL_EUNSUPPORTED: return "unsupported (bits must be 2, 3, 4 or 8; group 64; 3-bit needs the tiled layout; or forced path cannot serve shape)";
     case QL_EWORKSPACE: return "workspace missing or too small";
     case QL_EHIP: return "HIP runtime error";
     case QL_ERANGE: return "non-finite weight or f16 overflow of scale/bias";
