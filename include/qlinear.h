@@ -276,8 +276,9 @@ int qlinear_quantize_imatrix(const float *w, const float *importance, int bits, 
                              int64_t N, int64_t K, uint32_t *packed_q, uint16_t *scales,
                              uint16_t *biases, int *status_dev, void *stream);
 
-/* Device dequantize (check path): W_hat fp32 [N, K], one rounding per value,
- * bit-identical to fp32(scale)*q + fp32(bias). */
+/* Device dequantize (check path) of canonical-layout weights: W_hat fp32
+ * [N, K], one rounding per value, bit-identical to fp32(scale)*q + fp32(bias).
+ * Tiled weights go back to the canonical layout with qlinear_unrepack first. */
 int qlinear_dequantize(const uint32_t *packed_q, const void *scales, const void *biases,
                        int bits, int group, int64_t N, int64_t K, float *w_out,
                        void *stream);
