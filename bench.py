@@ -384,8 +384,8 @@ def load_traffic(src_hash):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile", choices=["none", "step", "copy"], default="none",
@@ -428,18 +428,19 @@ def main():
 
     steps, warmup = args.steps, args.warmup
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # HIP events around each GEMM launch (the roofline's kernel duration); the
+    # prepass time is the step time minus the GEMM time. Events around the
+    # prepass too would add a further marker per step to the timed region.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
 
     def step(evs=None):
-        if evs:
-            evs[0].record(stream)
         ql.qlinear_fast_activations(x, M, K, x16, rowscale, stream=stream)
         if evs:
-            evs[1].record(stream)
+            evs[0].record(stream)
         ql.qlinear_forward_ex(x, p, s, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
                               mode=ql.QL_MODE_FAST, x16=x16, rowscale=rowscale, stream=stream)
         if evs:
-            evs[2].record(stream)
+            evs[1].record(stream)
 
     for _ in range(warmup):
         step()
@@ -455,12 +456,30 @@ def main():
         return
 
     ms_step = (t1 - t0) * 1e3 / steps
-    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    # the rest of a step: prepass, launches and the event markers
+    pre_ms = max(ms_step - gemm_ms, 0.0)
     flop = 2.0 * M * N * K
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (gemm_ms * 1e-3) / 1e12
-    log(f"step {ms_step*1e3:.1f} us (prepass {pre_ms*1e3:.1f} us, gemm {gemm_ms*1e3:.1f} us) -> {value:.1f} TFLOP/s")
+    log(f"step {ms_step*1e3:.1f} us (gemm {gemm_ms*1e3:.1f} us, prepass and the rest {pre_ms*1e3:.1f} us) -> {value:.1f} TFLOP/s")
+    # distribution of the per-step event times, and a sustained ~1 s loop for
+    # clock-throttling context (both after the timed region)
+    per_step = sorted(a[1].elapsed_time(b[1]) * 1e3 for a, b in zip(ev[:-1], ev[1:]))   # GEMM end to GEMM end
+    q = lambda f: round(per_step[min(len(per_step) - 1, int(f * len(per_step)))], 1)
+    torch.cuda.synchronize()
+    n_sus, ts0 = 0, time.perf_counter()
+    while time.perf_counter() - ts0 < 1.0:
+        for _ in range(20):
+            step()
+        n_sus += 20
+        torch.cuda.synchronize()
+    sus_ms = (time.perf_counter() - ts0) * 1e3 / n_sus
+    timing = {"step_us_p10": q(0.1), "step_us_median": q(0.5), "step_us_p90": q(0.9),
+              "sustained_1s_step_us": round(sus_ms * 1e3, 1),
+              "sustained_1s_TFLOP/s": round(flop / (sus_ms * 1e-3) / 1e12, 1), "sustained_steps": n_sus}
+    log(f"per-step p10/median/p90 {timing['step_us_p10']}/{timing['step_us_median']}/{timing['step_us_p90']} us; "
+        f"sustained 1 s: {timing['sustained_1s_step_us']} us per step")
 
     secondary = {} if args.no_secondary else secondary_rows(torch, ql, inputs, (p, s, None), x)
     src_hash = gemm_source_hash()
@@ -484,7 +503,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "fused dequant-GEMM (fp16 MFMA)", "kernel_us": round(gemm_ms * 1e3, 2),
-                     "prepass_us": round(pre_ms * 1e3, 2), "kernel_source_sha": src_hash},
+                     "rest_of_step_us": round(pre_ms * 1e3, 2), "kernel_source_sha": src_hash},
+        "timing": timing,
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:
