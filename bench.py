@@ -122,6 +122,17 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
         "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
         "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4), "note": "qlinear_forward, canonical layout"}
     log(f"canonical qlinear_forward: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
+
+    # FAST numerics straight from canonical weights (no repack)
+    def fcf():
+        ql.qlinear_forward_ex(x_main, pc, sc, bc, bits, M, N, K, out, mode=ql.QL_MODE_FAST)
+
+    ms = time_calls(torch, fcf, 20, 5)
+    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+    rows[f"canonical_fast_M{M}_K{K}_N{N}_q{bits}"] = {
+        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+        "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4), "note": "prepass + FAST GEMM reading canonical code rows"}
+    log(f"canonical FAST: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
     del out, pc, sc, bc
 
     K, N = 4608, 27648

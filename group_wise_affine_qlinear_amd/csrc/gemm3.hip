@@ -111,6 +111,37 @@ template <> struct LaneCodes<3> {
   }
 };
 
+// Canonical layout (each row one little-endian code stream): a lane's 16
+// codes 16h .. 16h+15 of its row and group are 16*BITS/8 contiguous bytes at
+// row offset g*8*BITS + 2*BITS*h; the codes are in plain order, so a pair is
+// gathered with one byte permute (4-bit, 2-bit) before the AND-OR. 8-bit
+// bytes are already in the order LaneCodes<8> reads.
+template <int BITS> struct CanonCodes;
+template <> struct CanonCodes<4> {
+  static constexpr int kWords = 2;
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    // nibbles 2p, 2p+1 of word c: byte p of w and of w >> 4, low nibbles
+    const uint32_t sel = 0x0C040C00u + 0x00010001u * (uint32_t)p;
+    return dq_pair(and_or(perm(w[c] >> 4, w[c], sel), 0x000F000Fu, 0x64006400u), s2, b2);
+  }
+};
+template <> struct CanonCodes<8> {
+  static constexpr int kWords = 4;
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return LaneCodes<8>::pair(w, c, p, s2, b2);
+  }
+};
+template <> struct CanonCodes<2> {
+  static constexpr int kWords = 1;
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    // codes 8c+2p, 8c+2p+1 at bits 16c+4p and 16c+4p+2
+    const uint32_t t = w[0] >> (16 * c + 4 * p);
+    return dq_pair(and_or(perm(t >> 2, t, 0x0C040C00u), 0x00030003u, 0x64006400u), s2, b2);
+  }
+};
+template <int BITS, bool CANON> struct CodesOf { using type = LaneCodes<BITS>; };
+template <int BITS> struct CodesOf<BITS, true> { using type = CanonCodes<BITS>; };
+
 // Chunk swizzle of an x stage: logical 16-byte chunk c of row r sits at
 // position c ^ xswz(r). With this function the 64 lanes of an MFMA fragment
 // read (16 rows, four k-blocks) spread over the banks best among the
@@ -119,11 +150,11 @@ __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Accumulates rows m0 .. m0 + 16*MI of the block tile at (m0, n0) over groups
 // [g_begin, g_end): MI = 16 for a whole tile, fewer for a row piece.
-template <int BITS, int MI>
+template <int BITS, int MI, bool CANON>
 __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages], int64_t m0,
                                                  int64_t n0, int g_begin, int g_end, f32x4 (&acc)[MI][kNI]) {
   constexpr int S = kStages;
-  using LC = LaneCodes<BITS>;
+  using LC = typename CodesOf<BITS, CANON>::type;
   constexpr int WB = 64 * BITS / 8;     // code bytes of one column per group
   constexpr int BB = 32 * WB;           // bytes of one tiled block (32 columns x 1 group)
   constexpr int kRows = 16 * MI;
@@ -168,17 +199,53 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   const int64_t nstrips = (a.N + 31) / 32;
   int64_t strip = n0 / 32 + wave;
   if (strip >= nstrips) strip = nstrips - 1;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, strip * G * BB, (int64_t)G * BB);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.sb, strip * G * 128, (int64_t)G * 128);
-  const uint32_t wo = LC::offset(r16, h), so = (uint32_t)(r16 * 4);
-  uint32_t who = 0;  // 3-bit: the lane's high-bit word
-  if constexpr (BITS == 3) who = LC::hi_offset(r16, h);
-  constexpr uint32_t kColStep = LC::offset(16, 0) - LC::offset(0, 0);  // bytes per 16 columns
+  __amdgpu_buffer_rsrc_t wr, sr, br;
+  uint32_t wo = 0, so = 0, who = 0;  // who: 3-bit, the lane's high-bit word
+  uint32_t kColStep = 0;             // tiled: bytes per 16 columns
+  uint32_t rowo[kNI] = {}, srow[kNI] = {};  // canonical: the lane's row of each column block
+  if constexpr (CANON) {
+    // one descriptor over all rows (uniform), the row in the lane offset;
+    // rows past N repeat row N-1
+    wr = make_rsrc(a.w, 0, a.N * (a.K * BITS / 8));
+    sr = make_rsrc(a.s16, 0, a.N * (int64_t)G * 2);
+    br = make_rsrc(a.b16, 0, a.N * (int64_t)G * 2);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int64_t n = min<int64_t>(strip * 32 + ni * 16 + r16, a.N - 1);
+      rowo[ni] = (uint32_t)(n * (a.K * BITS / 8)) + (uint32_t)(h * 2 * BITS);
+      srow[ni] = (uint32_t)(n * G * 2);
+    }
+  } else {
+    wr = make_rsrc(a.w, strip * G * BB, (int64_t)G * BB);
+    sr = make_rsrc(a.sb, strip * G * 128, (int64_t)G * 128);
+    br = sr;
+    wo = LaneCodes<BITS>::offset(r16, h);
+    so = (uint32_t)(r16 * 4);
+    if constexpr (BITS == 3) who = LaneCodes<BITS>::hi_offset(r16, h);
+    kColStep = LaneCodes<BITS>::offset(16, 0) - LaneCodes<BITS>::offset(0, 0);
+  }
 
-  auto load_codes = [&](uint32_t (&w)[kNI][LC::kWords], uint32_t (&sb)[kNI], int gv) {
+  auto load_codes = [&](uint32_t (&w)[kNI][LC::kWords], uint32_t (&sb)[kNI], uint32_t (&bb)[kNI], int gv) {
     const int g = __builtin_amdgcn_readfirstlane(gv);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
+      if constexpr (CANON) {
+        const uint32_t go = (uint32_t)g * (8u * BITS);
+        if constexpr (BITS == 4) {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, rowo[ni], go, 0);
+          w[ni][0] = v[0];
+          w[ni][1] = v[1];
+        } else if constexpr (BITS == 8) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, rowo[ni], go, 0);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[ni][t] = v[t];
+        } else {
+          w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, rowo[ni], go, 0);
+        }
+        sb[ni] = __builtin_amdgcn_raw_buffer_load_b16(sr, srow[ni], (uint32_t)g * 2u, 0);
+        bb[ni] = __builtin_amdgcn_raw_buffer_load_b16(br, srow[ni], (uint32_t)g * 2u, 0);
+        continue;
+      }
       if constexpr (BITS == 4) {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
         w[ni][0] = v[0];
@@ -194,6 +261,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
         w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
       }
       sb[ni] = __builtin_amdgcn_raw_buffer_load_b32(sr, so + ni * 64u, (uint32_t)g * 128u, 0);
+      bb[ni] = 0u;
     }
   };
   auto issue_x = [&](unsigned char *X, int gv) {
@@ -226,14 +294,15 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // group g.
   u32x4 bf[kNI][2];
   uint32_t cq[S - 1][kNI][LC::kWords];
-  uint32_t sq[S - 1][kNI];
+  uint32_t sq[S - 1][kNI];   // tiled: s | b << 16; canonical: s
+  uint32_t bq[S - 1][kNI];   // canonical: b (unused when tiled)
   // piece i of the B fragments from cq[0]/sq[0]: fragment (ni, c) = i / 4, word i % 4
   auto dequant_piece = [&](u32x4 (&dst)[kNI][2], bool valid, int i) {
     const int f = i >> 2, p = i & 3, ni = f >> 1, c = f & 1;
-    const uint32_t v = valid ? sq[0][ni] : 0u;
+    const uint32_t v = valid ? (CANON ? (sq[0][ni] & 0xFFFFu) | (bq[0][ni] << 16) : sq[0][ni]) : 0u;
     const h2 s2 = __builtin_bit_cast(h2, (v & 0xFFFFu) * 0x10001u);
     const h2 b2 = __builtin_bit_cast(h2, (v >> 16) * 0x10001u);
-    if constexpr (BITS == 3) {
+    if constexpr (BITS == 3 && !CANON) {
       // the first piece of a column block (i = 8 ni) runs before its other
       // pieces: in both placements below pieces run in increasing i within a
       // column block
@@ -258,7 +327,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
       if (t == kHalf) {
         dma_barrier();  // stage g+1 has landed everywhere, stage g-1 is free
         issue_x(XD, min(g + S - 1, g_end - 1));
-        load_codes(cq[S - 2], sq[S - 2], min(g + S - 1, g_end - 1));
+        load_codes(cq[S - 2], sq[S - 2], bq[S - 2], min(g + S - 1, g_end - 1));
       }
       if (t + kAhead < kSteps) read_a(X, t + kAhead);
       else read_a(XN, t + kAhead - kSteps);
@@ -283,6 +352,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
 #pragma unroll
       for (int j = 0; j + 1 < S - 1; ++j) {
         sq[j][ni] = sq[j + 1][ni];
+        bq[j][ni] = bq[j + 1][ni];
 #pragma unroll
         for (int u = 0; u < LC::kWords; ++u) cq[j][ni][u] = cq[j + 1][ni][u];
       }
@@ -298,7 +368,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // for a group past the end are clamped to the last group and its weights
   // dequantize to zero, so the accumulators never pass through a branch.
   if (g_begin < g_end) {
-    load_codes(cq[0], sq[0], g_begin);
+    load_codes(cq[0], sq[0], bq[0], g_begin);
     issue_x(xs[0], g_begin);
     issue_x(xs[1], min(g_begin + 1, g_end - 1));
   }
@@ -306,13 +376,13 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   if (g_begin < g_end) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
-    load_codes(cq[0], sq[0], min(g_begin + 1, g_end - 1));
+    load_codes(cq[0], sq[0], bq[0], min(g_begin + 1, g_end - 1));
     // stages and codes up to g_begin + S - 2 are in flight now; each group g
     // requests g + S - 1
 #pragma unroll
     for (int j = 2; j < S - 1; ++j) {
       issue_x(xs[j], min(g_begin + j, g_end - 1));
-      load_codes(cq[j - 1], sq[j - 1], min(g_begin + j, g_end - 1));
+      load_codes(cq[j - 1], sq[j - 1], bq[j - 1], min(g_begin + j, g_end - 1));
     }
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) read_a(xs[0], t);
@@ -414,7 +484,7 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
 // block takes whole tiles t = blockIdx.x, + gridDim.x, ... below dp_tiles.
 // Power-of-two row scales commute exactly with the summation, so partials
 // carry them already.
-template <int BITS, bool OUT_BF16, int PMI>
+template <int BITS, bool OUT_BF16, int PMI, bool CANON>
 __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char x0[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
@@ -435,7 +505,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
       const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
       if (m0 < a.M) {  // uniform per block
         f32x4 pacc[PMI][kNI];
-        tile_accumulate3<BITS, PMI>(a, xs, m0, n0, gb, ge, pacc);
+        tile_accumulate3<BITS, PMI, CANON>(a, xs, m0, n0, gb, ge, pacc);
         tile_store3<OUT_BF16, PMI>(a, out, m0, n0, pacc);
       }
     }
@@ -444,7 +514,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   for (int t = blockIdx.x; t < a.dp_tiles; t += gridDim.x) {
     const int tile = xcd_remap(t, a.dp_tiles);
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
-    tile_accumulate3<BITS, kMI>(a, xs, m0, n0, gb, ge, acc);
+    tile_accumulate3<BITS, kMI, CANON>(a, xs, m0, n0, gb, ge, acc);
     tile_store3<OUT_BF16, kMI>(a, out, m0, n0, acc);
   }
 }
@@ -535,23 +605,34 @@ __global__ __launch_bounds__(256) void x16_row_kernel(const uint16_t *x, uint16_
   }
 }
 
-template <int BITS, bool OUT_BF16>
+template <int BITS, bool OUT_BF16, bool CANON>
 void launch3_out(const Gemm3Args &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.grid_x, (unsigned)a.splits);
   switch (a.tail_tiles > 0 ? a.tail_mi : 0) {
-    case 2: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 2>), grid, dim3(kNT), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 4>), grid, dim3(kNT), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 8>), grid, dim3(kNT), 0, stream, a); break;
-    default: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 0>), grid, dim3(kNT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 2, CANON>), grid, dim3(kNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 4, CANON>), grid, dim3(kNT), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 8, CANON>), grid, dim3(kNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 0, CANON>), grid, dim3(kNT), 0, stream, a); break;
   }
+}
+
+template <int BITS, bool CANON>
+void launch3_layout(const Gemm3Args &a, hipStream_t stream) {
+  if (a.out_bf16 && a.splits == 1) launch3_out<BITS, true, CANON>(a, stream);
+  else launch3_out<BITS, false, CANON>(a, stream);
 }
 
 template <int BITS>
 hipError_t launch3_bits(const Gemm3Args &a, hipStream_t stream) {
   if (a.tail_tiles > 0 && a.tail_mi != 2 && a.tail_mi != 4 && a.tail_mi != 8) return hipErrorInvalidValue;
   if (a.splits < 1 || (a.splits > 1 && a.tail_tiles > 0)) return hipErrorInvalidValue;
-  if (a.out_bf16 && a.splits == 1) launch3_out<BITS, true>(a, stream);
-  else launch3_out<BITS, false>(a, stream);
+  if constexpr (BITS == 3) {
+    if (a.canon) return hipErrorInvalidValue;  // 3-bit codes run on tiled weights only
+    launch3_layout<BITS, false>(a, stream);
+  } else {
+    if (a.canon) launch3_layout<BITS, true>(a, stream);
+    else launch3_layout<BITS, false>(a, stream);
+  }
   return hipGetLastError();
 }
 

@@ -203,7 +203,8 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   if (mode != QL_MODE_EXACT && mode != QL_MODE_FAST) return QL_EINVAL;
   p->mode = mode;
   if (mode == QL_MODE_FAST) {
-    if (!tiled) return QL_EUNSUPPORTED;
+    // canonical codes: 2/4/8-bit, addressed with 32-bit byte offsets
+    if (!tiled && (bits == 3 || N * (K * bits / 8) > (int64_t)INT32_MAX)) return QL_EUNSUPPORTED;
     if (forced && forced->gen != 3) return QL_EUNSUPPORTED;
     int fs = force_split > 0 ? force_split : 0;
     if (path == QL_PATH_GEMM && force_path == QL_PATH_GEMM) fs = force_split > 0 ? force_split : 1;
@@ -280,9 +281,10 @@ int validate_forward(const ql_forward_args *a) {
   if (a->epilogue != QL_EPI_NONE && a->epilogue != QL_EPI_SWIGLU && a->epilogue != QL_EPI_GATE_RESIDUAL)
     return QL_EINVAL;
   if (a->epilogue != QL_EPI_NONE) {
-    if (a->layout != QL_LAYOUT_TILED || a->mode == QL_MODE_EXACT || a->path == QL_PATH_SKINNY ||
-        a->path == QL_PATH_SPLITK || a->split_k > 1)
+    if (a->mode == QL_MODE_EXACT || a->path == QL_PATH_SKINNY || a->path == QL_PATH_SPLITK || a->split_k > 1)
       return QL_EUNSUPPORTED;
+    // the GLU order is a tiled repack
+    if (a->epilogue == QL_EPI_SWIGLU && a->layout != QL_LAYOUT_TILED) return QL_EUNSUPPORTED;
   }
   if (a->epilogue == QL_EPI_SWIGLU && a->N % 32) return QL_EINVAL;
   if (a->epilogue == QL_EPI_GATE_RESIDUAL) {
@@ -377,7 +379,8 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   Plan p;
   // the fused epilogues run on the FAST GEMM without a K split (they need
   // finished sums), at any M
-  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, true, QL_MODE_FAST, &p)
+  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile,
+                                  a->layout == QL_LAYOUT_TILED, QL_MODE_FAST, &p)
            : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, a->layout == QL_LAYOUT_TILED,
                        a->mode, &p);
   if (st != QL_OK) return st;
@@ -420,26 +423,30 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
       rowscale = rsw;
     }
     const bool split = p.g3.splits > 1;
+    const bool canon = a->layout == QL_LAYOUT_CANONICAL;
     float *partial = reinterpret_cast<float *>(after);
     ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales),
                      split ? static_cast<void *>(partial) : a->out,
                      a->M, a->N, a->K, G, split ? 0 : out_bf16,
                      p.g3.dp_tiles, p.g3.tail_tiles, p.g3.tail_mi, p.g3.splits, p.g3.grid_x, glu ? 1 : 0,
                      gated ? a->residual : nullptr, gated ? a->gate : nullptr,
-                     gated ? (int)std::min<int64_t>(a->gate_rows, a->M) : 0};
+                     gated ? (int)std::min<int64_t>(a->gate_rows, a->M) : 0,
+                     canon ? 1 : 0, canon ? static_cast<const uint16_t *>(a->scales) : nullptr,
+                     canon ? static_cast<const uint16_t *>(a->biases) : nullptr};
+    const char *lay = canon ? "canonical" : "tiled";
     if (gated)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_gate_tiled", a->bits,
-                    p.g3.tail_tiles > 0 ? "_tail" : "");
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_gate_%s", a->bits, p.g3.tail_tiles > 0 ? "_tail" : "",
+                    lay);
     else if (glu)
       std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_swiglu_tiled", a->bits,
                     p.g3.tail_tiles > 0 ? "_tail" : "");
     else if (split)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_split%d_tiled", a->bits, p.g3.splits);
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_split%d_%s", a->bits, p.g3.splits, lay);
     else if (p.g3.tail_tiles > 0)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_tiled", a->bits, p.g3.tail_tiles,
-                    16 / p.g3.tail_mi);
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_%s", a->bits, p.g3.tail_tiles,
+                    16 / p.g3.tail_mi, lay);
     else
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tiled", a->bits);
+      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_%s", a->bits, lay);
     set_last_path(buf);
     if (ql::launch_gemm3(a->bits, g3, stream) != hipSuccess) return QL_EHIP;
     if (split && ql::launch_splitk_reduce(partial, p.g3.splits, a->M, a->N, a->out, out_bf16, stream) != hipSuccess)

@@ -61,8 +61,8 @@ Gemm2Plan gemm2_plan(int bits, int tile_id, int64_t M, int64_t N, int G, int spl
 struct Gemm3Args {
   const uint16_t *x16;    // fp16 [M, K]
   const float *rowscale;  // [M], 2^e per row
-  const uint32_t *w;      // tiled codes
-  const uint32_t *sb;     // tiled scale|bias words
+  const uint32_t *w;      // tiled codes, or canonical codes [N, K*bits/32] when canon
+  const uint32_t *sb;     // tiled scale|bias words (unused when canon)
   void *out;              // [M, N] fp32 or bf16; with splits > 1 fp32 [splits, M, N]
   int64_t M, N, K;
   int G;
@@ -76,6 +76,9 @@ struct Gemm3Args {
   const void *residual;   // non-null with gate: out = residual + gate[m / gate_rows] * y
   const float *gate;      // fp32 [ceil(M / gate_rows), N]
   int gate_rows;          // 1 .. M (callers clamp larger values to M)
+  int canon;              // 1: canonical codes with separate f16 scales and biases
+  const uint16_t *s16;    // canonical scales [N, K/64] (canon only)
+  const uint16_t *b16;    // canonical biases [N, K/64] (canon only)
 };
 struct Gemm3Plan {
   int64_t tiles;

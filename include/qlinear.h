@@ -85,9 +85,11 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  *   value within 2^28 of the row's largest); outputs are scaled back by 2^e
  *   and accumulated in fp32 on fp16 MFMA. The added error
  *   is the half-ulp of fp16 on W (relative Frobenius error ~2e-4 on normal
- *   weights). Requires the TILED layout and |W| < 65504, which holds for
- *   weights quantized from fp16-range values (W lies between b and
- *   b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x
+ *   weights). Runs on TILED weights, or on CANONICAL 2/4/8-bit weights of
+ *   fewer than 2^31 code bytes (the same kernel reading each row's code
+ *   stream; identical results, slower: strided code loads), and requires
+ *   |W| < 65504, which holds for weights quantized from fp16-range values
+ *   (W lies between b and b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x
  *   unless the caller passes it (qlinear_fast_activations, x16/rowscale),
  *   plus splits*M*N*4 bytes of fp32 partials when K is split.
  * AUTO: FAST for the large-M paths (GEMM, SPLITK) on TILED weights, EXACT
@@ -117,8 +119,8 @@ typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
  *   This is the AdaLN gate of each DiT block, taken from the timestep
  *   embedding and applied to the attention-out and MLP-down projections
  *   (Ideogram 4 paper notes, section 2.1 pipeline; Ideogram-4-IQ4_M card,
- *   Conversion section: a per-layer scale and a tanh gate). Same path rules
- *   as SWIGLU (FAST GEMM, no K split, any M, QL_LAYOUT_TILED); a missing
+ *   Conversion section: a per-layer scale and a tanh gate). Runs the FAST
+ *   GEMM without a K split at any M, on tiled or canonical weights; a missing
  *   residual or gate or gate_rows < 1 is QL_EINVAL. With K == 0 the call
  *   copies residual to out.
  */
@@ -154,10 +156,10 @@ typedef struct ql_forward_args {
   int layout;                /* ql_layout. For QL_LAYOUT_TILED, packed_q holds
                                 the tiled codes, scales the tiled scale|bias
                                 words, and biases is ignored                */
-  int mode;                  /* ql_mode; FAST needs QL_LAYOUT_TILED and a
-                                large-M path (AUTO with M > 16, GEMM or
-                                SPLITK), else QL_EUNSUPPORTED; xsum is
-                                unused in FAST                              */
+  int mode;                  /* ql_mode; FAST needs a large-M path (AUTO
+                                with M > 16, GEMM or SPLITK) and tiled or
+                                canonical 2/4/8-bit codes, else
+                                QL_EUNSUPPORTED; xsum is unused in FAST     */
   const void *x16;           /* optional, FAST only: fp16 [M, K] activations
                                 and                                         */
   const float *rowscale;     /* [M] row scales from qlinear_fast_activations

@@ -68,9 +68,8 @@ def test_fast_is_auto_choice_for_tiled_large_m(torch):
 
 
 def test_fast_rejects_unsupported_requests(torch):
-    c = Case(64, 256, 256, 4, wid=412)
-    with pytest.raises(ql.QLinearError):   # canonical layout
-        run_forward(torch, c, mode=ql.QL_MODE_FAST)
+    with pytest.raises(ql.QLinearError):   # 3-bit codes on the canonical layout
+        run_forward(torch, Case(64, 256, 256, 3, wid=412), mode=ql.QL_MODE_FAST)
     with pytest.raises(ql.QLinearError):   # a K split needs two groups at least
         run_forward(torch, Case(64, 256, 64, 4, wid=414), layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST,
                     path=ql.QL_PATH_SPLITK)
@@ -222,3 +221,36 @@ def test_fast_split_k(torch, shape, splits, bits):
                      out_dtype="bf16")
     got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, inputs.f32_to_bf16_bits(y.cpu().numpy()))
+
+
+# canonical weights: the same kernel reads each row's code stream directly, so
+# its result equals the tiled run bit for bit (same fp16 weights, same MFMA
+# order, same tail pieces and K splits)
+CANON_CASES = [(520, 390, 320, 0, 0), (300, 520, 640, 0, 0), (17, 40, 64, 0, 0), (700, 600, 384, 6, 0),
+               (300, 2304, 448, 17, 0), (64, 600, 8192, 0, 5)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("case", CANON_CASES)
+def test_fast_canonical_equals_tiled(torch, monkeypatch, case, bits):
+    M, N, K, slots, splits = case
+    if slots:
+        monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
+    c = Case(M, N, K, bits, wid=470 + bits, x_structure="outlier")
+    path = ql.QL_PATH_SPLITK if splits else ql.QL_PATH_AUTO
+    yt = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=path, split_k=splits)
+    pt = ql.qlinear_last_path()
+    yc = run_forward(torch, c, mode=ql.QL_MODE_FAST, path=path, split_k=splits)
+    pc = ql.qlinear_last_path()
+    assert pc.endswith("_canonical") and pc.replace("_canonical", "_tiled") == pt, (pc, pt)
+    assert torch.equal(yc, yt), (pc, (yc - yt).abs().max().item())
+    check_fast(yc.cpu().numpy(), c)
+
+
+def test_fast_canonical_bf16_and_auto_mode(torch):
+    c = Case(300, 260, 384, 4, wid=480)
+    y = run_forward(torch, c, mode=ql.QL_MODE_FAST).cpu().numpy()
+    yb = run_forward(torch, c, mode=ql.QL_MODE_FAST, out_dtype="bf16")
+    assert np.array_equal(yb.view(torch.int16).cpu().numpy().view(np.uint16), inputs.f32_to_bf16_bits(y))
+    run_forward(torch, c)   # AUTO on canonical weights stays exact
+    assert not ql.qlinear_last_path().startswith("gemm3"), ql.qlinear_last_path()

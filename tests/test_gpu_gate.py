@@ -137,8 +137,6 @@ def test_gate_residual_rejects_bad_requests(torch):
     res = torch.zeros_like(out)
     gate = torch.zeros((1, 256), dtype=torch.float32, device="cuda")
     kw = dict(epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=gate, gate_rows=64)
-    with pytest.raises(ql.QLinearError):   # canonical layout
-        ql.qlinear_forward_ex(x, p, s, b, 4, 64, 256, 256, out, **kw)
     with pytest.raises(ql.QLinearError):   # EXACT numerics
         ql.qlinear_forward_ex(x, tq, tsb, None, 4, 64, 256, 256, out, layout=ql.QL_LAYOUT_TILED,
                               mode=ql.QL_MODE_EXACT, **kw)
@@ -166,3 +164,19 @@ def test_gate_residual_full_size_attention_out_sampled(torch):
     cols = np.unique(np.concatenate([[0, 15, 16, 255, 256, N - 1], rng.integers(0, N, 60)]))
     blk = out.index_select(0, torch.from_numpy(rows).cuda()).index_select(1, torch.from_numpy(cols).cuda())
     check(blk.cpu().numpy(), c, res, gate, gate_rows, rows, cols)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_gate_residual_canonical_equals_tiled(torch, bits):
+    """The gated update on canonical weights runs the FAST GEMM on the row code
+    streams and equals the tiled run bit for bit."""
+    c = Case(300, 640, 384, bits, wid=598 + bits)
+    res, gate = gate_inputs(c, 100, 598)
+    x, p, s, b = c.device(torch)
+    yt = run_gate(torch, c, 100, res, gate)
+    rd = dev(torch, res)
+    ql.qlinear_forward_ex(x, p, s, b, bits, c.M, c.N, c.K, rd, epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=rd,
+                          gate=dev(torch, gate), gate_rows=100)
+    torch.cuda.synchronize()
+    assert ql.qlinear_last_path().endswith("_gate_canonical"), ql.qlinear_last_path()
+    assert torch.equal(rd, yt)
