@@ -399,8 +399,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--profile", choices=["none", "step", "copy"], default="none",
-                    help="short run for rocprofv3: 'step' = the timed step only, 'copy' = a plain copy of known size")
+    ap.add_argument("--profile", choices=["none", "step", "copy", "skinny"], default="none",
+                    help="short run for rocprofv3: 'step' = the timed step only, 'copy' = a plain copy of known size, 'skinny' = the AdaLN skinny kernel")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -418,6 +418,19 @@ def main():
         sys.exit(1)
     ql.load_library()
 
+    if args.profile == "skinny":
+        # the skinny path at the AdaLN shape, M=1, tiled 4-bit weights, 8
+        # distinct weight copies rotated so every launch streams from HBM
+        M, K, N, copies = 1, 4608, 27648, 8
+        sets = make_weights(torch, ql, inputs, N, K, 4, 40, copies, tiled=True)
+        x = torch.from_numpy(inputs.activations_bf16(M, K, 40).view("int16")).cuda()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        for i in range(16 + 64):
+            p, s, _ = sets[i % copies]
+            ql.qlinear_forward_ex(x, p, s, None, 4, M, N, K, out, layout=ql.QL_LAYOUT_TILED)
+        torch.cuda.synchronize()
+        log(f"skinny M=1 K=4608 N=27648 q4 tiled: 80 launches ({ql.qlinear_last_path()})")
+        return
     if args.profile == "copy":
         n = 256 * 1024 * 1024 // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
