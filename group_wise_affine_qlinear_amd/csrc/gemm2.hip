@@ -197,6 +197,21 @@ __device__ __forceinline__ void tile_accumulate(const GemmArgs &a, Stage<BITS, B
         const u32x4 wv = *reinterpret_cast<const u32x4 *>(S.w + off);
         bq[ni][0] = as_bf16x8(unpack8_b8(wv[0], wv[1]));
         bq[ni][1] = as_bf16x8(unpack8_b8(wv[2], wv[3]));
+      } else if constexpr (BITS == 3) {
+        // tiled only: the 2-bit block of the low bits, then the high-bit word of
+        // half h/2 (pairs 8(h%2) .. +7 of this lane, bits P and 16 + P)
+        static_assert(TILED, "3-bit codes are staged from the tiled layout");
+        const int base = (col / 32) * BB;
+        const uint32_t wv = *reinterpret_cast<const uint32_t *>(S.w + base + (h >> 1) * 256 + (col % 32) * 8 + (h & 1) * 4);
+        const uint32_t hw = *reinterpret_cast<const uint32_t *>(S.w + base + 512 + (h >> 1) * 128 + (col % 32) * 4);
+        const uint32_t hs = (hw >> (8 * (h & 1))) << 2;  // this lane's pair j at bits 2 + j and 18 + j
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 r = unpack8_b2_pair(wv, c);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r[q] = and_or(hs >> (4 * c + q), 0x00040004u, r[q]);
+          bq[ni][c] = as_bf16x8(r);
+        }
       } else {
         const int off = TILED ? (col / 32) * BB + (h >> 1) * 256 + (col % 32) * 8 + (h & 1) * 4 : col * WB + h * 4;
         const uint32_t wv = *reinterpret_cast<const uint32_t *>(S.w + off);
@@ -426,14 +441,19 @@ hipError_t launch2_any(int bits, bool tiled, const GemmArgs &a, hipStream_t stre
   if (bits == 4) return tiled ? launch2<4, true, BM, BN, WMW, WNW>(a, stream) : launch2<4, false, BM, BN, WMW, WNW>(a, stream);
   if (bits == 8) return tiled ? launch2<8, true, BM, BN, WMW, WNW>(a, stream) : launch2<8, false, BM, BN, WMW, WNW>(a, stream);
   if (bits == 2) return tiled ? launch2<2, true, BM, BN, WMW, WNW>(a, stream) : launch2<2, false, BM, BN, WMW, WNW>(a, stream);
+  if (bits == 3) return tiled ? launch2<3, true, BM, BN, WMW, WNW>(a, stream) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 size_t gemm2_lds_bytes(int bits, int id) {
-  if (id == 10) return 2 * (bits == 4 ? sizeof(Stage<4, 256, 128>) : bits == 8 ? sizeof(Stage<8, 256, 128>) : sizeof(Stage<2, 256, 128>));
-  if (id == 11) return 2 * (bits == 4 ? sizeof(Stage<4, 128, 128>) : bits == 8 ? sizeof(Stage<8, 128, 128>) : sizeof(Stage<2, 128, 128>));
+  if (id == 10)
+    return 2 * (bits == 4 ? sizeof(Stage<4, 256, 128>) : bits == 8 ? sizeof(Stage<8, 256, 128>)
+                : bits == 3 ? sizeof(Stage<3, 256, 128>) : sizeof(Stage<2, 256, 128>));
+  if (id == 11)
+    return 2 * (bits == 4 ? sizeof(Stage<4, 128, 128>) : bits == 8 ? sizeof(Stage<8, 128, 128>)
+                : bits == 3 ? sizeof(Stage<3, 128, 128>) : sizeof(Stage<2, 128, 128>));
   return 0;
 }
 

@@ -184,8 +184,6 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
     if (envp > 0) path = envp;
   }
   if (path == QL_PATH_AUTO) path = (M <= kMaxSkinnyM) ? QL_PATH_SKINNY : QL_PATH_GEMM;
-  // 3-bit codes run on tiled weights only: the skinny kernel and the FAST GEMM
-  if (bits == 3 && !tiled) return QL_EUNSUPPORTED;
   if (path == QL_PATH_SKINNY) {
     if (M > kMaxSkinnyM || mode == QL_MODE_FAST) return QL_EUNSUPPORTED;
     p->path = QL_PATH_SKINNY;
@@ -223,7 +221,9 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
     return QL_OK;
   }
   if (forced && forced->gen == 3) return QL_EUNSUPPORTED;
-  if (bits == 3) return QL_EUNSUPPORTED;  // no exact-mode GEMM for 3-bit codes
+  // 3-bit codes: the GEMMs read the tiled layout (canonical 3-bit weights are
+  // repacked into the workspace first), second-generation tiles only
+  if (bits == 3 && (!tiled || (forced && forced->gen != 2))) return QL_EUNSUPPORTED;
   int splits = 0;
   if (tile <= 0) {
     for (const TableEntry &e : kTable) {
@@ -262,6 +262,13 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
     if (p->g2.sk_partial_bytes > p->ws_partial) p->ws_partial = p->g2.sk_partial_bytes;
   }
   return QL_OK;
+}
+
+// Workspace bytes of a tiled copy of canonical weights (codes, then scale|bias
+// words, each 256-byte aligned).
+size_t repack_ws_bytes(int bits, int64_t N, int64_t K) {
+  const int64_t n32 = round_up(N, 32);
+  return (size_t)round_up(n32 * K * bits / 32 * 4, 256) + (size_t)round_up(n32 * (K / kGroup) * 4, 256);
 }
 
 size_t plan_ws(const Plan &p) {
@@ -349,6 +356,16 @@ QL_API size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K)
   if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, false, QL_MODE_AUTO, &pc) == QL_OK) need = plan_ws(pc);
   if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, QL_MODE_AUTO, &pt) == QL_OK && plan_ws(pt) > need)
     need = plan_ws(pt);
+  if (bits == 3) {
+    // canonical 3-bit weights on a GEMM path: the plan on the tiled copy plus the copy
+    for (int mode : {QL_MODE_EXACT, QL_MODE_FAST}) {
+      Plan p3;
+      if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, mode, &p3) == QL_OK && p3.path != QL_PATH_SKINNY) {
+        const size_t n3 = (size_t)round_up((int64_t)plan_ws(p3), 256) + repack_ws_bytes(bits, N, K);
+        if (n3 > need) need = n3;
+      }
+    }
+  }
   return need;
 }
 
@@ -377,13 +394,21 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                                                                                                         : QL_EHIP;
   }
   Plan p;
+  // canonical 3-bit weights: the GEMM paths run on a tiled copy made in the
+  // workspace by the repack kernel (one pass over the weights per call); the
+  // skinny kernel reads the canonical stream directly
+  const bool canon3 = a->bits == 3 && a->layout == QL_LAYOUT_CANONICAL;
+  const bool plan_tiled = a->layout == QL_LAYOUT_TILED || canon3;
   // the fused epilogues run on the FAST GEMM without a K split (they need
   // finished sums), at any M
-  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile,
-                                  a->layout == QL_LAYOUT_TILED, QL_MODE_FAST, &p)
-           : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, a->layout == QL_LAYOUT_TILED,
-                       a->mode, &p);
+  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, plan_tiled, QL_MODE_FAST, &p)
+                      : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, plan_tiled, a->mode, &p);
   if (st != QL_OK) return st;
+  // AUTO keeps EXACT numerics on canonical weights (the plan above saw a tiled layout)
+  if (canon3 && a->mode == QL_MODE_AUTO && !(glu || gated) && p.path != QL_PATH_SKINNY && p.mode == QL_MODE_FAST) {
+    st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, true, QL_MODE_EXACT, &p);
+    if (st != QL_OK) return st;
+  }
   const int G = (int)(a->K / kGroup);
   const int out_bf16 = a->out_dtype == QL_OUT_BF16;
   char buf[160];
@@ -399,9 +424,10 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     set_last_path(buf);
     return ql::launch_skinny(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;
   }
-  if (a->layout == QL_LAYOUT_TILED && !ql::gemm_tile_supports_tiled(p.tile)) return QL_EUNSUPPORTED;
+  if (plan_tiled && !ql::gemm_tile_supports_tiled(p.tile)) return QL_EUNSUPPORTED;
   if (p.mode == QL_MODE_FAST && a->x16) p.ws_x16 = 0;  // caller's fp16 activations
-  const size_t need = plan_ws(p);
+  const size_t plan_need = (size_t)round_up((int64_t)plan_ws(p), 256);
+  const size_t need = plan_need + (canon3 ? repack_ws_bytes(a->bits, a->N, a->K) : 0);
   void *ws = a->workspace;
   if (ws) {
     if (a->workspace_bytes < need) return QL_EWORKSPACE;
@@ -409,6 +435,21 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   } else {
     st = get_owned_workspace(need, &ws);
     if (st != QL_OK) return st;
+  }
+  ql_forward_args tiled_args;
+  if (canon3) {
+    uint32_t *tq = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + plan_need);
+    uint32_t *tsb = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(tq) +
+                                                 round_up((int64_t)qlinear_tiled_words(3, a->N, a->K) * 4, 256));
+    if (ql::launch_repack(3, a->packed_q, static_cast<const uint16_t *>(a->scales),
+                          static_cast<const uint16_t *>(a->biases), a->N, a->K, 0, tq, tsb, stream) != hipSuccess)
+      return QL_EHIP;
+    tiled_args = *a;
+    tiled_args.packed_q = tq;
+    tiled_args.scales = tsb;
+    tiled_args.biases = nullptr;
+    tiled_args.layout = QL_LAYOUT_TILED;
+    a = &tiled_args;
   }
   if (p.mode == QL_MODE_FAST) {
     const uint16_t *x16 = static_cast<const uint16_t *>(a->x16);

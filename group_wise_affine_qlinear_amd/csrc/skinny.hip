@@ -42,10 +42,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne_s(float f) {
 // high-bit word.
 template <int BITS> struct LaneCodes { u32x4 v[BITS == 8 ? 2 : 1]; };
 
-template <int BITS>
+template <int BITS, bool TILED>
 __device__ __forceinline__ LaneCodes<BITS> load_codes(const uint32_t *p, const uint32_t *p2) {
   LaneCodes<BITS> c;
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 3 && !TILED) {
+    // canonical 3-bit: the lane's 32 codes are 12 bytes of the row's stream
+    c.v[0] = u32x4{p[0], p[1], p[2], 0u};
+  } else if constexpr (BITS == 4) {
     c.v[0] = *reinterpret_cast<const u32x4 *>(p);
   } else if constexpr (BITS == 8) {
     c.v[0] = *reinterpret_cast<const u32x4 *>(p);
@@ -65,7 +68,20 @@ template <int BITS, bool TILED>
 __device__ __forceinline__ bf16x8 codes_step(const LaneCodes<BITS> &c, int t) {
   if constexpr (BITS == 4) return as_bf16x8(TILED ? unpack8_b4_pair(c.v[0][t]) : unpack8_b4(c.v[0][t]));
   else if constexpr (BITS == 8) return as_bf16x8(unpack8_b8(c.v[t >> 1][(t & 1) * 2], c.v[t >> 1][(t & 1) * 2 + 1]));
-  else if constexpr (BITS == 3) {
+  else if constexpr (BITS == 3 && !TILED) {
+    // canonical: codes 8t .. 8t+7 are stream bits 24t .. 24t+23 of the lane's
+    // three words; code 2p of the step at bit 6p, code 2p+1 at bit 6p+3
+    const int b = 24 * t, j = b >> 5;
+    const uint32_t hi = j + 1 < 3 ? c.v[0][j + 1] : 0u;
+    const uint32_t v24 = __builtin_amdgcn_alignbit(hi, c.v[0][j], (uint32_t)(b & 31));
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a0 = v24 >> (6 * p);
+      r[p] = (a0 & 7u) | ((a0 << 13) & 0x00070000u) | 0x43004300u;
+    }
+    return as_bf16x8(r);
+  } else if constexpr (BITS == 3) {
     // low two bits as 2-bit codes, then the high bit of pair P = 4t + p (bits
     // P and 16 + P of the high-bit word) into bits 2 and 18: 128 + q
     u32x4 r = unpack8_b2_pair(c.v[0][t >> 1], t & 1);
@@ -136,14 +152,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     off2 = BITS == 3 ? 128 - l : 256;  // 3-bit: high-bit word 128 + l of the block
   } else {
     gstride = 2 * BITS;
-    wbase = a.w + n * (a.K * BITS / 32) + (BITS == 8 ? 8 * h : (BITS == 4 ? 4 * h : 2 * h));
+    wbase = a.w + n * (a.K * BITS / 32) + (BITS == 8 ? 8 * h : (BITS == 4 ? 4 * h : (BITS == 3 ? 3 * h : 2 * h)));
     sbbase = nullptr;
     off2 = 4;
   }
   auto load_g = [&](int g) {
     Slot<BITS, TILED> sl;
     const uint32_t *p = wbase + (int64_t)g * gstride;
-    sl.c = load_codes<BITS>(p, p + off2);
+    sl.c = load_codes<BITS, TILED>(p, p + off2);
     if constexpr (TILED) sl.sb = sbbase[32 * g];
     else sl.sb = 0;
     return sl;
@@ -407,7 +423,7 @@ hipError_t launch_skinny(int bits, const SkinnyArgs &a, hipStream_t stream) {
   if (bits == 4) return launch_bits<4>(a, stream);
   if (bits == 8) return launch_bits<8>(a, stream);
   if (bits == 2) return launch_bits<2>(a, stream);
-  if (bits == 3) return a.tiled ? launch_layout<3, true>(a, stream) : hipErrorInvalidValue;
+  if (bits == 3) return launch_bits<3>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -13,8 +13,11 @@
  * "Versions": group-wise affine Q4/Q8, group size 64, packed). 3-bit codes
  * serve the mixed-precision packs of the IQ4_M card (3-bit DiT bulk with
  * 8-bit modulation and conditioning; sections "Against the pack this
- * replaces" and "Conversion"); they run on the TILED layout only (the
- * skinny kernel and the FAST GEMM), other requests are QL_EUNSUPPORTED.
+ * replaces" and "Conversion"). They run on every path: the skinny kernel
+ * reads either layout; the GEMMs (exact and FAST) read the TILED layout, so
+ * a GEMM call on canonical 3-bit weights first repacks them into the
+ * workspace (one extra pass over the weights per call; repack once at load
+ * with qlinear_repack to avoid it).
  *
  * Conventions for every entry point:
  *  - Pointers whose name ends in _host are host memory; all others are device
@@ -53,8 +56,7 @@ typedef enum {
   QL_EINVAL = -1,        /* bad size, null pointer, K not a multiple of 64  */
   QL_EALIGN = -2,        /* x / out / packed_q not 16-byte aligned            */
   QL_EUNSUPPORTED = -3,  /* bits not in {2,3,4,8}, group != 64, forced path
-                            that cannot serve the shape, 3-bit codes on a
-                            path other than the tiled skinny / FAST GEMM     */
+                            that cannot serve the shape                      */
   QL_EWORKSPACE = -4,    /* caller workspace missing or too small             */
   QL_EHIP = -5,          /* a HIP runtime call or kernel launch failed        */
   QL_ERANGE = -6         /* non-finite weight, or f16 overflow of scale/bias  */
@@ -157,9 +159,10 @@ typedef struct ql_forward_args {
                                 the tiled codes, scales the tiled scale|bias
                                 words, and biases is ignored                */
   int mode;                  /* ql_mode; FAST needs a large-M path (AUTO
-                                with M > 16, GEMM or SPLITK) and tiled or
-                                canonical 2/4/8-bit codes, else
-                                QL_EUNSUPPORTED; xsum is unused in FAST     */
+                                with M > 16, GEMM or SPLITK), else
+                                QL_EUNSUPPORTED; canonical 3-bit codes run
+                                on a tiled copy in the workspace; xsum is
+                                unused in FAST                              */
   const void *x16;           /* optional, FAST only: fp16 [M, K] activations
                                 and                                         */
   const float *rowscale;     /* [M] row scales from qlinear_fast_activations
@@ -217,7 +220,8 @@ int64_t qlinear_group_sums_ld(int64_t M);
 int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x16, float *rowscale, void *stream);
 
 /* Bytes of device workspace qlinear_forward_ex needs for this shape under
- * automatic dispatch (an upper bound over all paths and splits it may pick). */
+ * automatic dispatch (an upper bound over all paths and splits it may pick;
+ * for 3-bit it includes the tiled copy of canonical weights). */
 size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K);
 
 /* Number of uint32 words of packed codes for an [N, K] weight: N*K*bits/32. */

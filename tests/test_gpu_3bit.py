@@ -1,9 +1,10 @@
 """GPU tests specific to 3-bit codes (the parity tests of the shared paths run
-3-bit alongside 2/4/8-bit): which requests the library serves, and the two
-3-bit paths at full size on sampled outputs.
+3-bit alongside 2/4/8-bit): which requests the library serves, and the 3-bit
+paths at full size on sampled outputs.
 
-3-bit codes run on the tiled layout only: the FAST GEMM for M > 16 and the
-skinny kernel for M <= 16. The canonical layout and the exact-mode GEMM
+3-bit codes run everywhere: the skinny kernel reads either layout; the GEMMs
+(exact and FAST) read the tiled layout, and canonical 3-bit weights on a GEMM
+path are repacked into the workspace first. Forced first-generation tiles
 return QL_EUNSUPPORTED."""
 import numpy as np
 import pytest
@@ -12,8 +13,8 @@ import oracle
 from group_wise_affine_qlinear_amd import inputs
 from group_wise_affine_qlinear_amd import qlinear as ql
 
-from gpu_helpers import (MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, Case, dev, run_forward,
-                         torch_or_skip)
+from gpu_helpers import (MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, Case, assert_parity, dev,
+                         run_forward, torch_or_skip)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,24 +29,26 @@ def torch():
     return t
 
 
-def test_3bit_requests_served_and_rejected(torch):
+def test_3bit_requests_and_paths(torch):
     c = Case(64, 256, 256, 3, wid=620)
-    with pytest.raises(ql.QLinearError) as e:      # canonical layout
-        run_forward(torch, c)
-    assert e.value.status == ql.QL_EUNSUPPORTED
-    with pytest.raises(ql.QLinearError) as e:      # canonical entry point
-        run_forward(torch, c, via_ex=False)
-    assert e.value.status == ql.QL_EUNSUPPORTED
-    with pytest.raises(ql.QLinearError) as e:      # exact-mode GEMM
-        run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
-    assert e.value.status == ql.QL_EUNSUPPORTED
-    run_forward(torch, c, layout=ql.QL_LAYOUT_TILED)
+    ref = c.reference()
+    y = run_forward(torch, c, via_ex=False)              # canonical entry point: exact, via a tiled copy
+    assert ql.qlinear_last_path().startswith("gemm2") and ql.qlinear_last_path().endswith("_tiled")
+    assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
+    y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
+    assert ql.qlinear_last_path().startswith("gemm2"), ql.qlinear_last_path()
+    assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
+    yt = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED)
     assert ql.qlinear_last_path().startswith("gemm3_f16_256x256_b3"), ql.qlinear_last_path()
+    yc = run_forward(torch, c, mode=ql.QL_MODE_FAST)       # FAST on canonical 3-bit: the same kernel on the copy
+    assert torch.equal(yc, yt)
     c8 = Case(8, 256, 256, 3, wid=621)
-    run_forward(torch, c8, layout=ql.QL_LAYOUT_TILED)
-    assert ql.qlinear_last_path() == "skinny_b3_m8_tiled"
-    with pytest.raises(ql.QLinearError) as e:      # skinny M on the canonical layout
-        run_forward(torch, c8)
+    for layout in (ql.QL_LAYOUT_TILED, ql.QL_LAYOUT_CANONICAL):
+        y8 = run_forward(torch, c8, layout=layout)
+        assert ql.qlinear_last_path().startswith("skinny_b3_m8"), ql.qlinear_last_path()
+        assert_parity(y8.cpu().numpy(), c8.reference(), what=ql.qlinear_last_path())
+    with pytest.raises(ql.QLinearError) as e:      # first-generation tiles take no 3-bit codes
+        run_forward(torch, c, path=ql.QL_PATH_GEMM, tile=1)
     assert e.value.status == ql.QL_EUNSUPPORTED
 
 
@@ -101,3 +104,13 @@ def test_3bit_full_size_sampled(torch, name):
     else:
         assert path.startswith("skinny_b3"), path
         assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, (path, e)
+    # the canonical entry point on the same 3-bit weights (exact numerics)
+    pc = torch.from_numpy(packed.view(np.int32)).cuda()
+    sc = torch.from_numpy(s16.view(np.int16)).cuda()
+    bc = torch.from_numpy(b16.view(np.int16)).cuda()
+    out.fill_(float("nan"))
+    ql.qlinear_forward(xd, pc, sc, bc, 3, 64, M, N, K, out)
+    torch.cuda.synchronize()
+    blk = out.index_select(0, ri).index_select(1, ci).cpu().numpy()
+    e = oracle.error_metrics(blk, ref)
+    assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, (ql.qlinear_last_path(), e)

@@ -68,8 +68,6 @@ def test_fast_is_auto_choice_for_tiled_large_m(torch):
 
 
 def test_fast_rejects_unsupported_requests(torch):
-    with pytest.raises(ql.QLinearError):   # 3-bit codes on the canonical layout
-        run_forward(torch, Case(64, 256, 256, 3, wid=412), mode=ql.QL_MODE_FAST)
     with pytest.raises(ql.QLinearError):   # a K split needs two groups at least
         run_forward(torch, Case(64, 256, 64, 4, wid=414), layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST,
                     path=ql.QL_PATH_SPLITK)

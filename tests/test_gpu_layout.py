@@ -121,7 +121,7 @@ GEMM2_SHAPES = [(520, 390, 320), (200, 300, 1024), (129, 129, 192), (17, 40, 64)
 
 @pytest.mark.parametrize("layout", [ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED])
 @pytest.mark.parametrize("tile", [10, 11])
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape", GEMM2_SHAPES)
 def test_gemm2_parity(torch, shape, bits, tile, layout):
     M, N, K = shape

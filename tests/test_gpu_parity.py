@@ -101,7 +101,7 @@ def test_tiny_config_all_paths(torch):
 GEMM_SHAPES = [(200, 300, 1024), (129, 129, 192), (17, 40, 64), (384, 256, 512)]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
 def test_gemm_ragged(torch, bits, shape):
     M, N, K = shape
@@ -122,7 +122,7 @@ def test_gemm_every_tile(torch, tile):
     assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("M", [1, 3, 8, 9, 16])
 def test_skinny_ragged(torch, bits, M):
     c = Case(M, 300, 1536, bits, wid=230 + M)
@@ -258,11 +258,9 @@ def degenerate_case(M, N, K, bits, wid):
 def test_degenerate_groups_every_path(torch, bits):
     c = degenerate_case(40, 96, 256, bits, wid=260 + bits)
     ref = c.reference()
-    runs = []
-    if bits != 3:   # 3-bit runs on the tiled layout only
-        runs += [dict(path=ql.QL_PATH_GEMM), dict(path=ql.QL_PATH_SPLITK), dict(path=ql.QL_PATH_SKINNY, m=16),
-                 dict(path=ql.QL_PATH_GEMM, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)]
-    runs += [dict(path=ql.QL_PATH_SKINNY, layout=ql.QL_LAYOUT_TILED, m=16)]
+    runs = [dict(path=ql.QL_PATH_GEMM), dict(path=ql.QL_PATH_SPLITK), dict(path=ql.QL_PATH_SKINNY, m=16),
+            dict(path=ql.QL_PATH_GEMM, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT),
+            dict(path=ql.QL_PATH_SKINNY, layout=ql.QL_LAYOUT_TILED, m=16)]
     for kw in runs:
         m = kw.pop("m", c.M)
         cc = c if m == c.M else Case(m, c.N, c.K, bits, wid=0, w=c.w, x=c.x[:m])

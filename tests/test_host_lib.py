@@ -176,8 +176,8 @@ def _args(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=3), ql.QL_EUNSUPPORTED),              # 3-bit: tiled layout only
-    (dict(bits=3, layout=1, mode=1, M=64), ql.QL_EUNSUPPORTED),   # no exact-mode 3-bit GEMM
+    (dict(bits=3, M=64, tile=1), ql.QL_EUNSUPPORTED),   # 3-bit codes: second-generation tiles only
+    (dict(bits=3, M=64, tile=5), ql.QL_EUNSUPPORTED),
     (dict(bits=5), ql.QL_EUNSUPPORTED),
     (dict(bits=16), ql.QL_EUNSUPPORTED),
     (dict(group=32), ql.QL_EUNSUPPORTED),
