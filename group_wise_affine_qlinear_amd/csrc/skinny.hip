@@ -387,9 +387,12 @@ hipError_t launch_mr(const SkinnyArgs &a, hipStream_t stream) {
   const size_t red = (size_t)kStrips * kKSplit * MR * 64 * 4;
   size_t lds = xbytes + (size_t)chunk * MPAD * 4 + (size_t)chunk * sbytes;
   if (lds < red) lds = red;
-  // codes kept in flight per lane: deeper for narrow codes and few output rows,
-  // bounded so the kernel stays within 128 VGPRs (4 waves per SIMD, 16 per CU)
-  constexpr int RING = BITS == 8 ? (MR == 8 ? 2 : 4) : (MR == 8 ? 3 : (MR == 4 ? 5 : (MR == 2 ? 6 : 8)));
+  // groups of codes kept in flight per lane, bounded so the kernel stays
+  // within 128 VGPRs (4 waves per SIMD, 16 per CU). Measured at N = 27648,
+  // K = 4608: 4 is the best depth at one or two rows for every code width
+  // (4-bit, one row: 16 us against 19 us with 8, since the kernel's 3456
+  // waves already keep ~14 MB of loads in flight); 5 at up to 8 rows, 3 at 16.
+  constexpr int RING = BITS == 8 ? (MR == 8 ? 2 : 4) : (MR == 8 ? 3 : (MR == 4 ? 5 : 4));
   auto kern = skinny_kernel<BITS, MR, RING, TILED, XB, SB>;
   static bool attr_set = false;
   if (!attr_set) {
