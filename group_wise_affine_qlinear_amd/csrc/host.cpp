@@ -177,6 +177,7 @@ constexpr int kFastTile = 20;
 
 int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int force_split,
               int force_tile, bool tiled, int mode, Plan *p) {
+  *p = Plan{};  // a re-plan into the same Plan keeps no field of the previous one
   const int G = (int)(K / kGroup);
   int path = force_path;
   if (path == QL_PATH_AUTO) {
@@ -271,6 +272,23 @@ size_t repack_ws_bytes(int bits, int64_t N, int64_t K) {
   return (size_t)round_up(n32 * K * bits / 32 * 4, 256) + (size_t)round_up(n32 * (K / kGroup) * 4, 256);
 }
 
+// Canonical weights on a GEMM path may run on a tiled copy that the repack
+// kernel writes into the workspace (one read and one write of the weights per
+// call). 3-bit codes always take it: the GEMMs read 3-bit codes in the tiled
+// layout only. The other widths take it under automatic dispatch (no forced
+// path, tile or split) from kCopyMinM rows on, where the GEMMs on tiled codes
+// save more than the copy costs. Measured, exact GEMM at K = N = 4608, 4-bit:
+// M = 256 43 us direct against 40 + 10 us through the copy, M = 512 73 against
+// 61 + 11, M = 4096 341 against 255 + 11. The skinny kernel reads canonical
+// codes directly.
+constexpr int64_t kCopyMinM = 512;
+
+bool copy_route(const ql_forward_args *a) {
+  if (a->layout != QL_LAYOUT_CANONICAL) return false;
+  if (a->bits == 3) return true;
+  return a->M >= kCopyMinM && a->path == QL_PATH_AUTO && a->tile == 0 && a->split_k == 0;
+}
+
 size_t plan_ws(const Plan &p) {
   if (p.path == QL_PATH_SKINNY) return 0;
   return (size_t)round_up((int64_t)p.ws_xsum, 256) + (size_t)round_up((int64_t)p.ws_x16, 256) + p.ws_partial;
@@ -356,13 +374,13 @@ QL_API size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K)
   if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, false, QL_MODE_AUTO, &pc) == QL_OK) need = plan_ws(pc);
   if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, QL_MODE_AUTO, &pt) == QL_OK && plan_ws(pt) > need)
     need = plan_ws(pt);
-  if (bits == 3) {
-    // canonical 3-bit weights on a GEMM path: the plan on the tiled copy plus the copy
+  if (bits == 3 || M >= kCopyMinM) {
+    // canonical weights on a GEMM path through a tiled copy: the plan on the copy plus the copy
     for (int mode : {QL_MODE_EXACT, QL_MODE_FAST}) {
-      Plan p3;
-      if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, mode, &p3) == QL_OK && p3.path != QL_PATH_SKINNY) {
-        const size_t n3 = (size_t)round_up((int64_t)plan_ws(p3), 256) + repack_ws_bytes(bits, N, K);
-        if (n3 > need) need = n3;
+      Plan pc3;
+      if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, mode, &pc3) == QL_OK && pc3.path != QL_PATH_SKINNY) {
+        const size_t nc = (size_t)round_up((int64_t)plan_ws(pc3), 256) + repack_ws_bytes(bits, N, K);
+        if (nc > need) need = nc;
       }
     }
   }
@@ -394,18 +412,16 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                                                                                                         : QL_EHIP;
   }
   Plan p;
-  // canonical 3-bit weights: the GEMM paths run on a tiled copy made in the
-  // workspace by the repack kernel (one pass over the weights per call); the
-  // skinny kernel reads the canonical stream directly
-  const bool canon3 = a->bits == 3 && a->layout == QL_LAYOUT_CANONICAL;
-  const bool plan_tiled = a->layout == QL_LAYOUT_TILED || canon3;
+  // canonical weights through a tiled copy (see copy_route)
+  const bool copy = copy_route(a);
+  const bool plan_tiled = a->layout == QL_LAYOUT_TILED || copy;
   // the fused epilogues run on the FAST GEMM without a K split (they need
   // finished sums), at any M
   st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, plan_tiled, QL_MODE_FAST, &p)
                       : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, plan_tiled, a->mode, &p);
   if (st != QL_OK) return st;
   // AUTO keeps EXACT numerics on canonical weights (the plan above saw a tiled layout)
-  if (canon3 && a->mode == QL_MODE_AUTO && !(glu || gated) && p.path != QL_PATH_SKINNY && p.mode == QL_MODE_FAST) {
+  if (copy && a->mode == QL_MODE_AUTO && !(glu || gated) && p.path != QL_PATH_SKINNY && p.mode == QL_MODE_FAST) {
     st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, true, QL_MODE_EXACT, &p);
     if (st != QL_OK) return st;
   }
@@ -427,7 +443,7 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   if (plan_tiled && !ql::gemm_tile_supports_tiled(p.tile)) return QL_EUNSUPPORTED;
   if (p.mode == QL_MODE_FAST && a->x16) p.ws_x16 = 0;  // caller's fp16 activations
   const size_t plan_need = (size_t)round_up((int64_t)plan_ws(p), 256);
-  const size_t need = plan_need + (canon3 ? repack_ws_bytes(a->bits, a->N, a->K) : 0);
+  const size_t need = plan_need + (copy ? repack_ws_bytes(a->bits, a->N, a->K) : 0);
   void *ws = a->workspace;
   if (ws) {
     if (a->workspace_bytes < need) return QL_EWORKSPACE;
@@ -437,11 +453,11 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     if (st != QL_OK) return st;
   }
   ql_forward_args tiled_args;
-  if (canon3) {
+  if (copy) {
     uint32_t *tq = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + plan_need);
     uint32_t *tsb = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(tq) +
-                                                 round_up((int64_t)qlinear_tiled_words(3, a->N, a->K) * 4, 256));
-    if (ql::launch_repack(3, a->packed_q, static_cast<const uint16_t *>(a->scales),
+                                                 round_up((int64_t)qlinear_tiled_words(a->bits, a->N, a->K) * 4, 256));
+    if (ql::launch_repack(a->bits, a->packed_q, static_cast<const uint16_t *>(a->scales),
                           static_cast<const uint16_t *>(a->biases), a->N, a->K, 0, tq, tsb, stream) != hipSuccess)
       return QL_EHIP;
     tiled_args = *a;
@@ -474,7 +490,7 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                      gated ? (int)std::min<int64_t>(a->gate_rows, a->M) : 0,
                      canon ? 1 : 0, canon ? static_cast<const uint16_t *>(a->scales) : nullptr,
                      canon ? static_cast<const uint16_t *>(a->biases) : nullptr};
-    const char *lay = canon ? "canonical" : "tiled";
+    const char *lay = canon ? "canonical" : (copy ? "tiled_copy" : "tiled");
     if (gated)
       std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_gate_%s", a->bits, p.g3.tail_tiles > 0 ? "_tail" : "",
                     lay);
@@ -528,10 +544,10 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   const ql::TileInfo *ti = ql::gemm_tile(p.tile);
   if (p.g2.sk_tiles > 0)
     std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_tail%dx%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
-                  p.g2.sk_tiles, p.g2.sk_pieces, tiled ? "tiled" : "canonical");
+                  p.g2.sk_tiles, p.g2.sk_pieces, tiled ? (copy ? "tiled_copy" : "tiled") : "canonical");
   else
     std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
-                  tiled ? "tiled" : "canonical");
+                  tiled ? (copy ? "tiled_copy" : "tiled") : "canonical");
   set_last_path(buf);
   const hipError_t le = (ti && ti->gen == 2) ? ql::launch_gemm2(a->bits, p.tile, tiled, g, stream)
                                              : ql::launch_gemm(a->bits, p.tile, g, stream);

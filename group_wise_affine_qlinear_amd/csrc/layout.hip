@@ -103,10 +103,15 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32
   if constexpr (BITS == 3) {
     // low-bit plane words at [h][col][t] (2-bit block), high-bit plane at 128 + [h][col]
     if (TO_TILED) {
+      // 8-byte loads: a group's 24 bytes start on an 8-byte boundary
       uint32_t cw[WPG];
-      const uint32_t *crow = src + n * (K * 3 / 32) + g * WPG;
+      const u32x2 *crow = reinterpret_cast<const u32x2 *>(src + n * (K * 3 / 32) + g * WPG);
 #pragma unroll
-      for (int j = 0; j < WPG; ++j) cw[j] = real ? crow[j] : 0u;
+      for (int j = 0; j < WPG / 2; ++j) {
+        const u32x2 v = real ? crow[j] : u32x2{0u, 0u};
+        cw[2 * j] = v[0];
+        cw[2 * j + 1] = v[1];
+      }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         uint32_t hi = 0;
@@ -155,13 +160,25 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint32_t *src, uint32
     return;
   }
   if (TO_TILED) {
-    const uint32_t *crow = src + n * (K * BITS / 32) + g * WPG;
+    // 16-byte loads of the column's WPG words (rows and groups start on
+    // 16-byte boundaries: packed_q is 16-byte aligned and a row holds a whole
+    // number of groups) and 16- (2-bit: 8-) byte stores of consecutive tiled
+    // words, so one store instruction of 32 lanes fills 512 contiguous bytes
+    const u32x4 *crow = reinterpret_cast<const u32x4 *>(src + n * (K * BITS / 32) + g * WPG);
 #pragma unroll
-    for (int j = 0; j < WPG; ++j) {
-      uint32_t w = real ? crow[j] : 0u;
-      if (BITS == 4) w = to_pair_b4(w);
-      if (BITS == 2) w = to_pair_b2(w);
-      blk[tpos(j)] = w;
+    for (int v = 0; v < WPG / 4; ++v) {
+      u32x4 w = real ? crow[v] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (BITS == 4) w[e] = to_pair_b4(w[e]);
+        if (BITS == 2) w[e] = to_pair_b2(w[e]);
+      }
+      if constexpr (BITS == 2) {
+        *reinterpret_cast<u32x2 *>(blk + tpos(4 * v)) = u32x2{w[0], w[1]};
+        *reinterpret_cast<u32x2 *>(blk + tpos(4 * v + 2)) = u32x2{w[2], w[3]};
+      } else {
+        *reinterpret_cast<u32x4 *>(blk + tpos(4 * v)) = w;
+      }
     }
     sb[(strip * G + g) * 32 + col] = real ? ((uint32_t)s[n * G + g] | ((uint32_t)b[n * G + g] << 16)) : 0u;
   } else {

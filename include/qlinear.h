@@ -72,6 +72,14 @@ typedef enum { QL_OUT_F32 = 0, QL_OUT_BF16 = 1 } ql_out_dtype;
  * 768 B: the low two bits as a 2-bit block, then a plane of high bits) and
  * the scale and bias become one uint32 (s | b << 16) per row and group, so a
  * wave's loads cover whole cache lines.
+ * Under automatic dispatch (path, tile and split_k all 0), a call on
+ * CANONICAL weights with M >= 512 first writes a TILED copy of them into the
+ * workspace and runs the GEMM on it (the copy is one pass over the weights;
+ * from 512 rows on the GEMM on tiled codes saves more than that). 3-bit
+ * weights take this copy on every GEMM path. Results equal those of the same
+ * call on weights repacked with qlinear_repack, bit for bit; the path name
+ * reported by qlinear_last_path then ends in "_tiled_copy". Forced paths,
+ * tiles or splits (2/4/8-bit) run the kernels on the canonical code rows.
  */
 typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
 
@@ -177,8 +185,9 @@ typedef struct ql_forward_args {
 /*
  * y = x @ W_hat^T with W_hat defined above, fp32 out, default stream.
  * M, N >= 0 (0 is a no-op), K >= 0 and a multiple of 64 (K == 0 writes zeros),
- * group must be 64. Scratch memory the kernels need (per-group row sums of x
- * and split-K partials) comes from a library-owned per-device buffer that is
+ * group must be 64. Scratch memory the kernels need (per-group row sums of x,
+ * split-K partials and, from 512 rows on, the tiled copy of the weights
+ * described at ql_layout) comes from a library-owned per-device buffer that is
  * grown on demand with hipMalloc; calls on one device therefore must not
  * overlap in time (use qlinear_forward_ex with your own workspace for that).
  */
@@ -221,7 +230,8 @@ int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x16, flo
 
 /* Bytes of device workspace qlinear_forward_ex needs for this shape under
  * automatic dispatch (an upper bound over all paths and splits it may pick;
- * for 3-bit it includes the tiled copy of canonical weights). */
+ * for 3-bit codes, and for M >= 512, it includes the tiled copy of canonical
+ * weights). */
 size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K);
 
 /* Number of uint32 words of packed codes for an [N, K] weight: N*K*bits/32. */

@@ -33,7 +33,7 @@ def test_3bit_requests_and_paths(torch):
     c = Case(64, 256, 256, 3, wid=620)
     ref = c.reference()
     y = run_forward(torch, c, via_ex=False)              # canonical entry point: exact, via a tiled copy
-    assert ql.qlinear_last_path().startswith("gemm2") and ql.qlinear_last_path().endswith("_tiled")
+    assert ql.qlinear_last_path().startswith("gemm2") and ql.qlinear_last_path().endswith("_tiled_copy")
     assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
     y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
     assert ql.qlinear_last_path().startswith("gemm2"), ql.qlinear_last_path()

@@ -235,7 +235,9 @@ def test_fast_canonical_equals_tiled(torch, monkeypatch, case, bits):
     if slots:
         monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
     c = Case(M, N, K, bits, wid=470 + bits, x_structure="outlier")
-    path = ql.QL_PATH_SPLITK if splits else ql.QL_PATH_AUTO
+    # from 512 rows on, automatic dispatch runs canonical weights on a tiled
+    # copy: force the GEMM path there to test the kernel on the code rows
+    path = ql.QL_PATH_SPLITK if splits else (ql.QL_PATH_GEMM if M >= 512 else ql.QL_PATH_AUTO)
     yt = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=path, split_k=splits)
     pt = ql.qlinear_last_path()
     yc = run_forward(torch, c, mode=ql.QL_MODE_FAST, path=path, split_k=splits)

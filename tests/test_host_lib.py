@@ -242,3 +242,43 @@ def test_tiled_sizes_and_repack_validation(lib):
     assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_EALIGN
     a = _args(layout=5)
     assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_EINVAL
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+def _forward_status(lib, M, N, K, bits, ws_bytes, mode, layout):
+    # placeholder device addresses: a call is either rejected before any HIP
+    # call (QL_EWORKSPACE here) or fails at its first launch (no device)
+    a = ql.ql_forward_args()
+    a.x, a.packed_q, a.scales, a.biases, a.out, a.workspace = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+    a.bits, a.group, a.M, a.N, a.K = bits, 64, M, N, K
+    a.workspace_bytes, a.mode, a.layout = ws_bytes, mode, layout
+    return lib.qlinear_forward_ex(ctypes.byref(a), None)
+
+
+@pytest.mark.skipif(_gpu_present(), reason="passes placeholder device addresses: runs only where no GPU is visible")
+@pytest.mark.parametrize("shape", [(17, 40, 64), (300, 2304, 448), (511, 256, 256), (512, 256, 256),
+                                   (640, 300, 448), (4096, 4608, 4608), (512, 4608, 53248)])
+def test_workspace_bytes_bounds_every_mode_and_layout(lib, shape):
+    """qlinear_workspace_bytes is enough for every mode and layout under
+    automatic dispatch (canonical weights from 512 rows on and 3-bit weights
+    add their tiled copy), and one byte less than a call's need is refused."""
+    M, N, K = shape
+    for bits in (2, 3, 4, 8):
+        wb = lib.qlinear_workspace_bytes(bits, M, N, K)
+        for mode in (ql.QL_MODE_AUTO, ql.QL_MODE_EXACT, ql.QL_MODE_FAST):
+            for layout in (ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED):
+                lo, hi = 0, wb + 1
+                while lo < hi:   # smallest size not refused for lack of workspace
+                    mid = (lo + hi) // 2
+                    if _forward_status(lib, M, N, K, bits, mid, mode, layout) == ql.QL_EWORKSPACE:
+                        lo = mid + 1
+                    else:
+                        hi = mid
+                assert lo <= wb, (bits, mode, layout, lo, wb)
+                if layout == ql.QL_LAYOUT_CANONICAL and M >= 512 and mode == ql.QL_MODE_AUTO:
+                    copy = ql.qlinear_tiled_words(bits, N, K) * 4 + ql.qlinear_tiled_sb_words(N, K) * 4
+                    assert lo >= copy, (bits, lo, copy)
