@@ -120,19 +120,29 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     tf = 2 * M * N * K / (ms * 1e-3) / 1e12
     rows[f"canonical_entry_M{M}_K{K}_N{N}_q{bits}"] = {
         "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-        "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4), "note": "qlinear_forward, canonical layout"}
+        "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4),
+        "note": "qlinear_forward, canonical layout (automatic dispatch: tiled copy in the workspace, exact GEMM)"}
     log(f"canonical qlinear_forward: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
 
-    # FAST numerics straight from canonical weights (no repack)
-    def fcf():
-        ql.qlinear_forward_ex(x_main, pc, sc, bc, bits, M, N, K, out, mode=ql.QL_MODE_FAST)
+    # the same weights with the kernels forced onto the canonical code rows, and FAST numerics
+    variants = (
+        ("canonical_exact_direct", {"path": ql.QL_PATH_GEMM}, PEAK_BF16_TFLOPS,
+         "exact GEMM reading the canonical code rows (forced GEMM path, no copy)"),
+        ("canonical_fast", {"mode": ql.QL_MODE_FAST}, PEAK_F16_TFLOPS,
+         "prepass + FAST GEMM, automatic dispatch (tiled copy in the workspace)"),
+        ("canonical_fast_direct", {"mode": ql.QL_MODE_FAST, "path": ql.QL_PATH_GEMM}, PEAK_F16_TFLOPS,
+         "prepass + FAST GEMM reading the canonical code rows (forced GEMM path, no copy)"),
+    )
+    for name, kw, peak, note in variants:
+        def fv(kw=kw):
+            ql.qlinear_forward_ex(x_main, pc, sc, bc, bits, M, N, K, out, **kw)
 
-    ms = time_calls(torch, fcf, 20, 5)
-    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-    rows[f"canonical_fast_M{M}_K{K}_N{N}_q{bits}"] = {
-        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-        "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4), "note": "prepass + FAST GEMM reading canonical code rows"}
-    log(f"canonical FAST: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
+        ms = time_calls(torch, fv, 20, 5)
+        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+        rows[f"{name}_M{M}_K{K}_N{N}_q{bits}"] = {
+            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+            "frac_mfma": round(tf / peak, 4), "note": note}
+        log(f"{name}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
     del out, pc, sc, bc
 
     K, N = 4608, 27648
