@@ -326,6 +326,9 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
       const int c = t / MI, mi = t % MI;
       if (t == kHalf) {
         dma_barrier();  // stage g+1 has landed everywhere, stage g-1 is free
+        // the second half runs at raised wave priority (back to normal at the
+        // end of the group): 1-1.5 % faster on the large shapes, measured
+        __builtin_amdgcn_s_setprio(1);
         issue_x(XD, min(g + S - 1, g_end - 1));
         load_codes(cq[S - 2], sq[S - 2], bq[S - 2], min(g + S - 1, g_end - 1));
       }
@@ -345,6 +348,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
       bf[ni][0] = bn[ni][0];
