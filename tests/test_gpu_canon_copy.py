@@ -9,6 +9,7 @@ exact bound against the oracle. Forced paths, tiles and splits keep the
 kernels on the canonical code rows."""
 import pytest
 
+from group_wise_affine_qlinear_amd import inputs
 from group_wise_affine_qlinear_amd import qlinear as ql
 
 from gpu_helpers import Case, assert_parity, run_forward, torch_or_skip
@@ -73,3 +74,28 @@ def test_copy_route_workspace(torch):
     with pytest.raises(ql.QLinearError) as e:
         ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, workspace=ws[:4096])
     assert e.value.status == ql.QL_EWORKSPACE
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_copy_route_gate_residual_in_place(torch, out_dtype):
+    """The fused gated update on canonical weights at M >= 512 runs on the copy
+    and equals the same update on caller-repacked weights, bit for bit."""
+    M, N, K, bits = 600, 520, 384, 4
+    c = Case(M, N, K, bits, wid=740)
+    x, p, s, b = c.device(torch)
+    tq, tsb = ql.qlinear_repack(p, s, b, bits, 64, N, K)
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    res0 = torch.from_numpy(inputs.residual_stream(M, N, 741)).cuda().to(dt)
+    gate = torch.from_numpy(inputs.adaln_gate(3, N, 741)).cuda()
+    yc = res0.clone()
+    ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, yc, epilogue=ql.QL_EPI_GATE_RESIDUAL,
+                          residual=yc, gate=gate, gate_rows=200)
+    torch.cuda.synchronize()
+    pc = ql.qlinear_last_path()
+    assert pc.endswith("_gate_tiled_copy"), pc
+    yt = res0.clone()
+    ql.qlinear_forward_ex(x, tq, tsb, None, bits, M, N, K, yt, layout=ql.QL_LAYOUT_TILED,
+                          epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=yt, gate=gate, gate_rows=200)
+    torch.cuda.synchronize()
+    assert ql.qlinear_last_path() == pc[:-len("_copy")], (ql.qlinear_last_path(), pc)
+    assert torch.equal(yc, yt)

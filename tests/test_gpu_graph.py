@@ -46,6 +46,7 @@ def test_graph_replays_match_eager(torch):
     y_res = torch.empty((M, N), dtype=torch.float32, device="cuda")
     y_exact = torch.empty((M, N), dtype=torch.float32, device="cuda")
     y_skinny = torch.empty((8, N), dtype=torch.float32, device="cuda")
+    y_copy = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
     def sequence():
         ql.qlinear_fast_activations(x, M, K, x16, rs)
@@ -59,8 +60,10 @@ def test_graph_replays_match_eager(torch):
         ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_exact, path=ql.QL_PATH_SPLITK, split_k=3,
                               workspace=ws[1])
         ql.qlinear_forward_ex(xs, p, s, b, bits, 8, N, K, y_skinny, workspace=ws[2])
+        # canonical weights at M >= 512: repack into the workspace, then the GEMM on the copy
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_copy, workspace=ws[0])
 
-    outs = (y_fast, y_glu, y_res, y_exact, y_skinny)
+    outs = (y_fast, y_glu, y_res, y_exact, y_skinny, y_copy)
     y_res.copy_(res0)
     sequence()
     torch.cuda.synchronize()
