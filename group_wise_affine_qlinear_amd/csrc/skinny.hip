@@ -114,7 +114,7 @@ template <int BITS, bool TILED> struct Slot {
   uint32_t sb;            // tiled: s | b << 16 ; unused for canonical
 };
 
-template <int BITS, int MR, int kRing, bool TILED, int XB, int SB>
+template <int BITS, int MR, int kRing, bool TILED, int XB, int SB, int kBatch>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void skinny_kernel(SkinnyArgs a, int chunk_groups) {
   constexpr int MPAD = MR <= 4 ? 8 : 16;  // row stride of the per-group row-sum table
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -321,10 +321,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int u = 0; u < kRing; ++u) {
           // consume the slot, then refill the same registers: a new load never
           // overlaps the old value, so the ring needs no register copies
-          // (a copy of a load in flight would force a wait for it)
+          // (a copy of a load in flight would force a wait for it). Slots are
+          // refilled kBatch at a time, back to back: on canonical rows the
+          // loads of kBatch consecutive groups then share their cache lines
+          // while the lines are still in the vector cache.
           process(g + u, ring[u]);
           __builtin_amdgcn_sched_barrier(0);
-          ring[u] = load_g(min(g + u + kRing, glast));
+          if (u % kBatch == kBatch - 1) {
+#pragma unroll
+            for (int v = u + 1 - kBatch; v <= u; ++v) ring[v] = load_g(min(g + v + kRing, glast));
+          }
         }
       }
 #pragma unroll
@@ -392,8 +398,18 @@ hipError_t launch_mr(const SkinnyArgs &a, hipStream_t stream) {
   // K = 4608: 4 is the best depth at one or two rows for every code width
   // (4-bit, one row: 16 us against 19 us with 8, since the kernel's 3456
   // waves already keep ~14 MB of loads in flight); 5 at up to 8 rows, 3 at 16.
-  constexpr int RING = BITS == 8 ? (MR == 8 ? 2 : 4) : (MR == 8 ? 3 : (MR == 4 ? 5 : 4));
-  auto kern = skinny_kernel<BITS, MR, RING, TILED, XB, SB>;
+  constexpr int RING_T = BITS == 8 ? (MR == 8 ? 2 : 4) : (MR == 8 ? 3 : (MR == 4 ? 5 : 4));
+  // canonical rows at one or two output rows: refill in batches of groups
+  // that share 128-byte lines (3/4-bit: four groups, 8-bit: two), with a
+  // deeper ring at one row so a batch is in flight while the other is
+  // consumed. Measured at N = 27648, K = 4608, one row: 4-bit 24.4 -> 22.3 us,
+  // 3-bit 24.6 -> 22.9, 8-bit 34.1 -> 33.1; 2-bit (16-byte groups) was
+  // slower batched and keeps single refills.
+  constexpr bool kBatched = !TILED && MR <= 2 && BITS != 2;
+  constexpr int BATCH = !kBatched ? 1 : (MR == 1 ? (BITS == 8 ? 2 : 4) : 2);
+  constexpr int RING = (kBatched && MR == 1 && BITS != 8) ? 8 : RING_T;
+  static_assert(RING % BATCH == 0, "the ring refills whole batches");
+  auto kern = skinny_kernel<BITS, MR, RING, TILED, XB, SB, BATCH>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
