@@ -22,7 +22,9 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +77,24 @@ def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1, tiled=False):
         raise RuntimeError("quantizer reported a range error")
     del w
     return sets
+
+
+def smi_snapshot():
+    """Socket power and clocks from amd-smi (context only; None where the tool
+    or a field is unavailable)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout[r.stdout.index("{"):])
+        g = d["gpu_data"][0]
+        clocks = g["clock"]
+        gfx = [v["clk"]["value"] for k, v in clocks.items()
+               if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        return {"socket_power_W": g["power"]["socket_power"]["value"],
+                "gfx_clk_MHz_mean": round(sum(gfx) / len(gfx)) if gfx else None,
+                "mem_clk_MHz": clocks["mem_0"]["clk"]["value"]}
+    except Exception:
+        return None
 
 
 def time_calls(torch, fn, iters, warmup):
@@ -368,6 +388,29 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
             "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "weight_copies_rotated": copies}
         log(f"llm_cond_proj {lname}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
         del sets
+    del x, out
+
+    # one GPU's share under two-way tensor parallelism at 1024x1024 (M = 4608):
+    # column shards (QKV, gate/up: N halved, no exchange) and row shards
+    # (attention-out, down: K halved, fp32 partial y for an all-reduce that is
+    # not run here)
+    M = 4608
+    for name, K, N in (("qkv_col_shard", 4608, 6912), ("gateup_col_shard", 4608, 12288),
+                       ("attn_out_row_shard", 2304, 4608), ("down_row_shard", 6144, 4608)):
+        (p, s, _), = make_weights(torch, ql, inputs, N, K, 4, 8, tiled=True)
+        x = torch.from_numpy(inputs.activations_bf16(M, K, 8).view("int16")).cuda()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+        def fs():
+            ql.qlinear_forward_ex(x, p, s, None, 4, M, N, K, out, layout=ql.QL_LAYOUT_TILED)
+
+        ms = time_calls(torch, fs, 20, 5)
+        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+        rows[f"tp2_{name}_M{M}_K{K}_N{N}_q4"] = {
+            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+            "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4), "note": "prepass + FAST GEMM on one GPU's shard"}
+        log(f"tp2 {name}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
+        del p, s, x, out
     return rows
 
 
@@ -452,6 +495,10 @@ def main():
         return
 
     M, K, N, bits = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"], WORKLOAD["bits"]
+    # amd-smi only in the plain run (a profiler's preload would reach the child)
+    smi = {"before_setup": smi_snapshot() if args.profile == "none" else None,
+           "note": "single amd-smi metric readings, which lag a load of about a second; the engine clock "
+                   "during the GEMM (GRBM_GUI_ACTIVE over the traced duration) is in the pipeline profile"}
     log(f"setup {WORKLOAD['name']}")
     (p, s, _), = make_weights(torch, ql, inputs, N, K, bits, WORKLOAD["wid"], tiled=True)
     x = torch.from_numpy(inputs.activations_bf16(M, K, WORKLOAD["wid"]).view("int16")).cuda()
@@ -502,13 +549,18 @@ def main():
     per_step = sorted(a[1].elapsed_time(b[1]) * 1e3 for a, b in zip(ev[:-1], ev[1:]))   # GEMM end to GEMM end
     q = lambda f: round(per_step[min(len(per_step) - 1, int(f * len(per_step)))], 1)
     torch.cuda.synchronize()
+    # amd-smi sampled from a side thread while the sustained loop runs; the
+    # loop lasts at least 1 s and until the sample has returned
+    sampler = threading.Thread(target=lambda: smi.__setitem__("during_sustained_loop", smi_snapshot()))
     n_sus, ts0 = 0, time.perf_counter()
-    while time.perf_counter() - ts0 < 1.0:
+    sampler.start()
+    while time.perf_counter() - ts0 < 1.0 or (sampler.is_alive() and time.perf_counter() - ts0 < 30.0):
         for _ in range(20):
             step()
         n_sus += 20
         torch.cuda.synchronize()
     sus_ms = (time.perf_counter() - ts0) * 1e3 / n_sus
+    sampler.join()
     timing = {"step_us_p10": q(0.1), "step_us_median": q(0.5), "step_us_p90": q(0.9),
               "sustained_1s_step_us": round(sus_ms * 1e3, 1),
               "sustained_1s_TFLOP/s": round(flop / (sus_ms * 1e-3) / 1e12, 1), "sustained_steps": n_sus}
@@ -539,6 +591,7 @@ def main():
                      "kernel": "fused dequant-GEMM (fp16 MFMA)", "kernel_us": round(gemm_ms * 1e3, 2),
                      "rest_of_step_us": round(pre_ms * 1e3, 2), "kernel_source_sha": src_hash},
         "timing": timing,
+        "smi": smi,
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:
