@@ -97,13 +97,16 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  *   is the half-ulp of fp16 on W (relative Frobenius error ~2e-4 on normal
  *   weights). Runs on TILED weights, or on CANONICAL 2/4/8-bit weights of
  *   fewer than 2^31 code bytes (the same kernel reading each row's code
- *   stream; identical results, slower: strided code loads), and requires
+ *   stream; identical results, slower: strided code loads; under automatic
+ *   dispatch with M >= 512 canonical weights run on a tiled copy, see
+ *   ql_layout), and requires
  *   |W| < 65504, which holds for weights quantized from fp16-range values
  *   (W lies between b and b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x
  *   unless the caller passes it (qlinear_fast_activations, x16/rowscale),
  *   plus splits*M*N*4 bytes of fp32 partials when K is split.
  * AUTO: FAST for the large-M paths (GEMM, SPLITK) on TILED weights, EXACT
- *   otherwise. The skinny (M <= 16) path is always EXACT.
+ *   otherwise (also when CANONICAL weights run on a tiled copy). The skinny
+ *   (M <= 16) path is always EXACT.
  */
 typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
 
