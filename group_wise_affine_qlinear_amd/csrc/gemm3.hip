@@ -405,12 +405,14 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 }
 
 // Stores rows m0 .. m0 + 16*MI of a tile, times the row scales, into out
-// ([M, N] fp32 or bf16). With GLU-ordered weights subtile ni = 0 of a wave
+// ([M, N] fp32 or bf16). The row scales come from LDS (rs_lds[m - m0], staged
+// by the caller): a global load among the stores would wait for every store
+// before it, since one counter tracks both, which cost ~6 % of the kernel. With GLU-ordered weights subtile ni = 0 of a wave
 // holds gate outputs and ni = 1 the up outputs of the same 16 columns
 // f = 16*strip + r16 of the [M, N/2] result, which gets silu(gate) * up.
 template <bool OUT_BF16, int MI>
 __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64_t m0, int64_t n0,
-                                            const f32x4 (&acc)[MI][kNI]) {
+                                            const f32x4 (&acc)[MI][kNI], const float *rs_lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,7 +428,7 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
       for (int i = 0; i < 4; ++i) {
         const int64_t m = row0 + mi * 16 + i;
         if (m >= a.M) continue;
-        const float rs = a.rowscale[m];
+        const float rs = rs_lds[m - m0];
         const float v = swiglu(acc[mi][0][i] * rs, acc[mi][1][i] * rs);
         if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * F + f] = f32_to_bf16_rne3(v);
         else reinterpret_cast<float *>(out)[m * F + f] = v;
@@ -445,7 +447,7 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
       for (int i = 0; i < 4; ++i) {
         const int64_t m = row0 + mi * 16 + i;
         if (!full && m >= a.M) continue;
-        const float rs = a.rowscale[m];
+        const float rs = rs_lds[m - m0];
         const float *grow = a.gate + (int64_t)((uint32_t)m / (uint32_t)a.gate_rows) * a.N;
 #pragma unroll
         for (int ni = 0; ni < kNI; ++ni) {
@@ -469,7 +471,7 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
     for (int i = 0; i < 4; ++i) {
       const int64_t m = row0 + mi * 16 + i;
       if (!full && m >= a.M) continue;
-      const float rs = a.rowscale[m];
+      const float rs = rs_lds[m - m0];
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni) {
         const int64_t n = col0 + ni * 16;
@@ -493,7 +495,19 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char x0[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x2[kXStage];
+  __shared__ __attribute__((aligned(16))) float rs_lds[kBM];
   unsigned char *const xs[kStages] = {x0, x1, x2};
+  // the row scales of a tile's rows: requested at the tile's start (one value
+  // per thread), written to LDS once the K loop has ended (its last barrier
+  // also ends every wave's reads of the previous tile's scales)
+  auto tile_rs = [&](int64_t m0, int rows) -> float {
+    const int64_t m = m0 + threadIdx.x;
+    return (int)threadIdx.x < rows && m < a.M ? a.rowscale[m] : 0.f;
+  };
+  auto stage_rs = [&](float v, int rows) {
+    if ((int)threadIdx.x < rows) rs_lds[threadIdx.x] = v;
+    __syncthreads();
+  };
   const int tiles_n = (int)((a.N + kBN - 1) / kBN);
   const int split = blockIdx.y;
   const int gps = (a.G + a.splits - 1) / a.splits;
@@ -509,8 +523,10 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
       const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
       if (m0 < a.M) {  // uniform per block
         f32x4 pacc[PMI][kNI];
+        const float rs = tile_rs(m0, 16 * PMI);
         tile_accumulate3<BITS, PMI, CANON>(a, xs, m0, n0, gb, ge, pacc);
-        tile_store3<OUT_BF16, PMI>(a, out, m0, n0, pacc);
+        stage_rs(rs, 16 * PMI);
+        tile_store3<OUT_BF16, PMI>(a, out, m0, n0, pacc, rs_lds);
       }
     }
   }
@@ -518,8 +534,10 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   for (int t = blockIdx.x; t < a.dp_tiles; t += gridDim.x) {
     const int tile = xcd_remap(t, a.dp_tiles);
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
+    const float rs = tile_rs(m0, kBM);
     tile_accumulate3<BITS, kMI, CANON>(a, xs, m0, n0, gb, ge, acc);
-    tile_store3<OUT_BF16, kMI>(a, out, m0, n0, acc);
+    stage_rs(rs, kBM);
+    tile_store3<OUT_BF16, kMI>(a, out, m0, n0, acc, rs_lds);
   }
 }
 
