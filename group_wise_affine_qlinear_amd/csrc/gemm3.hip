@@ -440,29 +440,47 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
   if (a.gate) {
     // gated residual update: out = residual + gate[m / gate_rows] * y, one
     // fused multiply-add in fp32; each element is read and written by the
-    // same lane, so residual may be out itself
+    // same lane, so residual may be out itself. Residual and gate values are
+    // read for two subtile rows at a time before their stores, so a load
+    // waits behind earlier stores once per pair of subtile rows
+    constexpr int CH = MI < 2 ? MI : 2;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mc = 0; mc < MI; mc += CH) {
+      float rv[CH][4][kNI], gv[CH][4][kNI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = row0 + mi * 16 + i;
-        if (!full && m >= a.M) continue;
-        const float rs = rs_lds[m - m0];
-        const float *grow = a.gate + (int64_t)((uint32_t)m / (uint32_t)a.gate_rows) * a.N;
+      for (int c = 0; c < CH; ++c)
 #pragma unroll
-        for (int ni = 0; ni < kNI; ++ni) {
-          const int64_t n = col0 + ni * 16;
-          if (!full && n >= a.N) continue;
-          const float v = acc[mi][ni][i] * rs;
-          if constexpr (OUT_BF16) {
-            const float r = bf16_lo(reinterpret_cast<const uint16_t *>(a.residual)[m * a.N + n]);
-            reinterpret_cast<uint16_t *>(out)[m * a.N + n] = f32_to_bf16_rne3(__builtin_fmaf(grow[n], v, r));
-          } else {
-            const float r = reinterpret_cast<const float *>(a.residual)[m * a.N + n];
-            reinterpret_cast<float *>(out)[m * a.N + n] = __builtin_fmaf(grow[n], v, r);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + (mc + c) * 16 + i;
+          const float *grow = a.gate + (int64_t)((uint32_t)m / (uint32_t)a.gate_rows) * a.N;
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni) {
+            const int64_t n = col0 + ni * 16;
+            const bool ok = full || (m < a.M && n < a.N);
+            if constexpr (OUT_BF16)
+              rv[c][i][ni] = ok ? bf16_lo(reinterpret_cast<const uint16_t *>(a.residual)[m * a.N + n]) : 0.f;
+            else
+              rv[c][i][ni] = ok ? reinterpret_cast<const float *>(a.residual)[m * a.N + n] : 0.f;
+            gv[c][i][ni] = ok ? grow[n] : 0.f;
           }
         }
-      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + (mc + c) * 16 + i;
+          if (!full && m >= a.M) continue;
+          const float rs = rs_lds[m - m0];
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni) {
+            const int64_t n = col0 + ni * 16;
+            if (!full && n >= a.N) continue;
+            const float y = __builtin_fmaf(gv[c][i][ni], acc[mc + c][ni][i] * rs, rv[c][i][ni]);
+            if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * a.N + n] = f32_to_bf16_rne3(y);
+            else reinterpret_cast<float *>(out)[m * a.N + n] = y;
+          }
+        }
+    }
     return;
   }
 #pragma unroll
