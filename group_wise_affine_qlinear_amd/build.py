@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlinear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["host.cpp", "gemm.hip", "gemm2.hip", "gemm3.hip", "skinny.hip", "misc.hip", "layout.hip"]
+SOURCES = ["gemm3.hip", "gemm4.hip", "gemm2.hip", "host.cpp", "gemm.hip", "skinny.hip", "misc.hip", "layout.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -55,7 +55,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

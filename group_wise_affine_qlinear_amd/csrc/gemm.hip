@@ -318,13 +318,10 @@ template <int BITS, int BM, int BN, int WMW, int WNW>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t stream) {
   using S = Smem<BITS, BM, BN>;
   auto kern = gemm_kernel<BITS, BM, BN, WMW, WNW>;
-  static bool attr_set = false;  // benign race: setting the same attribute twice is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (cheap; the library keeps no per-device state)
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
+  if (e != hipSuccess) return e;
   const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
   dim3 grid(tiles, a.splits);
   hipLaunchKernelGGL(kern, grid, dim3(64 * WMW * WNW), S::total, stream, a);
@@ -345,6 +342,7 @@ const TileInfo kTiles[] = {
     {10, 256, 128, 2, 2, "gemm2_256x128_w2x2", 2},
     {11, 128, 128, 1, 2, "gemm2_128x128_w1x2", 2},
     {20, 256, 256, 2, 4, "gemm3_f16_256x256_w2x4", 3},
+    {30, 256, 256, 1, 8, "gemm4_bf16x2_256x256_w1x8", 4},
 };
 
 }  // namespace

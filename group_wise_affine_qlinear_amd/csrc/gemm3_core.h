@@ -1,0 +1,880 @@
+// Large-M dequant-GEMM on 256 x 256 block tiles, shared by two numerics:
+//
+// FAST (gemm3.hip): every weight is dequantized once per block tile and group
+// to fp16 with one rounding,
+//     W16[n,k] = fp16( (s[n,g]*q[n,k] + b[n,g]) * 2^-c[n] )  (one rounding, packed
+//                                                           fp16 fused multiply-add)
+// and x enters as fp16 from a prepass that scales each row by the power of
+// two 2^-e bringing its largest magnitude into [2^14, 2^15), so the
+// conversion from bf16 is exact for every value within 2^28 of the row's
+// largest (scaled magnitude >= 2^-14). Outputs are multiplied back by 2^e
+// (row) and 2^c (column). c[n] is 0 unless the column's weights could reach
+// the fp16 limit: each tile first scans its columns' scale and bias words
+// for the bound max(|b|, |b + (2^bits-1)*s|) over its K range and, where
+// that bound is >= 65504, takes c = floor(log2 bound) - 14, so every
+// weight of any finite f16 scale and bias stays finite in fp16. fp16 keeps
+// 11 significant bits where bf16 keeps 8, so the only rounding beyond fp32
+// accumulation is the half-ulp (2^-11 relative) of W16: relative Frobenius
+// error ~2e-4 on the pages' shapes, against 1.7e-3 for weights rounded to
+// bf16.
+//
+// SPLIT (gemm4.hip): bf16 x straight from the caller (no prepass). Each
+// weight is dequantized in fp32 exactly as the affine format defines it,
+// W = s*q + b (one rounding: s*q is exact), and split into two bf16 terms
+// hi = bf16(W), lo = bf16(W - hi) (both round to nearest even; W - hi is
+// exact), so |W - hi - lo| <= 2^-16 |W|. Both terms go through the bf16
+// MFMA against the same x fragment, accumulating in fp32: twice the matrix
+// work of FAST, no activation prepass, no scratch memory and no range
+// condition on x or W (bf16 has the fp32 exponent range). Relative
+// Frobenius error ~1e-5.
+//
+// Kernel. Block tile 256 x 256 with eight waves side by side, each owning all
+// 256 rows and one 32-column strip (16 x 2 subtiles of 16 x 16 x 32 MFMAs,
+// 128 fp32 accumulators). A wave's strip is exactly one block of the tiled
+// weight layout, so each lane loads its own codes (8 bytes per column-half for
+// 4-bit) and dequantizes them straight into B fragments: every weight is
+// dequantized once per tile and weights never pass through LDS. x (fp16 or
+// bf16) moves by LDS DMA into a ring of three 32 KB stages (rows of 128
+// bytes, 16-byte chunks XOR-swizzled by row, see xswz), issued 1.5 groups
+// ahead of its use; one barrier per group, in the middle of the group's
+// MFMAs, so the waves of a SIMD never idle at a group edge.
+//
+// Grid. One block per CU runs whole tiles (t, t + gridDim.x, ...). When the
+// tile count is a little past a multiple of the CU count, the last tiles are
+// cut along M into pieces of 32, 64 or 128 rows (same code, fewer 16-row
+// subtiles per wave) that run first, so every CU does the same work and no
+// partial sums are needed. When there are fewer tiles than CUs, K may be
+// split into ranges (blockIdx.y) that write fp32 partials for an ordered
+// reduction.
+#pragma once
+
+#include "ql_device.h"
+#include "ql_kernels.h"
+
+namespace ql {
+
+namespace g3 {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf2;
+
+constexpr int kBM = 256, kBN = 256, kNW = 8, kNT = 64 * kNW;
+constexpr int kWN = 32, kMI = kBM / 16, kNI = kWN / 16;  // a wave: all rows x 32 columns
+constexpr int kXStage = kBM * 128;               // bytes of one x stage
+constexpr int kStages = 3;                       // x stages in the LDS ring
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne3(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two codes (1024 + q as fp16 bit patterns in the halves of v) -> two weights.
+__device__ __forceinline__ uint32_t dq_pair(uint32_t v, h2 s2, h2 b2) {
+  const h2 q = __builtin_bit_cast(h2, v) - h2{(_Float16)1024.0f, (_Float16)1024.0f};  // exact
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+}
+
+// Two codes (byte 0 and byte 2 of qp) -> hi and lo bf16 pairs of the fp32
+// weights s*q + b (SPLIT numerics).
+__device__ __forceinline__ void split_pair(uint32_t qp, float s, float b, uint32_t &hi, uint32_t &lo) {
+  const float w0 = __builtin_fmaf((float)(qp & 0xFFu), s, b);
+  const float w1 = __builtin_fmaf((float)((qp >> 16) & 0xFFu), s, b);
+  const bf2 h = {(__bf16)w0, (__bf16)w1};  // v_cvt_pk_bf16_f32, round to nearest even
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const float r0 = w0 - __uint_as_float(hb << 16);           // exact
+  const float r1 = w1 - __uint_as_float(hb & 0xFFFF0000u);   // exact
+  const bf2 l = {(__bf16)r0, (__bf16)r1};
+  hi = hb;
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// A lane's codes of one column and group: codes 16h .. 16h+15 (h = lane / 16),
+// i.e. k-blocks 2h and 2h+1, as they sit in the tiled layout. pair(w, c, p)
+// gives word p of the FAST B fragment of k-block 2h + c (two fp16 weights);
+// qpair(w, c, p) gives the same two codes in bytes 0 and 2.
+template <int BITS> struct LaneCodes;
+// 4-bit block [h'2][col32][4 words]: words 2(h%2), +1 of half h/2, pair order
+// (code 2p at bits 4p, code 2p+1 at 16 + 4p).
+template <> struct LaneCodes<4> {
+  static constexpr int kWords = 2;
+  __device__ static constexpr uint32_t offset(int col, int h) { return (h >> 1) * 512 + col * 16 + (h & 1) * 8; }
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return dq_pair(and_or(w[c] >> (4 * p), 0x000F000Fu, 0x64006400u), s2, b2);
+  }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) { return (w[c] >> (4 * p)) & 0x000F000Fu; }
+};
+// 8-bit block [part2][h'2][col32][4 words]: part h%2, half h/2, little-endian.
+template <> struct LaneCodes<8> {
+  static constexpr int kWords = 4;
+  __device__ static constexpr uint32_t offset(int col, int h) { return (h & 1) * 1024 + (h >> 1) * 512 + col * 16; }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) {
+    // bytes (b0, b1) or (b2, b3) of word 2c + p/2 into bytes 0 and 2
+    return perm(0u, w[2 * c + (p >> 1)], (p & 1) ? 0x0C030C02u : 0x0C010C00u);
+  }
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return dq_pair(qpair(w, c, p) | 0x64006400u, s2, b2);
+  }
+};
+// 2-bit block [h'2][col32][2 words]: word h%2 of half h/2, pair order (code 2p
+// at bits 2p, code 2p+1 at 16 + 2p); chunk c is pairs 4c .. 4c+3.
+template <> struct LaneCodes<2> {
+  static constexpr int kWords = 1;
+  __device__ static constexpr uint32_t offset(int col, int h) { return (h >> 1) * 256 + col * 8 + (h & 1) * 4; }
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return dq_pair(and_or(w[0] >> (8 * c + 2 * p), 0x00030003u, 0x64006400u), s2, b2);
+  }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) {
+    return (w[0] >> (8 * c + 2 * p)) & 0x00030003u;
+  }
+};
+
+// 3-bit block: the 2-bit block of the low bits (word h%2 of half h/2, as
+// above), then the high-bit plane [h'2][col32][1 word] at byte 512 (code 2P
+// of the half at bit P, code 2P+1 at bit 16+P). w[0] is the low-bit word,
+// w[1] the high-bit word of half h/2 after prep(): the lane's pairs
+// 8(h%2) .. +7 moved to bits 2.. and 18.. (prep runs once per group, when
+// the codes have arrived).
+template <> struct LaneCodes<3> {
+  static constexpr int kWords = 2;
+  __device__ static constexpr uint32_t offset(int col, int h) { return (h >> 1) * 256 + col * 8 + (h & 1) * 4; }
+  __device__ static constexpr uint32_t hi_offset(int col, int h) { return 512 + (h >> 1) * 128 + col * 4; }
+  __device__ static uint32_t prep(uint32_t hw, int h) { return (hw >> (8 * (h & 1))) << 2; }
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    const uint32_t lo = and_or(w[0] >> (8 * c + 2 * p), 0x00030003u, 0x64006400u);
+    return dq_pair(and_or(w[1] >> (4 * c + p), 0x00040004u, lo), s2, b2);
+  }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) {
+    return ((w[0] >> (8 * c + 2 * p)) & 0x00030003u) | ((w[1] >> (4 * c + p)) & 0x00040004u);
+  }
+};
+
+// Canonical layout (each row one little-endian code stream): a lane's 16
+// codes 16h .. 16h+15 of its row and group are 16*BITS/8 contiguous bytes at
+// row offset g*8*BITS + 2*BITS*h; the codes are in plain order, so a pair is
+// gathered with one byte permute (4-bit, 2-bit) before the AND-OR. 8-bit
+// bytes are already in the order LaneCodes<8> reads.
+template <int BITS> struct CanonCodes;
+template <> struct CanonCodes<4> {
+  static constexpr int kWords = 2;
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    // nibbles 2p, 2p+1 of word c: byte p of w and of w >> 4, low nibbles
+    const uint32_t sel = 0x0C040C00u + 0x00010001u * (uint32_t)p;
+    return dq_pair(and_or(perm(w[c] >> 4, w[c], sel), 0x000F000Fu, 0x64006400u), s2, b2);
+  }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) {
+    const uint32_t sel = 0x0C040C00u + 0x00010001u * (uint32_t)p;
+    return perm(w[c] >> 4, w[c], sel) & 0x000F000Fu;
+  }
+};
+template <> struct CanonCodes<8> {
+  static constexpr int kWords = 4;
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    return LaneCodes<8>::pair(w, c, p, s2, b2);
+  }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) { return LaneCodes<8>::qpair(w, c, p); }
+};
+template <> struct CanonCodes<2> {
+  static constexpr int kWords = 1;
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], int c, int p, h2 s2, h2 b2) {
+    // codes 8c+2p, 8c+2p+1 at bits 16c+4p and 16c+4p+2
+    const uint32_t t = w[0] >> (16 * c + 4 * p);
+    return dq_pair(and_or(perm(t >> 2, t, 0x0C040C00u), 0x00030003u, 0x64006400u), s2, b2);
+  }
+  __device__ static uint32_t qpair(const uint32_t (&w)[kWords], int c, int p) {
+    const uint32_t t = w[0] >> (16 * c + 4 * p);
+    return perm(t >> 2, t, 0x0C040C00u) & 0x00030003u;
+  }
+};
+template <int BITS, bool CANON> struct CodesOf { using type = LaneCodes<BITS>; };
+template <int BITS> struct CodesOf<BITS, true> { using type = CanonCodes<BITS>; };
+
+// Chunk swizzle of an x stage: logical 16-byte chunk c of row r sits at
+// position c ^ xswz(r). With this function the 64 lanes of an MFMA fragment
+// read (16 rows, four k-blocks) spread over the banks best among the
+// XOR swizzles measured on MI355X (194 B/clk/CU against 140 for c ^ (r & 7)).
+__device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// The part of a tile's K loop both numerics share: x copies into the stage
+// ring, the lane's code and scale/bias loads, A-fragment reads. MI 16-row
+// subtiles per wave (16 for a whole tile, fewer for a row piece).
+template <int BITS, int MI, bool CANON>
+struct TileIO {
+  using LC = typename CodesOf<BITS, CANON>::type;
+  static constexpr int WB = 64 * BITS / 8;     // code bytes of one column per group
+  static constexpr int BB = 32 * WB;           // bytes of one tiled block (32 columns x 1 group)
+  static constexpr int kRows = 16 * MI;
+  static constexpr int XC = kRows / 8;         // 1 KB x copies per group (8 rows each)
+  static constexpr int XPW = XC >= kNW ? XC / kNW : 1;  // copies per issuing wave
+  static_assert(XC % kNW == 0 || kNW % XC == 0, "x copies must spread evenly over the waves");
+
+  const Gemm3Args &a;
+  int lane, wave, r16, h, G;
+  bool x_issuer;
+  __amdgpu_buffer_rsrc_t xr, wr, sr, br;
+  uint32_t xo[XPW];
+  uint32_t wo = 0, so = 0, who = 0;  // who: 3-bit, the lane's high-bit word
+  uint32_t kColStep = 0;             // tiled: bytes per 16 columns
+  uint32_t rowo[kNI] = {}, srow[kNI] = {};  // canonical: the lane's row of each column block
+  int a_off[2][4];
+  int a_base;
+
+  __device__ TileIO(const Gemm3Args &args, int64_t m0, int64_t n0) : a(args) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    r16 = lane & 15;
+    h = lane >> 4;
+    G = a.G;
+    // x copies: copy i of this wave fills block rows (wave*XPW + i)*8 .. +7, lane L
+    // row +L/8 at chunk position L & 7, which holds logical chunk
+    // (L & 7) ^ xswz(row). Rows past M repeat the last row. With fewer copies
+    // than waves only the first XC waves copy.
+    const int64_t xrow = a.K * 2;
+    const int64_t mrows = min<int64_t>(kRows, a.M - m0);
+    x_issuer = XC >= kNW || wave < XC;
+    xr = make_rsrc(a.x16, m0 * xrow, mrows * xrow);
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) {
+      const int rr = (wave * XPW + i) * 8 + (lane >> 3);
+      const int r = rr < mrows ? rr : (int)mrows - 1;
+      xo[i] = (uint32_t)(r * xrow) + (uint32_t)(((lane & 7) ^ xswz(rr)) * 16);
+    }
+    // this wave's strip of the tiled codes; past N repeat the last strip
+    const int64_t nstrips = (a.N + 31) / 32;
+    int64_t strip = n0 / 32 + wave;
+    if (strip >= nstrips) strip = nstrips - 1;
+    if constexpr (CANON) {
+      // one descriptor over all rows (uniform), the row in the lane offset;
+      // rows past N repeat row N-1
+      wr = make_rsrc(a.w, 0, a.N * (a.K * BITS / 8));
+      sr = make_rsrc(a.s16, 0, a.N * (int64_t)G * 2);
+      br = make_rsrc(a.b16, 0, a.N * (int64_t)G * 2);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t n = min<int64_t>(strip * 32 + ni * 16 + r16, a.N - 1);
+        rowo[ni] = (uint32_t)(n * (a.K * BITS / 8)) + (uint32_t)(h * 2 * BITS);
+        srow[ni] = (uint32_t)(n * G * 2);
+      }
+    } else {
+      wr = make_rsrc(a.w, strip * G * BB, (int64_t)G * BB);
+      sr = make_rsrc(a.sb, strip * G * 128, (int64_t)G * 128);
+      br = sr;
+      wo = LC::offset(r16, h);
+      so = (uint32_t)(r16 * 4);
+      if constexpr (BITS == 3) who = LaneCodes<BITS>::hi_offset(r16, h);
+      kColStep = LC::offset(16, 0) - LC::offset(0, 0);
+    }
+    // A fragments: rows mi*16 + r16, k-block 2h + c, at chunk position
+    // (2h + c) ^ xswz(mi*16 + r16) = (2h + c) ^ ((r16 ^ (r16 >> 3) ^ 2mi) & 7):
+    // four lane offsets per chunk, by mi & 3
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a_off[c][q] = ((2 * h + c) ^ ((r16 ^ (r16 >> 3) ^ (2 * q)) & 7)) * 16;
+    a_base = r16 * 128;
+  }
+
+  // Codes and scale/bias of group gv for this lane's two column blocks.
+  // Tiled: sb = s | b << 16, bb unused; canonical: sb = s, bb = b.
+  __device__ __forceinline__ void load_codes(uint32_t (&w)[kNI][LC::kWords], uint32_t (&sb)[kNI], uint32_t (&bb)[kNI],
+                                             int gv) const {
+    const int g = __builtin_amdgcn_readfirstlane(gv);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      if constexpr (CANON) {
+        const uint32_t go = (uint32_t)g * (8u * BITS);
+        if constexpr (BITS == 4) {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, rowo[ni], go, 0);
+          w[ni][0] = v[0];
+          w[ni][1] = v[1];
+        } else if constexpr (BITS == 8) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, rowo[ni], go, 0);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[ni][t] = v[t];
+        } else {
+          w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, rowo[ni], go, 0);
+        }
+        sb[ni] = __builtin_amdgcn_raw_buffer_load_b16(sr, srow[ni], (uint32_t)g * 2u, 0);
+        bb[ni] = __builtin_amdgcn_raw_buffer_load_b16(br, srow[ni], (uint32_t)g * 2u, 0);
+        continue;
+      }
+      if constexpr (BITS == 4) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
+        w[ni][0] = v[0];
+        w[ni][1] = v[1];
+      } else if constexpr (BITS == 8) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[ni][t] = v[t];
+      } else if constexpr (BITS == 3) {
+        w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
+        w[ni][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, who + ni * 64u, (uint32_t)g * BB, 0);
+      } else {
+        w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, wo + ni * kColStep, (uint32_t)g * BB, 0);
+      }
+      sb[ni] = __builtin_amdgcn_raw_buffer_load_b32(sr, so + ni * 64u, (uint32_t)g * 128u, 0);
+      bb[ni] = 0u;
+    }
+  }
+
+  __device__ __forceinline__ void issue_x(unsigned char *X, int gv) const {
+    const int g = __builtin_amdgcn_readfirstlane(gv);
+    if (x_issuer) {
+#pragma unroll
+      for (int i = 0; i < XPW; ++i) dma16(xr, xo[i], (uint32_t)g * 128u, X + (wave * XPW + i) * 1024);
+    }
+  }
+
+  // A fragment of step t = c*MI + mi: rows mi*16 + r16, k-block 2h + c.
+  __device__ __forceinline__ h8 read_a(const unsigned char *X, int t) const {
+    const int c = t / MI, mi = t % MI;
+    return *reinterpret_cast<const h8 *>(X + a_base + mi * 2048 + a_off[c][mi & 3]);
+  }
+
+  // Largest |W| the column blocks of this lane can produce over groups
+  // [g_begin, g_end): max over groups of max(|b|, |b + Q*s|), W lying between
+  // b and b + Q*s. The four lanes of a column (h = 0..3) scan every fourth
+  // group and combine their maxima.
+  __device__ void column_bounds(int g_begin, int g_end, float (&bound)[kNI]) const {
+    constexpr float Q = (float)((1 << BITS) - 1);
+    constexpr int U = 6;
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) bound[ni] = 0.f;
+    for (int g0 = g_begin + h; g0 < g_end; g0 += 4 * U) {
+      uint32_t sv[U][kNI], bv[U][kNI];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // g differs between the lanes of a column: it goes into the per-lane offset
+        const int g = min(g0 + 4 * u, g_end - 1);
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni) {
+          if constexpr (CANON) {
+            sv[u][ni] = __builtin_amdgcn_raw_buffer_load_b16(sr, srow[ni] + (uint32_t)g * 2u, 0u, 0);
+            bv[u][ni] = __builtin_amdgcn_raw_buffer_load_b16(br, srow[ni] + (uint32_t)g * 2u, 0u, 0);
+          } else {
+            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(sr, so + ni * 64u + (uint32_t)g * 128u, 0u, 0);
+            sv[u][ni] = v & 0xFFFFu;
+            bv[u][ni] = v >> 16;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni) {
+          const float s = f16_to_f32((uint16_t)sv[u][ni]), b = f16_to_f32((uint16_t)bv[u][ni]);
+          bound[ni] = fmaxf(bound[ni], fmaxf(fabsf(b), fabsf(__builtin_fmaf(Q, s, b))));
+        }
+    }
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      bound[ni] = fmaxf(bound[ni], __shfl_xor(bound[ni], 16));
+      bound[ni] = fmaxf(bound[ni], __shfl_xor(bound[ni], 32));
+    }
+  }
+};
+
+// FAST numerics: accumulates rows m0 .. m0 + 16*MI of the block tile at
+// (m0, n0) over groups [g_begin, g_end) on fp16 MFMA; cs[ni] receives the
+// power-of-two output scale 2^c of the lane's column blocks.
+template <int BITS, int MI, bool CANON>
+__device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages], int64_t m0,
+                                                 int64_t n0, int g_begin, int g_end, f32x4 (&acc)[MI][kNI],
+                                                 float (&cs)[kNI]) {
+  constexpr int S = kStages;
+  using IO = TileIO<BITS, MI, CANON>;
+  using LC = typename IO::LC;
+  constexpr int kSteps = 2 * MI;        // steps (c, mi) of kNI MFMAs per group
+  constexpr int kHalf = kSteps / 2;
+  // A fragments are read this many steps ahead of their use; the ring index
+  // t % (kAhead + 1) continues across groups, whose reads ahead wrap into
+  // the next stage, which is complete only after the mid-group barrier
+  constexpr int kAhead = (kSteps % 4 == 0 && kHalf >= 3) ? 3 : 1;
+  static_assert(kSteps % (kAhead + 1) == 0, "A-fragment ring must divide the steps of a group");
+  static_assert(kAhead <= kHalf, "reads of the next stage must follow the mid-group barrier");
+  // the next group's B fragments are built in 4 * 2 * kNI pieces of one word
+  // (two weights), spread over the steps of the second half so the vector
+  // work sits between MFMAs instead of in bursts
+  constexpr int kPieces = 8 * kNI;
+  constexpr int kPerStep = (kPieces + kHalf - 1) / kHalf;
+  const IO io(a, m0, n0);
+  const int h = io.h;
+
+  // per-column fp16 range: weights of a column whose bound reaches 65504 are
+  // scaled by 2^-c before the fp16 rounding (scale and bias multiplied by an
+  // exact power of two), and the column's outputs by 2^c at the store
+  h2 wsc[kNI];
+  {
+    float bound[kNI];
+    io.column_bounds(g_begin, g_end, bound);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int c = bound[ni] < 65504.f ? 0 : max(0, min(ilogbf(bound[ni]) - 14, 30));
+      cs[ni] = __uint_as_float((uint32_t)(127 + c) << 23);
+      const _Float16 inv = (_Float16)__uint_as_float((uint32_t)(127 - c) << 23);
+      wsc[ni] = h2{inv, inv};
+    }
+  }
+
+  h8 af[kAhead + 1];
+  // B fragments of the group being multiplied, built from codes that arrived
+  // earlier; a group past the end gets zero scale and bias, so its weights
+  // are zero and its step adds nothing. Codes and scale|bias words of groups
+  // g+1 .. g+S-2 are held (cq[0] = g+1); those of g+S-1 are requested in
+  // group g.
+  u32x4 bf[kNI][2];
+  uint32_t cq[S - 1][kNI][LC::kWords];
+  uint32_t sq[S - 1][kNI];   // tiled: s | b << 16; canonical: s
+  uint32_t bq[S - 1][kNI];   // canonical: b (unused when tiled)
+  // piece i of the B fragments from cq[0]/sq[0]: fragment (ni, c) = i / 4, word i % 4
+  auto dequant_piece = [&](u32x4 (&dst)[kNI][2], bool valid, int i) {
+    const int f = i >> 2, p = i & 3, ni = f >> 1, c = f & 1;
+    const uint32_t v = valid ? (CANON ? (sq[0][ni] & 0xFFFFu) | (bq[0][ni] << 16) : sq[0][ni]) : 0u;
+    const h2 s2 = __builtin_bit_cast(h2, (v & 0xFFFFu) * 0x10001u) * wsc[ni];
+    const h2 b2 = __builtin_bit_cast(h2, (v >> 16) * 0x10001u) * wsc[ni];
+    if constexpr (BITS == 3 && !CANON) {
+      // the first piece of a column block (i = 8 ni) runs before its other
+      // pieces: in both placements below pieces run in increasing i within a
+      // column block
+      if (c == 0 && p == 0) cq[0][ni][1] = LC::prep(cq[0][ni][1], h);
+    }
+    uint32_t r = LC::pair(cq[0][ni], c, p, s2, b2);
+    asm volatile("" : "+v"(r));  // keeps the piece where it is placed, between MFMAs
+    dst[ni][c][p] = r;
+  };
+
+  // One group on stage X. First half: MFMAs on the fragments in hand. Then
+  // the barrier, after which the next stage XN is complete and the stage of
+  // the previous group (XD) is free: the x copies for S-1 groups ahead go
+  // into XD and their codes are requested. Second half: MFMAs, with the next
+  // group's B fragments dequantized in between and the first A fragments of
+  // XN read ahead, so the next group starts without a stall.
+  auto step = [&](const unsigned char *X, const unsigned char *XN, unsigned char *XD, int g) {
+    u32x4 bn[kNI][2];
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      const int c = t / MI, mi = t % MI;
+      if (t == kHalf) {
+        dma_barrier();  // stage g+1 has landed everywhere, stage g-1 is free
+        // the second half runs at raised wave priority (back to normal at the
+        // end of the group): 1-1.5 % faster on the large shapes, measured
+        __builtin_amdgcn_s_setprio(1);
+        io.issue_x(XD, min(g + S - 1, g_end - 1));
+        io.load_codes(cq[S - 2], sq[S - 2], bq[S - 2], min(g + S - 1, g_end - 1));
+      }
+      if (t + kAhead < kSteps) af[(t + kAhead) % (kAhead + 1)] = io.read_a(X, t + kAhead);
+      else af[(t + kAhead) % (kAhead + 1)] = io.read_a(XN, t + kAhead - kSteps);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t % (kAhead + 1)], __builtin_bit_cast(h8, bf[ni][c]),
+                                                             acc[mi][ni], 0, 0, 0);
+        if (t >= kHalf) {
+#pragma unroll
+          for (int u = 0; u < kPerStep; ++u) {
+            const int i = (t - kHalf) * kPerStep + u;
+            if ((u % kNI) == ni && i < kPieces) dequant_piece(bn, g + 1 < g_end, i);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      bf[ni][0] = bn[ni][0];
+      bf[ni][1] = bn[ni][1];
+#pragma unroll
+      for (int j = 0; j + 1 < S - 1; ++j) {
+        sq[j][ni] = sq[j + 1][ni];
+        bq[j][ni] = bq[j + 1][ni];
+#pragma unroll
+        for (int u = 0; u < LC::kWords; ++u) cq[j][ni][u] = cq[j + 1][ni][u];
+      }
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Groups run S at a time (one per x stage) in straight-line code: loads
+  // for a group past the end are clamped to the last group and its weights
+  // dequantize to zero, so the accumulators never pass through a branch.
+  if (g_begin < g_end) {
+    io.load_codes(cq[0], sq[0], bq[0], g_begin);
+    io.issue_x(xs[0], g_begin);
+    io.issue_x(xs[1], min(g_begin + 1, g_end - 1));
+  }
+  dma_barrier();  // first two stages and the first codes have arrived
+  if (g_begin < g_end) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
+    io.load_codes(cq[0], sq[0], bq[0], min(g_begin + 1, g_end - 1));
+    // stages and codes up to g_begin + S - 2 are in flight now; each group g
+    // requests g + S - 1
+#pragma unroll
+    for (int j = 2; j < S - 1; ++j) {
+      io.issue_x(xs[j], min(g_begin + j, g_end - 1));
+      io.load_codes(cq[j - 1], sq[j - 1], bq[j - 1], min(g_begin + j, g_end - 1));
+    }
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) af[t] = io.read_a(xs[0], t);
+  }
+  for (int g = g_begin; g < g_end; g += S) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) step(xs[k], xs[(k + 1) % S], xs[(k + S - 1) % S], g + k);
+  }
+  dma_barrier();  // the copies requested past the last group have landed; every stage is free
+}
+
+// SPLIT numerics: same tile walk on bf16 MFMA with hi and lo weight
+// fragments. The k-block c = 1 fragments of group g are built during the
+// first half of group g (from the codes of g), the c = 0 fragments of group
+// g+1 during the second half (from the codes of g+1), so each half refills
+// the fragments the other half does not use and no second fragment set is
+// held. Code slots: [0] = group g, [1] = group g+1, requested when group g
+// starts (half a group before its first use). Each A fragment feeds four
+// MFMAs, so it is read one step ahead.
+template <int BITS, int MI, bool CANON>
+__device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsigned char *const (&xs)[kStages],
+                                                      int64_t m0, int64_t n0, int g_begin, int g_end,
+                                                      f32x4 (&acc)[MI][kNI]) {
+  constexpr int S = kStages;
+  using IO = TileIO<BITS, MI, CANON>;
+  using LC = typename IO::LC;
+  constexpr int kSteps = 2 * MI;
+  constexpr int kHalf = kSteps / 2;
+  constexpr int kAhead = 1;
+  // 4 * kNI pieces (one word of one fragment: two weights, hi and lo) per
+  // half, spread evenly over the half's steps
+  constexpr int kPieces = 4 * kNI;
+  constexpr int kStride = kHalf >= kPieces ? kHalf / kPieces : 1;
+  constexpr int kPerStep = kHalf >= kPieces ? 1 : kPieces / kHalf;
+  static_assert(kHalf >= kPieces ? kHalf % kPieces == 0 : kPieces % kHalf == 0, "pieces spread evenly");
+  const IO io(a, m0, n0);
+  const int h = io.h;
+
+  h8 af[kAhead + 1];
+  u32x4 bh[kNI][2], bl[kNI][2];
+  uint32_t cq[2][kNI][LC::kWords];
+  uint32_t sq[2][kNI];
+  uint32_t bq[2][kNI];
+  float sf[kNI], bfl[kNI];  // fp32 scale and bias of the slot being dequantized
+
+  auto prep_slot = [&](int slot, bool valid) {
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const uint32_t v = valid ? (CANON ? (sq[slot][ni] & 0xFFFFu) | (bq[slot][ni] << 16) : sq[slot][ni]) : 0u;
+      sf[ni] = f16_to_f32((uint16_t)(v & 0xFFFFu));
+      bfl[ni] = f16_to_f32((uint16_t)(v >> 16));
+    }
+  };
+  // piece i (fragment ni = i / 4 of k-block c, word p = i % 4) from slot
+  auto dequant_piece = [&](int slot, int c, int i) {
+    const int ni = i >> 2, p = i & 3;
+    if constexpr (BITS == 3 && !CANON) {
+      if (c == 0 && p == 0) cq[slot][ni][1] = LC::prep(cq[slot][ni][1], h);
+    }
+    uint32_t hi, lo;
+    split_pair(LC::qpair(cq[slot][ni], c, p), sf[ni], bfl[ni], hi, lo);
+    asm volatile("" : "+v"(hi), "+v"(lo));  // keeps the piece where it is placed, between MFMAs
+    bh[ni][c][p] = hi;
+    bl[ni][c][p] = lo;
+  };
+
+  auto step = [&](const unsigned char *X, const unsigned char *XN, unsigned char *XD, int g) {
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      const int c = t / MI, mi = t % MI;
+      const int tt = t % kHalf;
+      if (t == 0) {
+        io.load_codes(cq[1], sq[1], bq[1], min(g + 1, g_end - 1));
+        prep_slot(0, g < g_end);
+      }
+      if (t == kHalf) {
+        dma_barrier();  // stage g+1 and the codes of g+1 have landed, stage g-1 is free
+        __builtin_amdgcn_s_setprio(1);
+        io.issue_x(XD, min(g + S - 1, g_end - 1));
+        prep_slot(1, g + 1 < g_end);
+      }
+      if (t + kAhead < kSteps) af[(t + kAhead) % (kAhead + 1)] = io.read_a(X, t + kAhead);
+      else af[(t + kAhead) % (kAhead + 1)] = io.read_a(XN, t + kAhead - kSteps);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, af[t % (kAhead + 1)]);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh[ni][c]), acc[mi][ni],
+                                                              0, 0, 0);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl[ni][c]), acc[mi][ni],
+                                                              0, 0, 0);
+      if (tt % kStride == 0) {
+#pragma unroll
+        for (int u = 0; u < kPerStep; ++u) {
+          const int i = (tt / kStride) * kPerStep + u;
+          if (i < kPieces) {
+            if (t < kHalf) dequant_piece(0, 1, i);  // k-block 1 of group g
+            else dequant_piece(1, 0, i);            // k-block 0 of group g+1
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      sq[0][ni] = sq[1][ni];
+      bq[0][ni] = bq[1][ni];
+#pragma unroll
+      for (int u = 0; u < LC::kWords; ++u) cq[0][ni][u] = cq[1][ni][u];
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (g_begin < g_end) {
+    io.load_codes(cq[0], sq[0], bq[0], g_begin);
+    io.issue_x(xs[0], g_begin);
+    io.issue_x(xs[1], min(g_begin + 1, g_end - 1));
+  }
+  dma_barrier();  // first two stages and the codes of the first group have arrived
+  if (g_begin < g_end) {
+    prep_slot(0, true);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) dequant_piece(0, 0, i);  // k-block 0 of the first group
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) af[t] = io.read_a(xs[0], t);
+  }
+  for (int g = g_begin; g < g_end; g += S) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) step(xs[k], xs[(k + 1) % S], xs[(k + S - 1) % S], g + k);
+  }
+  dma_barrier();  // the copies requested past the last group have landed; every stage is free
+}
+
+// silu(g) * u: g / (1 + e^-g) with the hardware exponential and reciprocal;
+// e^-g overflows to +inf for g < -88 and the quotient is then -0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Stores rows m0 .. m0 + 16*MI of a tile, times the row scales rs and the
+// column scales cs, into out ([M, N] fp32 or bf16). The row scales come from
+// LDS (rs_lds[m - m0], staged by the caller): a global load among the stores
+// would wait for every store before it, since one counter tracks both, which
+// cost ~6 % of the kernel. Without SCALED (SPLIT numerics) there are no
+// scales. With GLU-ordered weights subtile ni = 0 of a wave holds gate outputs
+// and ni = 1 the up outputs of the same 16 columns f = 16*strip + r16 of the
+// [M, N/2] result, which gets silu(gate) * up.
+template <bool OUT_BF16, int MI, bool SCALED>
+__device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64_t m0, int64_t n0,
+                                            const f32x4 (&acc)[MI][kNI], const float *rs_lds, const float (&cs)[kNI]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, h = lane >> 4;
+  const int64_t row0 = m0 + 4 * h;
+  auto row_scale = [&](int64_t m) -> float {
+    if constexpr (SCALED) return rs_lds[m - m0];
+    else return 1.f;
+  };
+  auto col = [&](float v, int ni) -> float {
+    if constexpr (SCALED) return v * cs[ni];
+    else return v;
+  };
+  if (a.glu) {
+    const int64_t F = a.N / 2;
+    const int64_t f = (n0 / 32 + wave) * 16 + r16;
+    if (f >= F) return;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = row0 + mi * 16 + i;
+        if (m >= a.M) continue;
+        const float rs = row_scale(m);
+        const float v = swiglu(col(acc[mi][0][i] * rs, 0), col(acc[mi][1][i] * rs, 1));
+        if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * F + f] = f32_to_bf16_rne3(v);
+        else reinterpret_cast<float *>(out)[m * F + f] = v;
+      }
+    return;
+  }
+  const int64_t col0 = n0 + wave * kWN + r16;
+  const bool full = (m0 + 16 * MI <= a.M) && (n0 + kBN <= a.N);
+  if (a.gate) {
+    // gated residual update: out = residual + gate[m / gate_rows] * y, one
+    // fused multiply-add in fp32; each element is read and written by the
+    // same lane, so residual may be out itself. Residual and gate values are
+    // read for two subtile rows at a time before their stores, so a load
+    // waits behind earlier stores once per pair of subtile rows
+    constexpr int CH = MI < 2 ? MI : 2;
+#pragma unroll
+    for (int mc = 0; mc < MI; mc += CH) {
+      float rv[CH][4][kNI], gv[CH][4][kNI];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + (mc + c) * 16 + i;
+          const float *grow = a.gate + (int64_t)((uint32_t)m / (uint32_t)a.gate_rows) * a.N;
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni) {
+            const int64_t n = col0 + ni * 16;
+            const bool ok = full || (m < a.M && n < a.N);
+            if constexpr (OUT_BF16)
+              rv[c][i][ni] = ok ? bf16_lo(reinterpret_cast<const uint16_t *>(a.residual)[m * a.N + n]) : 0.f;
+            else
+              rv[c][i][ni] = ok ? reinterpret_cast<const float *>(a.residual)[m * a.N + n] : 0.f;
+            gv[c][i][ni] = ok ? grow[n] : 0.f;
+          }
+        }
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + (mc + c) * 16 + i;
+          if (!full && m >= a.M) continue;
+          const float rs = row_scale(m);
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni) {
+            const int64_t n = col0 + ni * 16;
+            if (!full && n >= a.N) continue;
+            const float y = __builtin_fmaf(gv[c][i][ni], col(acc[mc + c][ni][i] * rs, ni), rv[c][i][ni]);
+            if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * a.N + n] = f32_to_bf16_rne3(y);
+            else reinterpret_cast<float *>(out)[m * a.N + n] = y;
+          }
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = row0 + mi * 16 + i;
+      if (!full && m >= a.M) continue;
+      const float rs = row_scale(m);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t n = col0 + ni * 16;
+        if (!full && n >= a.N) continue;
+        const float v = col(acc[mi][ni][i] * rs, ni);
+        if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m * a.N + n] = f32_to_bf16_rne3(v);
+        else reinterpret_cast<float *>(out)[m * a.N + n] = v;
+      }
+    }
+}
+
+// blockIdx.y = K range (a.splits of them; each writes its own fp32 slice of
+// out, [splits, M, N], for an ordered reduction afterwards). Blocks
+// [0, tail_tiles * 16/PMI) first run the row pieces of the last tail_tiles
+// tiles (PMI 16-row subtiles each, pieces of one tile on one XCD), then every
+// block takes whole tiles t = blockIdx.x, + gridDim.x, ... below dp_tiles.
+// Power-of-two row and column scales commute exactly with the summation, so
+// partials carry them already.
+template <int BITS, bool OUT_BF16, int PMI, bool CANON, bool SPLIT>
+__global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char x0[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char x2[kXStage];
+  __shared__ __attribute__((aligned(16))) float rs_lds[kBM];
+  unsigned char *const xs[kStages] = {x0, x1, x2};
+  // FAST: the row scales of a tile's rows, requested at the tile's start (one
+  // value per thread), written to LDS once the K loop has ended (its last
+  // barrier also ends every wave's reads of the previous tile's scales)
+  auto tile_rs = [&](int64_t m0, int rows) -> float {
+    if constexpr (SPLIT) return 1.f;
+    const int64_t m = m0 + threadIdx.x;
+    return (int)threadIdx.x < rows && m < a.M ? a.rowscale[m] : 0.f;
+  };
+  auto stage_rs = [&](float v, int rows) {
+    if constexpr (SPLIT) return;
+    if ((int)threadIdx.x < rows) rs_lds[threadIdx.x] = v;
+    __syncthreads();
+  };
+  auto accumulate = [&](auto &acc_, int64_t m0, int64_t n0, int gb, int ge, float (&cs)[kNI]) {
+    constexpr int MI = sizeof(acc_) / sizeof(acc_[0]);
+    if constexpr (SPLIT) {
+      tile_accumulate_split<BITS, MI, CANON>(a, xs, m0, n0, gb, ge, acc_);
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) cs[ni] = 1.f;
+    } else {
+      tile_accumulate3<BITS, MI, CANON>(a, xs, m0, n0, gb, ge, acc_, cs);
+    }
+  };
+  const int tiles_n = (int)((a.N + kBN - 1) / kBN);
+  const int split = blockIdx.y;
+  const int gps = (a.G + a.splits - 1) / a.splits;
+  const int gb = split * gps, ge = min(a.G, gb + gps);
+  void *out = a.splits > 1 ? static_cast<void *>(static_cast<float *>(a.out) + (int64_t)split * a.M * a.N) : a.out;
+
+  if constexpr (PMI > 0) {
+    constexpr int kPieces = 16 / PMI;
+    if ((int)blockIdx.x < a.tail_tiles * kPieces) {
+      const int tail = blockIdx.x % a.tail_tiles, piece = blockIdx.x / a.tail_tiles;
+      const int tile = a.dp_tiles + tail;
+      const int64_t m0 = (int64_t)(tile / tiles_n) * kBM + piece * 16 * PMI;
+      const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
+      if (m0 < a.M) {  // uniform per block
+        f32x4 pacc[PMI][kNI];
+        float cs[kNI];
+        const float rs = tile_rs(m0, 16 * PMI);
+        accumulate(pacc, m0, n0, gb, ge, cs);
+        stage_rs(rs, 16 * PMI);
+        tile_store3<OUT_BF16, PMI, !SPLIT>(a, out, m0, n0, pacc, rs_lds, cs);
+      }
+    }
+  }
+  f32x4 acc[kMI][kNI];
+  for (int t = blockIdx.x; t < a.dp_tiles; t += gridDim.x) {
+    const int tile = xcd_remap(t, a.dp_tiles);
+    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
+    float cs[kNI];
+    const float rs = tile_rs(m0, kBM);
+    accumulate(acc, m0, n0, gb, ge, cs);
+    stage_rs(rs, kBM);
+    tile_store3<OUT_BF16, kMI, !SPLIT>(a, out, m0, n0, acc, rs_lds, cs);
+  }
+}
+
+template <int BITS, bool OUT_BF16, bool CANON, bool SPLIT>
+void launch3_out(const Gemm3Args &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.grid_x, (unsigned)a.splits);
+  switch (a.tail_tiles > 0 ? a.tail_mi : 0) {
+    case 2: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 2, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 4, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 8, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 0, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
+  }
+}
+
+template <int BITS, bool CANON, bool SPLIT>
+void launch3_layout(const Gemm3Args &a, hipStream_t stream) {
+  if (a.out_bf16 && a.splits == 1) launch3_out<BITS, true, CANON, SPLIT>(a, stream);
+  else launch3_out<BITS, false, CANON, SPLIT>(a, stream);
+}
+
+template <int BITS, bool SPLIT>
+hipError_t launch3_bits(const Gemm3Args &a, hipStream_t stream) {
+  if (a.tail_tiles > 0 && a.tail_mi != 2 && a.tail_mi != 4 && a.tail_mi != 8) return hipErrorInvalidValue;
+  if (a.splits < 1 || (a.splits > 1 && a.tail_tiles > 0)) return hipErrorInvalidValue;
+  if constexpr (BITS == 3) {
+    if (a.canon) return hipErrorInvalidValue;  // 3-bit codes run on tiled weights only
+    launch3_layout<BITS, false, SPLIT>(a, stream);
+  } else {
+    if (a.canon) launch3_layout<BITS, true, SPLIT>(a, stream);
+    else launch3_layout<BITS, false, SPLIT>(a, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace g3
+
+}  // namespace ql

@@ -80,41 +80,6 @@ float f16_to_f32(uint16_t h) {
   return f;
 }
 
-// ---- library-owned workspace for qlinear_forward (one per device)
-struct Workspace {
-  void *ptr = nullptr;
-  size_t bytes = 0;
-};
-constexpr int kMaxDevices = 64;
-Workspace g_ws[kMaxDevices];
-std::mutex g_ws_mutex;
-
-int get_owned_workspace(size_t need, void **out) {
-  *out = nullptr;
-  if (need == 0) return QL_OK;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QL_EHIP;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace &w = g_ws[dev];
-  if (w.bytes < need) {
-    if (w.ptr) {
-      // earlier launches may still read the old buffer
-      if (hipDeviceSynchronize() != hipSuccess) return QL_EHIP;
-      if (hipFree(w.ptr) != hipSuccess) return QL_EHIP;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    const size_t sz = (size_t)round_up((int64_t)need, 1 << 20);
-    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
-      w.ptr = nullptr;
-      return QL_EHIP;
-    }
-    w.bytes = sz;
-  }
-  *out = w.ptr;
-  return QL_OK;
-}
-
 // ---- dispatch
 struct Plan {
   int path = QL_PATH_AUTO;
@@ -124,8 +89,16 @@ struct Plan {
   int groups_per_split = 0;
   size_t ws_xsum = 0, ws_partial = 0;
   size_t ws_x16 = 0;  // fast mode: fp16 x and per-row scales
+  bool copy = false;  // canonical 3-bit codes: the GEMM runs on a tiled copy in the workspace
   ql::Gemm2Plan g2{};
   ql::Gemm3Plan g3{};
+};
+
+// What a call brings besides the operands; it decides which plans need no
+// library scratch. scratch: a workspace is passed (scratch plans allowed);
+// x16, xsum: the caller's FAST activations / EXACT group sums.
+struct Caller {
+  bool scratch = false, x16 = false, xsum = false;
 };
 
 size_t ti_sizes(int tile) {
@@ -172,11 +145,25 @@ int choose_splits(int64_t tiles, int G) {
   return s < 1 ? 1 : s;
 }
 
-// Large-M fast-mode tile (gemm3.hip).
+// Large-M tiles of the FAST (gemm3.hip) and SPLIT (gemm4.hip) numerics.
 constexpr int kFastTile = 20;
+constexpr int kSplitTile = 30;
 
+// Workspace bytes of a tiled copy of canonical weights (codes, then scale|bias
+// words, each 256-byte aligned).
+size_t repack_ws_bytes(int bits, int64_t N, int64_t K) {
+  const int64_t n32 = round_up(N, 32);
+  return (size_t)round_up(n32 * K * bits / 32 * 4, 256) + (size_t)round_up(n32 * (K / kGroup) * 4, 256);
+}
+
+// Plans a forward call. Automatic numerics for the large-M path: FAST when
+// the call may use scratch (or brings its fp16 activations), SPLIT otherwise:
+// SPLIT needs no scratch unless K is split, and K is split only with a
+// workspace; a grid of fewer tiles than CUs that is not split along K is cut
+// into row pieces instead. Canonical 3-bit codes run every GEMM on a tiled copy in the
+// workspace.
 int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int force_split,
-              int force_tile, bool tiled, int mode, Plan *p) {
+              int force_tile, bool tiled, int mode, Caller c, Plan *p) {
   *p = Plan{};  // a re-plan into the same Plan keeps no field of the previous one
   const int G = (int)(K / kGroup);
   int path = force_path;
@@ -186,7 +173,7 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   }
   if (path == QL_PATH_AUTO) path = (M <= kMaxSkinnyM) ? QL_PATH_SKINNY : QL_PATH_GEMM;
   if (path == QL_PATH_SKINNY) {
-    if (M > kMaxSkinnyM || mode == QL_MODE_FAST) return QL_EUNSUPPORTED;
+    if (M > kMaxSkinnyM || mode == QL_MODE_FAST || mode == QL_MODE_SPLIT) return QL_EUNSUPPORTED;
     p->path = QL_PATH_SKINNY;
     p->mode = QL_MODE_EXACT;
     return QL_OK;
@@ -195,36 +182,42 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   int tile = force_tile > 0 ? force_tile : env_int("QLINEAR_TILE", 0);
   const ql::TileInfo *forced = tile > 0 ? ql::gemm_tile(tile) : nullptr;
   if (tile > 0 && !forced) return QL_EUNSUPPORTED;
+  // canonical codes on the FAST and SPLIT GEMMs are addressed with 32-bit byte offsets
+  const bool canon_big = !tiled && bits != 3 && N * (K * bits / 8) > (int64_t)INT32_MAX;
   if (mode == QL_MODE_AUTO) {
-    if (forced) mode = forced->gen == 3 ? QL_MODE_FAST : QL_MODE_EXACT;
-    else mode = tiled ? QL_MODE_FAST : QL_MODE_EXACT;
+    if (forced) mode = forced->gen == 3 ? QL_MODE_FAST : forced->gen == 4 ? QL_MODE_SPLIT : QL_MODE_EXACT;
+    else if (canon_big) mode = QL_MODE_EXACT;
+    else mode = (c.scratch || c.x16) ? QL_MODE_FAST : QL_MODE_SPLIT;
   }
-  if (mode != QL_MODE_EXACT && mode != QL_MODE_FAST) return QL_EINVAL;
+  if (mode != QL_MODE_EXACT && mode != QL_MODE_FAST && mode != QL_MODE_SPLIT) return QL_EINVAL;
   p->mode = mode;
-  if (mode == QL_MODE_FAST) {
-    // canonical codes: 2/4/8-bit, addressed with 32-bit byte offsets
-    if (!tiled && (bits == 3 || N * (K * bits / 8) > (int64_t)INT32_MAX)) return QL_EUNSUPPORTED;
-    if (forced && forced->gen != 3) return QL_EUNSUPPORTED;
+  // the GEMMs read 3-bit codes in the tiled layout only
+  p->copy = bits == 3 && !tiled;
+  if (p->copy) tiled = true;
+  if (mode == QL_MODE_FAST || mode == QL_MODE_SPLIT) {
+    const int gen = mode == QL_MODE_FAST ? 3 : 4;
+    if (canon_big) return QL_EUNSUPPORTED;
+    if (forced && forced->gen != gen) return QL_EUNSUPPORTED;
     int fs = force_split > 0 ? force_split : 0;
     if (path == QL_PATH_GEMM && force_path == QL_PATH_GEMM) fs = force_split > 0 ? force_split : 1;
     if (path == QL_PATH_SPLITK && fs < 2) fs = 2;
+    if (fs <= 0 && !c.scratch) fs = 1;  // no workspace: no K split
     if (fs > G) fs = G;
     // QLINEAR_GEMM_SLOTS: resident-block count override, for tests of the
     // tail pieces and K splits on small shapes
-    p->g3 = ql::gemm3_plan(M, N, G, env_int("QLINEAR_GEMM_SLOTS", 0), fs);
+    p->g3 = ql::gemm3_plan(M, N, G, env_int("QLINEAR_GEMM_SLOTS", 0), fs, true);
     if (path == QL_PATH_SPLITK && p->g3.splits < 2) return QL_EUNSUPPORTED;
     p->path = p->g3.splits > 1 ? QL_PATH_SPLITK : QL_PATH_GEMM;
-    p->tile = kFastTile;
+    p->tile = gen == 3 ? kFastTile : kSplitTile;
     p->splits = p->g3.splits;
     p->groups_per_split = G > 0 ? (G + p->splits - 1) / p->splits : 0;
-    p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
+    if (mode == QL_MODE_FAST && !c.x16) p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
     p->ws_partial = p->g3.partial_bytes;
     return QL_OK;
   }
-  if (forced && forced->gen == 3) return QL_EUNSUPPORTED;
-  // 3-bit codes: the GEMMs read the tiled layout (canonical 3-bit weights are
-  // repacked into the workspace first), second-generation tiles only
-  if (bits == 3 && (!tiled || (forced && forced->gen != 2))) return QL_EUNSUPPORTED;
+  if (forced && forced->gen >= 3) return QL_EUNSUPPORTED;
+  // 3-bit codes: second-generation tiles only
+  if (bits == 3 && forced && forced->gen != 2) return QL_EUNSUPPORTED;
   int splits = 0;
   if (tile <= 0) {
     for (const TableEntry &e : kTable) {
@@ -255,7 +248,7 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   p->tile = tile;
   p->splits = splits;
   p->groups_per_split = gps;
-  p->ws_xsum = (size_t)G * (size_t)round_up(M, 256) * 4u;
+  p->ws_xsum = c.xsum ? 0 : (size_t)G * (size_t)round_up(M, 256) * 4u;
   p->ws_partial = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4u : 0;
   if (ti->gen == 2) {
     // QLINEAR_GEMM_SLOTS: as above
@@ -265,33 +258,16 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   return QL_OK;
 }
 
-// Workspace bytes of a tiled copy of canonical weights (codes, then scale|bias
-// words, each 256-byte aligned).
-size_t repack_ws_bytes(int bits, int64_t N, int64_t K) {
-  const int64_t n32 = round_up(N, 32);
-  return (size_t)round_up(n32 * K * bits / 32 * 4, 256) + (size_t)round_up(n32 * (K / kGroup) * 4, 256);
-}
-
-// Canonical weights on a GEMM path may run on a tiled copy that the repack
-// kernel writes into the workspace (one read and one write of the weights per
-// call). 3-bit codes always take it: the GEMMs read 3-bit codes in the tiled
-// layout only. The other widths take it under automatic dispatch (no forced
-// path, tile or split) from kCopyMinM rows on, where the GEMMs on tiled codes
-// save more than the copy costs. Measured, exact GEMM at K = N = 4608, 4-bit:
-// M = 256 43 us direct against 40 + 10 us through the copy, M = 512 73 against
-// 61 + 11, M = 4096 341 against 255 + 11. The skinny kernel reads canonical
-// codes directly.
-constexpr int64_t kCopyMinM = 512;
-
-bool copy_route(const ql_forward_args *a) {
-  if (a->layout != QL_LAYOUT_CANONICAL) return false;
-  if (a->bits == 3) return true;
-  return a->M >= kCopyMinM && a->path == QL_PATH_AUTO && a->tile == 0 && a->split_k == 0;
-}
-
+// Scratch bytes a plan takes from the workspace (the tiled copy of canonical
+// 3-bit codes is added by the caller, it depends on N and K).
 size_t plan_ws(const Plan &p) {
   if (p.path == QL_PATH_SKINNY) return 0;
   return (size_t)round_up((int64_t)p.ws_xsum, 256) + (size_t)round_up((int64_t)p.ws_x16, 256) + p.ws_partial;
+}
+
+size_t plan_total_ws(const Plan &p, int bits, int64_t N, int64_t K) {
+  const size_t need = (size_t)round_up((int64_t)plan_ws(p), 256);
+  return need + (p.copy && p.path != QL_PATH_SKINNY ? repack_ws_bytes(bits, N, K) : 0);
 }
 
 int validate_forward(const ql_forward_args *a) {
@@ -301,12 +277,14 @@ int validate_forward(const ql_forward_args *a) {
   if (a->M > (1LL << 31) - 1 || a->N > (1LL << 31) - 1 || a->K > (1LL << 30)) return QL_EINVAL;
   if (a->out_dtype != QL_OUT_F32 && a->out_dtype != QL_OUT_BF16) return QL_EINVAL;
   if (a->layout != QL_LAYOUT_CANONICAL && a->layout != QL_LAYOUT_TILED) return QL_EINVAL;
-  if (a->mode != QL_MODE_AUTO && a->mode != QL_MODE_EXACT && a->mode != QL_MODE_FAST) return QL_EINVAL;
+  if (a->mode != QL_MODE_AUTO && a->mode != QL_MODE_EXACT && a->mode != QL_MODE_FAST && a->mode != QL_MODE_SPLIT)
+    return QL_EINVAL;
   if ((a->x16 == nullptr) != (a->rowscale == nullptr)) return QL_EINVAL;
   if (a->epilogue != QL_EPI_NONE && a->epilogue != QL_EPI_SWIGLU && a->epilogue != QL_EPI_GATE_RESIDUAL)
     return QL_EINVAL;
   if (a->epilogue != QL_EPI_NONE) {
-    if (a->mode == QL_MODE_EXACT || a->path == QL_PATH_SKINNY || a->path == QL_PATH_SPLITK || a->split_k > 1)
+    if (a->mode == QL_MODE_EXACT || a->mode == QL_MODE_SPLIT || a->path == QL_PATH_SKINNY ||
+        a->path == QL_PATH_SPLITK || a->split_k > 1)
       return QL_EUNSUPPORTED;
     // the GLU order is a tiled repack
     if (a->epilogue == QL_EPI_SWIGLU && a->layout != QL_LAYOUT_TILED) return QL_EUNSUPPORTED;
@@ -368,23 +346,43 @@ QL_API size_t qlinear_packed_words(int bits, int64_t N, int64_t K) {
 
 QL_API size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K) {
   if (!bits_ok(bits) || M <= 0 || N <= 0 || K <= 0 || K % kGroup) return 0;
-  // the larger of the canonical (exact) and tiled (fast) needs
-  Plan pc, pt;
+  // the largest need over both layouts and every numerics mode a call with a
+  // workspace may run under automatic path selection
+  Caller c;
+  c.scratch = true;
   size_t need = 0;
-  if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, false, QL_MODE_AUTO, &pc) == QL_OK) need = plan_ws(pc);
-  if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, QL_MODE_AUTO, &pt) == QL_OK && plan_ws(pt) > need)
-    need = plan_ws(pt);
-  if (bits == 3 || M >= kCopyMinM) {
-    // canonical weights on a GEMM path through a tiled copy: the plan on the copy plus the copy
-    for (int mode : {QL_MODE_EXACT, QL_MODE_FAST}) {
-      Plan pc3;
-      if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, true, mode, &pc3) == QL_OK && pc3.path != QL_PATH_SKINNY) {
-        const size_t nc = (size_t)round_up((int64_t)plan_ws(pc3), 256) + repack_ws_bytes(bits, N, K);
-        if (nc > need) need = nc;
-      }
+  for (bool tiled : {false, true})
+    for (int mode : {QL_MODE_AUTO, QL_MODE_EXACT, QL_MODE_FAST, QL_MODE_SPLIT}) {
+      Plan p;
+      if (make_plan(bits, M, N, K, QL_PATH_AUTO, 0, 0, tiled, mode, c, &p) != QL_OK) continue;
+      need = std::max(need, plan_total_ws(p, bits, N, K));
     }
+  // the fused epilogues run the FAST GEMM at every M, with no K split
+  for (bool tiled : {false, true}) {
+    Plan p;
+    if (make_plan(bits, M, N, K, QL_PATH_GEMM, 1, 0, tiled, QL_MODE_FAST, c, &p) == QL_OK)
+      need = std::max(need, plan_total_ws(p, bits, N, K));
   }
   return need;
+}
+
+QL_API size_t qlinear_forward_workspace_bytes(const ql_forward_args *a) {
+  if (!a) return 0;
+  // size the call as if it had a workspace: the pointer is only checked for alignment
+  ql_forward_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (validate_forward(&b) != QL_OK || b.M == 0 || b.N == 0 || b.K == 0) return 0;
+  Caller c;
+  c.scratch = true;
+  c.x16 = b.x16 != nullptr;
+  c.xsum = b.xsum != nullptr;
+  const bool fused = b.epilogue == QL_EPI_SWIGLU || b.epilogue == QL_EPI_GATE_RESIDUAL;
+  const bool tiled = b.layout == QL_LAYOUT_TILED;
+  Plan p;
+  const int st = fused ? make_plan(b.bits, b.M, b.N, b.K, QL_PATH_GEMM, 1, b.tile, tiled, QL_MODE_FAST, c, &p)
+                       : make_plan(b.bits, b.M, b.N, b.K, b.path, b.split_k, b.tile, tiled, b.mode, c, &p);
+  return st == QL_OK ? plan_total_ws(p, b.bits, b.N, b.K) : 0;
 }
 
 QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
@@ -412,45 +410,41 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                                                                                                         : QL_EHIP;
   }
   Plan p;
-  // canonical weights through a tiled copy (see copy_route)
-  const bool copy = copy_route(a);
-  const bool plan_tiled = a->layout == QL_LAYOUT_TILED || copy;
+  Caller c;
+  c.scratch = a->workspace != nullptr;
+  c.x16 = a->x16 != nullptr;
+  c.xsum = a->xsum != nullptr;
+  const bool tiled_in = a->layout == QL_LAYOUT_TILED;
   // the fused epilogues run on the FAST GEMM without a K split (they need
   // finished sums), at any M
-  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, plan_tiled, QL_MODE_FAST, &p)
-                      : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, plan_tiled, a->mode, &p);
+  st = (glu || gated) ? make_plan(a->bits, a->M, a->N, a->K, QL_PATH_GEMM, 1, a->tile, tiled_in, QL_MODE_FAST, c, &p)
+                      : make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, tiled_in, a->mode, c, &p);
   if (st != QL_OK) return st;
-  // AUTO keeps EXACT numerics on canonical weights (the plan above saw a tiled layout)
-  if (copy && a->mode == QL_MODE_AUTO && !(glu || gated) && p.path != QL_PATH_SKINNY && p.mode == QL_MODE_FAST) {
-    st = make_plan(a->bits, a->M, a->N, a->K, a->path, a->split_k, a->tile, true, QL_MODE_EXACT, &p);
-    if (st != QL_OK) return st;
-  }
   const int G = (int)(a->K / kGroup);
   const int out_bf16 = a->out_dtype == QL_OUT_BF16;
   char buf[160];
   if (p.path == QL_PATH_SKINNY) {
-    const bool tiled = a->layout == QL_LAYOUT_TILED;
     ql::SkinnyArgs s{static_cast<const uint16_t *>(a->x),
                      a->packed_q,
-                     tiled ? nullptr : static_cast<const uint16_t *>(a->scales),
-                     tiled ? nullptr : static_cast<const uint16_t *>(a->biases),
-                     tiled ? static_cast<const uint32_t *>(a->scales) : nullptr,
-                     a->out, a->M, a->N, a->K, G, out_bf16, tiled ? 1 : 0};
-    std::snprintf(buf, sizeof(buf), "skinny_b%d_m%lld_%s", a->bits, (long long)a->M, tiled ? "tiled" : "canonical");
+                     tiled_in ? nullptr : static_cast<const uint16_t *>(a->scales),
+                     tiled_in ? nullptr : static_cast<const uint16_t *>(a->biases),
+                     tiled_in ? static_cast<const uint32_t *>(a->scales) : nullptr,
+                     a->out, a->M, a->N, a->K, G, out_bf16, tiled_in ? 1 : 0};
+    std::snprintf(buf, sizeof(buf), "skinny_b%d_m%lld_%s", a->bits, (long long)a->M, tiled_in ? "tiled" : "canonical");
     set_last_path(buf);
     return ql::launch_skinny(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;
   }
+  const bool copy = p.copy;
+  const bool plan_tiled = tiled_in || copy;
   if (plan_tiled && !ql::gemm_tile_supports_tiled(p.tile)) return QL_EUNSUPPORTED;
-  if (p.mode == QL_MODE_FAST && a->x16) p.ws_x16 = 0;  // caller's fp16 activations
+  // scratch comes only from the caller's workspace: a plan that needs some
+  // without one is refused before anything is launched
   const size_t plan_need = (size_t)round_up((int64_t)plan_ws(p), 256);
-  const size_t need = plan_need + (copy ? repack_ws_bytes(a->bits, a->N, a->K) : 0);
+  const size_t need = plan_total_ws(p, a->bits, a->N, a->K);
   void *ws = a->workspace;
-  if (ws) {
-    if (a->workspace_bytes < need) return QL_EWORKSPACE;
+  if (need > 0) {
+    if (!ws || a->workspace_bytes < need) return QL_EWORKSPACE;
     if (!aligned16(ws)) return QL_EALIGN;
-  } else {
-    st = get_owned_workspace(need, &ws);
-    if (st != QL_OK) return st;
   }
   ql_forward_args tiled_args;
   if (copy) {
@@ -467,11 +461,14 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     tiled_args.layout = QL_LAYOUT_TILED;
     a = &tiled_args;
   }
-  if (p.mode == QL_MODE_FAST) {
-    const uint16_t *x16 = static_cast<const uint16_t *>(a->x16);
-    const float *rowscale = a->rowscale;
+  const bool canon = a->layout == QL_LAYOUT_CANONICAL;
+  const char *lay = canon ? "canonical" : (copy ? "tiled_copy" : "tiled");
+  if (p.mode == QL_MODE_FAST || p.mode == QL_MODE_SPLIT) {
+    const bool fast = p.mode == QL_MODE_FAST;
+    const uint16_t *x16 = static_cast<const uint16_t *>(fast ? a->x16 : a->x);
+    const float *rowscale = fast ? a->rowscale : nullptr;
     char *after = static_cast<char *>(ws) + round_up((int64_t)p.ws_x16, 256);
-    if (!x16) {
+    if (fast && !x16) {
       uint16_t *x16w = static_cast<uint16_t *>(ws);
       float *rsw = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up(a->M * a->K * 2, 256));
       if (ql::launch_x16(static_cast<const uint16_t *>(a->x), x16w, rsw, a->M, a->K, stream) != hipSuccess)
@@ -480,7 +477,6 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
       rowscale = rsw;
     }
     const bool split = p.g3.splits > 1;
-    const bool canon = a->layout == QL_LAYOUT_CANONICAL;
     float *partial = reinterpret_cast<float *>(after);
     ql::Gemm3Args g3{x16, rowscale, a->packed_q, static_cast<const uint32_t *>(a->scales),
                      split ? static_cast<void *>(partial) : a->out,
@@ -490,22 +486,23 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                      gated ? (int)std::min<int64_t>(a->gate_rows, a->M) : 0,
                      canon ? 1 : 0, canon ? static_cast<const uint16_t *>(a->scales) : nullptr,
                      canon ? static_cast<const uint16_t *>(a->biases) : nullptr};
-    const char *lay = canon ? "canonical" : (copy ? "tiled_copy" : "tiled");
+    const char *kname = fast ? "gemm3_f16" : "gemm4_bf16x2";
     if (gated)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_gate_%s", a->bits, p.g3.tail_tiles > 0 ? "_tail" : "",
+      std::snprintf(buf, sizeof(buf), "%s_256x256_b%d%s_gate_%s", kname, a->bits, p.g3.tail_tiles > 0 ? "_tail" : "",
                     lay);
     else if (glu)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d%s_swiglu_tiled", a->bits,
+      std::snprintf(buf, sizeof(buf), "%s_256x256_b%d%s_swiglu_tiled", kname, a->bits,
                     p.g3.tail_tiles > 0 ? "_tail" : "");
     else if (split)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_split%d_%s", a->bits, p.g3.splits, lay);
+      std::snprintf(buf, sizeof(buf), "%s_256x256_b%d_split%d_%s", kname, a->bits, p.g3.splits, lay);
     else if (p.g3.tail_tiles > 0)
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_tail%dx%d_%s", a->bits, p.g3.tail_tiles,
+      std::snprintf(buf, sizeof(buf), "%s_256x256_b%d_tail%dx%d_%s", kname, a->bits, p.g3.tail_tiles,
                     16 / p.g3.tail_mi, lay);
     else
-      std::snprintf(buf, sizeof(buf), "gemm3_f16_256x256_b%d_%s", a->bits, lay);
+      std::snprintf(buf, sizeof(buf), "%s_256x256_b%d_%s", kname, a->bits, lay);
     set_last_path(buf);
-    if (ql::launch_gemm3(a->bits, g3, stream) != hipSuccess) return QL_EHIP;
+    const hipError_t le = fast ? ql::launch_gemm3(a->bits, g3, stream) : ql::launch_gemm4(a->bits, g3, stream);
+    if (le != hipSuccess) return QL_EHIP;
     if (split && ql::launch_splitk_reduce(partial, p.g3.splits, a->M, a->N, a->out, out_bf16, stream) != hipSuccess)
       return QL_EHIP;
     return QL_OK;
@@ -544,10 +541,9 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   const ql::TileInfo *ti = ql::gemm_tile(p.tile);
   if (p.g2.sk_tiles > 0)
     std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_tail%dx%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
-                  p.g2.sk_tiles, p.g2.sk_pieces, tiled ? (copy ? "tiled_copy" : "tiled") : "canonical");
+                  p.g2.sk_tiles, p.g2.sk_pieces, lay);
   else
-    std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_%s", ti ? ti->name : "gemm", a->bits, p.splits,
-                  tiled ? (copy ? "tiled_copy" : "tiled") : "canonical");
+    std::snprintf(buf, sizeof(buf), "%s_b%d_split%d_%s", ti ? ti->name : "gemm", a->bits, p.splits, lay);
   set_last_path(buf);
   const hipError_t le = (ti && ti->gen == 2) ? ql::launch_gemm2(a->bits, p.tile, tiled, g, stream)
                                              : ql::launch_gemm(a->bits, p.tile, g, stream);

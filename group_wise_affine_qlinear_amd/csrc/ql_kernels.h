@@ -31,7 +31,7 @@ struct TileInfo {
   int id, bm, bn, warps_m, warps_n;
   const char *name;
   int gen;  // 1: gemm.hip (canonical, exact), 2: gemm2.hip (either layout, exact),
-            // 3: gemm3.hip (tiled, fast)
+            // 3: gemm3.hip (either layout, fast), 4: gemm4.hip (either layout, split bf16)
 };
 
 // GEMM tile configurations compiled into the library (id >= 1).
@@ -86,10 +86,15 @@ struct Gemm3Plan {
   size_t partial_bytes;   // splits > 1: fp32 [splits, M, N]
 };
 // slots <= 0: one block per CU of the current device; force_splits > 0 fixes
-// the K split
-Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits);
+// the K split. fill_by_pieces: with fewer tiles than slots and no K split,
+// cut every tile along M into row pieces so the grid covers the CUs (needs no
+// scratch, unlike a K split).
+Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits, bool fill_by_pieces = false);
 hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream);
 hipError_t launch_gemm3(int bits, const Gemm3Args &a, hipStream_t stream);
+// SPLIT numerics (gemm4.hip): same arguments, x16 holds the caller's bf16 x,
+// rowscale is unused, glu and gate must be off.
+hipError_t launch_gemm4(int bits, const Gemm3Args &a, hipStream_t stream);
 
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N,
                                 void *out, int out_bf16, hipStream_t stream);

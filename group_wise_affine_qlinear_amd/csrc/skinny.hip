@@ -410,13 +410,10 @@ hipError_t launch_mr(const SkinnyArgs &a, hipStream_t stream) {
   constexpr int RING = (kBatched && MR == 1 && BITS != 8) ? 8 : RING_T;
   static_assert(RING % BATCH == 0, "the ring refills whole batches");
   auto kern = skinny_kernel<BITS, MR, RING, TILED, XB, SB, BATCH>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (cheap; the library keeps no per-device state)
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (e != hipSuccess) return e;
   const unsigned blocks = (unsigned)((a.N + 32 * kStrips - 1) / (32 * kStrips));
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, a, chunk);
   return hipGetLastError();

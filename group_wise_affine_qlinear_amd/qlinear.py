@@ -21,7 +21,7 @@ QL_OK, QL_EINVAL, QL_EALIGN, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP, QL_ERANGE 
 QL_OUT_F32, QL_OUT_BF16 = 0, 1
 QL_PATH_AUTO, QL_PATH_SKINNY, QL_PATH_GEMM, QL_PATH_SPLITK = 0, 1, 2, 3
 QL_LAYOUT_CANONICAL, QL_LAYOUT_TILED = 0, 1
-QL_MODE_AUTO, QL_MODE_EXACT, QL_MODE_FAST = 0, 1, 2
+QL_MODE_AUTO, QL_MODE_EXACT, QL_MODE_FAST, QL_MODE_SPLIT = 0, 1, 2, 3
 QL_EPI_NONE, QL_EPI_SWIGLU, QL_EPI_GATE_RESIDUAL = 0, 1, 2
 
 EXPORTED = (
@@ -30,7 +30,7 @@ EXPORTED = (
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
     "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
     "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations", "qlinear_repack_glu",
-    "qlinear_unrepack_glu", "qlinear_quantize_imatrix",
+    "qlinear_unrepack_glu", "qlinear_quantize_imatrix", "qlinear_forward_workspace_bytes",
 )
 
 
@@ -96,6 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_forward": ([vp, vp, vp, vp, i32, i32, i64, i64, i64, vp], i32),
         "qlinear_forward_ex": ([ctypes.POINTER(ql_forward_args), vp], i32),
         "qlinear_workspace_bytes": ([i32, i64, i64, i64], sz),
+        "qlinear_forward_workspace_bytes": ([ctypes.POINTER(ql_forward_args)], sz),
         "qlinear_packed_words": ([i32, i64, i64], sz),
         "qlinear_pack_host": ([vp, i32, i64, i64, vp], i32),
         "qlinear_unpack_host": ([vp, i32, i64, i64, vp], i32),
@@ -183,8 +184,13 @@ def qlinear_forward(x, packed_q, scales, biases, bits, group, M, N, K, out):
     return out
 
 
+# Default of ``qlinear_forward_ex(workspace=...)``: a workspace of
+# ``qlinear_workspace_bytes`` taken from torch's caching allocator for the call.
+TORCH_WORKSPACE = "torch"
+
+
 def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group=64,
-                       workspace=None, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
+                       workspace=TORCH_WORKSPACE, stream=None, path=QL_PATH_AUTO, split_k=0, tile=0,
                        xsum=None, layout=QL_LAYOUT_CANONICAL, mode=QL_MODE_AUTO, x16=None,
                        rowscale=None, epilogue=QL_EPI_NONE, residual=None, gate=None, gate_rows=0):
     """C ``qlinear_forward_ex``: explicit stream, workspace, out dtype, layout, numerics mode
@@ -192,7 +198,11 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
 
     With ``layout=QL_LAYOUT_TILED``, ``packed_q`` and ``scales`` are the outputs of
     ``qlinear_repack`` (tiled codes, tiled scale|bias words) and ``biases`` is ignored.
-    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights);
+    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights when a
+    workspace is passed, SPLIT otherwise). ``workspace`` is a device tensor the library may use
+    as scratch, ``None`` (the call keeps to plans that need none, as the C call with a NULL
+    workspace), or by default a tensor of ``qlinear_workspace_bytes`` bytes that torch's caching
+    allocator provides on the call's stream (the library itself never allocates);
     ``x16``/``rowscale`` are optional FAST-mode activations from ``qlinear_fast_activations``.
     ``epilogue=QL_EPI_SWIGLU`` takes GLU-ordered tiled weights (``qlinear_repack_glu``) and
     writes ``out`` [M, N/2] = silu(gate) * up. ``epilogue=QL_EPI_GATE_RESIDUAL`` writes
@@ -223,9 +233,13 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
         raise TypeError("out must be float32 or bfloat16")
     a.epilogue = epilogue
     a.out = _dev_ptr(out, "out", (out.dtype,), (M, N // 2 if epilogue == QL_EPI_SWIGLU else N))
-    if workspace is not None:
-        a.workspace = _dev_ptr(workspace, "workspace", (workspace.dtype,))
-        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if isinstance(workspace, str):
+        if workspace != TORCH_WORKSPACE:
+            raise ValueError(f"workspace must be a device tensor, None or {TORCH_WORKSPACE!r}")
+        workspace = None
+        nbytes = -1   # sized below, once every field of the call is set
+    else:
+        nbytes = None
     a.path, a.split_k, a.tile, a.mode = path, split_k, tile, mode
     if xsum is not None:
         a.xsum = _dev_ptr(xsum, "xsum", (torch.float32,))
@@ -241,6 +255,17 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
     if x16 is not None:
         a.x16 = _dev_ptr(x16, "x16", (torch.float16, torch.int16), (M, K))
         a.rowscale = _dev_ptr(rowscale, "rowscale", (torch.float32,), (M,))
+    if nbytes == -1:
+        nbytes = int(lib.qlinear_forward_workspace_bytes(ctypes.byref(a)))
+        if nbytes > 0:
+            # allocated on the current stream; a call on another stream marks
+            # the tensor in use there so the allocator does not hand it out early
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+            if stream is not None and not isinstance(stream, int):
+                workspace.record_stream(stream)
+    if workspace is not None:
+        a.workspace = _dev_ptr(workspace, "workspace", (workspace.dtype,))
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib.qlinear_forward_ex(ctypes.byref(a), _stream_handle(stream))
     _check(st, "qlinear_forward_ex")
     return out

@@ -14,10 +14,10 @@
  * serve the mixed-precision packs of the IQ4_M card (3-bit DiT bulk with
  * 8-bit modulation and conditioning; sections "Against the pack this
  * replaces" and "Conversion"). They run on every path: the skinny kernel
- * reads either layout; the GEMMs (exact and FAST) read the TILED layout, so
- * a GEMM call on canonical 3-bit weights first repacks them into the
- * workspace (one extra pass over the weights per call; repack once at load
- * with qlinear_repack to avoid it).
+ * reads either layout; the GEMMs read the TILED layout, so a GEMM call on
+ * canonical 3-bit weights first repacks them into the workspace (one extra
+ * pass over the weights per call; repack once at load with qlinear_repack to
+ * avoid it).
  *
  * Conventions for every entry point:
  *  - Pointers whose name ends in _host are host memory; all others are device
@@ -71,44 +71,54 @@ typedef enum { QL_OUT_F32 = 0, QL_OUT_BF16 = 1 } ql_out_dtype;
  * codes form one contiguous block (4-bit 1 KB, 8-bit 2 KB, 2-bit 512 B, 3-bit
  * 768 B: the low two bits as a 2-bit block, then a plane of high bits) and
  * the scale and bias become one uint32 (s | b << 16) per row and group, so a
- * wave's loads cover whole cache lines.
- * Under automatic dispatch (path, tile and split_k all 0), a call on
- * CANONICAL weights with M >= 512 first writes a TILED copy of them into the
- * workspace and runs the GEMM on it (the copy is one pass over the weights;
- * from 512 rows on the GEMM on tiled codes saves more than that). 3-bit
- * weights take this copy on every GEMM path. Results equal those of the same
- * call on weights repacked with qlinear_repack, bit for bit; the path name
- * reported by qlinear_last_path then ends in "_tiled_copy". Forced paths,
- * tiles or splits (2/4/8-bit) run the kernels on the canonical code rows.
+ * wave's loads cover whole cache lines. Every path reads 2/4/8-bit codes in
+ * either layout directly. The large-M GEMMs read 3-bit codes in the tiled
+ * layout only: a GEMM call on CANONICAL 3-bit weights first writes a tiled
+ * copy of them into the workspace (one pass over the weights per call; it
+ * needs a workspace, and the path name ends in "_tiled_copy"). Repack 3-bit
+ * weights once at load with qlinear_repack to avoid it.
  */
 typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
 
 /*
- * Numerics of the large-M GEMM path.
+ * Numerics of the large-M GEMM path. Every mode computes the product with the
+ * weights of the format above; they differ in how the weights meet the MFMA.
  * EXACT: codes enter the bf16 MFMA as exact integers and each group's scale
  *   and bias are applied to the fp32 accumulator; the only rounding is fp32
  *   accumulation (relative Frobenius error ~1e-6 against an fp64 product).
+ *   Needs per-group row sums of x: K/64 * roundup(M, 256) floats of workspace
+ *   unless the caller passes them (qlinear_group_sums, xsum).
+ * SPLIT: each weight is dequantized in fp32 exactly as defined above,
+ *   W = s*q + b (one rounding), split into two bf16 terms hi = bf16(W) and
+ *   lo = bf16(W - hi) (round to nearest even; |W - hi - lo| <= 2^-16 |W|),
+ *   and both terms go through the bf16 MFMA against bf16 x with fp32
+ *   accumulation (relative Frobenius error ~1e-5). Reads x as given, needs no
+ *   scratch unless K is split, and holds for any finite weights and x.
  * FAST: each weight is dequantized once per block tile to fp16 with a single
  *   rounding, W16 = fp16(s*q + b), and x enters as fp16 after scaling each
  *   row by the power of two 2^-e that brings its largest magnitude into
  *   [2^14, 2^15), exact for every scaled value of magnitude >= 2^-14 (every
  *   value within 2^28 of the row's largest); outputs are scaled back by 2^e
- *   and accumulated in fp32 on fp16 MFMA. The added error
- *   is the half-ulp of fp16 on W (relative Frobenius error ~2e-4 on normal
- *   weights). Runs on TILED weights, or on CANONICAL 2/4/8-bit weights of
- *   fewer than 2^31 code bytes (the same kernel reading each row's code
- *   stream; identical results, slower: strided code loads; under automatic
- *   dispatch with M >= 512 canonical weights run on a tiled copy, see
- *   ql_layout), and requires
- *   |W| < 65504, which holds for weights quantized from fp16-range values
- *   (W lies between b and b + (2^bits - 1)*s). Uses M*K*2 + M*4 workspace bytes for the fp16 x
- *   unless the caller passes it (qlinear_fast_activations, x16/rowscale),
- *   plus splits*M*N*4 bytes of fp32 partials when K is split.
- * AUTO: FAST for the large-M paths (GEMM, SPLITK) on TILED weights, EXACT
- *   otherwise (also when CANONICAL weights run on a tiled copy). The skinny
- *   (M <= 16) path is always EXACT.
+ *   and accumulated in fp32 on fp16 MFMA. The added error is the half-ulp of
+ *   fp16 on W (relative Frobenius error ~2e-4 on normal weights). A column
+ *   whose weights could reach the fp16 limit (max over its groups of
+ *   max(|b|, |b + (2^bits - 1)*s|) >= 65504) has its fp16 weights scaled by
+ *   a power of two 2^-c and its outputs by 2^c, so any finite f16 scale and
+ *   bias are served (such a column's weights are then exact to one rounding
+ *   relative to its largest magnitude). Runs on either layout (canonical
+ *   2/4/8-bit codes of fewer than 2^31 code bytes; slower than tiled: strided
+ *   code loads). Uses M*K*2 + M*4 workspace bytes for the fp16 x unless the
+ *   caller passes it (qlinear_fast_activations, x16/rowscale).
+ * A K split (few output tiles, long K) adds splits*M*N*4 bytes of fp32
+ *   partials to any mode's workspace.
+ * AUTO: FAST when the call has a workspace (or its own fp16 activations),
+ *   SPLIT otherwise (EXACT for canonical codes of 2^31 bytes or more). The
+ *   skinny (M <= 16) path is always EXACT and needs no workspace. Without a
+ *   workspace K is never split. A grid of fewer 256 x 256 tiles than CUs that
+ *   is not split along K is cut into row pieces of 128, 64 or 32 rows instead
+ *   (long-K, few-row shapes run slower than with a workspace's K split).
  */
-typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2 } ql_mode;
+typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2, QL_MODE_SPLIT = 3 } ql_mode;
 
 /*
  * Fused epilogues.
@@ -157,8 +167,11 @@ typedef struct ql_forward_args {
   int64_t M, N, K;
   void *out;                 /* [M, N] ([M, N/2] with QL_EPI_SWIGLU), dtype per out_dtype */
   int out_dtype;             /* ql_out_dtype                                 */
-  void *workspace;           /* device scratch, may be NULL if ws_bytes==0   */
-  size_t workspace_bytes;    /* >= qlinear_workspace_bytes(...)              */
+  void *workspace;           /* device scratch owned by the caller, or NULL:
+                                NULL restricts the call to plans that need
+                                no scratch (see qlinear_forward_ex)         */
+  size_t workspace_bytes;    /* bytes at workspace; qlinear_workspace_bytes()
+                                is enough for every plan of the shape       */
   int path;                  /* ql_path; QL_PATH_AUTO unless testing         */
   int split_k;               /* 0 = auto; >0 forces the K split count        */
   int tile;                  /* 0 = auto; >0 forces a GEMM tile id (tests)   */
@@ -169,11 +182,10 @@ typedef struct ql_forward_args {
   int layout;                /* ql_layout. For QL_LAYOUT_TILED, packed_q holds
                                 the tiled codes, scales the tiled scale|bias
                                 words, and biases is ignored                */
-  int mode;                  /* ql_mode; FAST needs a large-M path (AUTO
-                                with M > 16, GEMM or SPLITK), else
-                                QL_EUNSUPPORTED; canonical 3-bit codes run
-                                on a tiled copy in the workspace; xsum is
-                                unused in FAST                              */
+  int mode;                  /* ql_mode; FAST and SPLIT need a large-M path
+                                (AUTO with M > 16, GEMM or SPLITK), else
+                                QL_EUNSUPPORTED; xsum is used by EXACT only,
+                                x16/rowscale by FAST only                   */
   const void *x16;           /* optional, FAST only: fp16 [M, K] activations
                                 and                                         */
   const float *rowscale;     /* [M] row scales from qlinear_fast_activations
@@ -186,20 +198,32 @@ typedef struct ql_forward_args {
 } ql_forward_args;
 
 /*
- * y = x @ W_hat^T with W_hat defined above, fp32 out, default stream.
+ * y = x @ W_hat^T with W_hat defined above, fp32 out, default stream; the
+ * call of the method's spec form (x, packed_q, scales, biases, bits,
+ * group, M, N, K, out) on canonical weights.
  * M, N >= 0 (0 is a no-op), K >= 0 and a multiple of 64 (K == 0 writes zeros),
- * group must be 64. Scratch memory the kernels need (per-group row sums of x,
- * split-K partials and, from 512 rows on, the tiled copy of the weights
- * described at ql_layout) comes from a library-owned per-device buffer that is
- * grown on demand with hipMalloc; calls on one device therefore must not
- * overlap in time (use qlinear_forward_ex with your own workspace for that).
+ * group must be 64. The call allocates no memory and uses no scratch: M <= 16
+ * runs the skinny kernel, larger M the SPLIT GEMM without a K split (see
+ * ql_mode; few-tile shapes run as row pieces). The library holds no buffers or other state between calls, so
+ * concurrent calls on different streams are independent. The one case that
+ * needs scratch, canonical 3-bit codes with M > 16 (tiled copy, see
+ * ql_layout), returns QL_EWORKSPACE: use qlinear_forward_ex with a workspace,
+ * or repack the weights.
  */
 int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales,
                     const void *biases, int bits, int group, int64_t M, int64_t N,
                     int64_t K, float *out);
 
-/* Same product with explicit stream, workspace, output dtype and path. If
- * args->workspace is NULL the library-owned buffer is used as above. */
+/* Same product with explicit stream, workspace, output dtype, layout, numerics
+ * mode, fused epilogue and forced path (tests). Scratch comes only from
+ * args->workspace, which the caller owns and sizes with
+ * qlinear_workspace_bytes; the library never allocates device memory and
+ * never synchronizes. With a NULL workspace automatic selection keeps to
+ * plans that need none (no K split, SPLIT numerics on the large-M path
+ * unless FAST activations are passed); a request that still needs scratch
+ * (EXACT without xsum, FAST or an epilogue without x16, a forced K split,
+ * canonical 3-bit GEMMs) returns QL_EWORKSPACE before anything is launched.
+ * Calls that share one workspace must not overlap in time. */
 int qlinear_forward_ex(const ql_forward_args *args, void *stream);
 
 /*
@@ -231,11 +255,17 @@ int64_t qlinear_group_sums_ld(int64_t M);
  */
 int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x16, float *rowscale, void *stream);
 
-/* Bytes of device workspace qlinear_forward_ex needs for this shape under
- * automatic dispatch (an upper bound over all paths and splits it may pick;
- * for 3-bit codes, and for M >= 512, it includes the tiled copy of canonical
- * weights). */
+/* Bytes of device workspace that serve every qlinear_forward_ex call of this
+ * shape with automatic path, tile and split, under any numerics mode, layout
+ * or epilogue (an upper bound over the plans; for 3-bit codes it includes the
+ * tiled copy of canonical weights). 0 for invalid arguments. */
 size_t qlinear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K);
+
+/* Bytes of workspace the call described by args needs when it is given a
+ * workspace (args->workspace and args->workspace_bytes are not read): exact
+ * for forced paths, tiles and splits as well, 0 when the plan needs none or
+ * the arguments are invalid. */
+size_t qlinear_forward_workspace_bytes(const ql_forward_args *args);
 
 /* Number of uint32 words of packed codes for an [N, K] weight: N*K*bits/32. */
 size_t qlinear_packed_words(int bits, int64_t N, int64_t K);

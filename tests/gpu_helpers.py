@@ -87,3 +87,24 @@ def assert_parity(y_gpu, y_ref, design=True, what=""):
     if design:
         assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, (what, e)
     return e
+
+
+def assert_rows(y_gpu, y_ref, relf=RELF_TOL, maxabs=MAXABS_RMS_TOL, what="", axis=0):
+    """Acceptance bar on the whole result and on every row (axis=0) or column
+    (axis=1) against that slice's own scale: rows of x, or columns of the
+    weights, may differ in magnitude by many orders. A slice whose reference
+    is all zero must come back exactly zero."""
+    y = np.asarray(y_gpu, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    e = oracle.error_metrics(y, r)
+    assert e["relF"] <= relf and e["maxabs_over_rms"] <= maxabs, (what, e)
+    if axis == 1:
+        y, r = y.T, r.T
+    for i in range(r.shape[0]):
+        if not np.any(r[i]):
+            assert not np.any(y[i]), (what, "zero slice", i)
+            continue
+        ei = oracle.error_metrics(y[i:i + 1], r[i:i + 1])
+        assert ei["relF"] <= relf and ei["maxabs_over_rms"] <= maxabs, (what, "slice", i, ei)
+    return e

@@ -3,9 +3,10 @@
 paths at full size on sampled outputs.
 
 3-bit codes run everywhere: the skinny kernel reads either layout; the GEMMs
-(exact and FAST) read the tiled layout, and canonical 3-bit weights on a GEMM
-path are repacked into the workspace first. Forced first-generation tiles
-return QL_EUNSUPPORTED."""
+(EXACT, FAST and SPLIT) read the tiled layout, and canonical 3-bit weights on
+a GEMM path are repacked into the workspace first (without a workspace such a
+call returns QL_EWORKSPACE). Forced first-generation tiles return
+QL_EUNSUPPORTED."""
 import numpy as np
 import pytest
 
@@ -32,9 +33,13 @@ def torch():
 def test_3bit_requests_and_paths(torch):
     c = Case(64, 256, 256, 3, wid=620)
     ref = c.reference()
-    y = run_forward(torch, c, via_ex=False)              # canonical entry point: exact, via a tiled copy
-    assert ql.qlinear_last_path().startswith("gemm2") and ql.qlinear_last_path().endswith("_tiled_copy")
-    assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
+    with pytest.raises(ql.QLinearError) as e:      # canonical 3-bit GEMM without a workspace: the copy needs one
+        run_forward(torch, c, via_ex=False)
+    assert e.value.status == ql.QL_EWORKSPACE
+    for mode, kname in ((ql.QL_MODE_EXACT, "gemm2"), (ql.QL_MODE_SPLIT, "gemm4_bf16x2")):
+        y = run_forward(torch, c, mode=mode)          # canonical 3-bit: the GEMM on a tiled copy in the workspace
+        assert ql.qlinear_last_path().startswith(kname) and ql.qlinear_last_path().endswith("_tiled_copy")
+        assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
     y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
     assert ql.qlinear_last_path().startswith("gemm2"), ql.qlinear_last_path()
     assert_parity(y.cpu().numpy(), ref, what=ql.qlinear_last_path())
@@ -104,12 +109,13 @@ def test_3bit_full_size_sampled(torch, name):
     else:
         assert path.startswith("skinny_b3"), path
         assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, (path, e)
-    # the canonical entry point on the same 3-bit weights (exact numerics)
+    # the same 3-bit weights in the canonical layout, SPLIT numerics (the GEMM
+    # runs on a tiled copy in the workspace; the skinny kernel reads them directly)
     pc = torch.from_numpy(packed.view(np.int32)).cuda()
     sc = torch.from_numpy(s16.view(np.int16)).cuda()
     bc = torch.from_numpy(b16.view(np.int16)).cuda()
     out.fill_(float("nan"))
-    ql.qlinear_forward(xd, pc, sc, bc, 3, 64, M, N, K, out)
+    ql.qlinear_forward_ex(xd, pc, sc, bc, 3, M, N, K, out, mode=ql.QL_MODE_SPLIT if M > 16 else ql.QL_MODE_AUTO)
     torch.cuda.synchronize()
     blk = out.index_select(0, ri).index_select(1, ci).cpu().numpy()
     e = oracle.error_metrics(blk, ref)

@@ -1,18 +1,20 @@
-"""GPU tests of the FAST numerics mode (fp16 dequant-GEMM on tiled weights).
+"""GPU tests of the FAST numerics mode (fp16 dequant-GEMM).
 
-Each case is compared twice: with the oracle's written-out definition of the
-mode (``oracle.forward_fast``: weights rounded once to fp16, rows scaled by a
-power of two into fp16), where only fp32 accumulation separates the two, and
-with the exact product (``oracle.forward``) under the acceptance bound and the
-mode's own error budget (fp16 half-ulp on the weights)."""
+Every case is compared with the oracle's plain fp64 product (``oracle.forward``,
+the format's definition) at the acceptance bar, on the whole result and row by
+row against each row's own scale, and under the mode's error budget (fp16
+half-ulp on the weights). Cases are also compared with the oracle's
+written-out model of the mode (``oracle.forward_fast``: weights rounded once
+to fp16, rows scaled by a power of two into fp16), where only fp32
+accumulation separates the two."""
 import numpy as np
 import pytest
 
 import oracle
 from group_wise_affine_qlinear_amd import inputs, qlinear as ql
 
-from gpu_helpers import (Case, MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, assert_parity, dev,
-                         run_forward, torch_or_skip)
+from gpu_helpers import (Case, MAXABS_RMS_DESIGN, MAXABS_RMS_TOL, RELF_DESIGN, RELF_TOL, assert_parity, assert_rows,
+                         dev, run_forward, torch_or_skip)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +38,9 @@ def check_fast(y, c):
     ref_def = oracle.forward_fast(c.x, c.packed, c.s16, c.b16, c.bits, c.K)
     e = oracle.error_metrics(y, ref_def)
     assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, ("vs definition", e)
-    e2 = oracle.error_metrics(y, c.reference())
-    assert e2["relF"] <= RELF_TOL and e2["maxabs_over_rms"] <= MAXABS_RMS_TOL, ("vs exact, acceptance", e2)
+    ref = c.reference()
+    assert_rows(y, ref, what="vs exact, acceptance, row by row")
+    e2 = oracle.error_metrics(y, ref)
     assert e2["relF"] <= RELF_FAST and e2["maxabs_over_rms"] <= MAXABS_RMS_FAST, ("vs exact, budget", e2)
 
 
@@ -54,12 +57,17 @@ def test_fast_parity(torch, shape, bits):
     check_fast(y.cpu().numpy(), c)
 
 
-def test_fast_is_auto_choice_for_tiled_large_m(torch):
+def test_fast_is_auto_choice_with_a_workspace(torch):
     c = Case(64, 256, 256, 4, wid=410)
     run_forward(torch, c, layout=ql.QL_LAYOUT_TILED)
     assert ql.qlinear_last_path().startswith("gemm3")
     run_forward(torch, c)
-    assert not ql.qlinear_last_path().startswith("gemm3")
+    assert ql.qlinear_last_path().startswith("gemm3") and ql.qlinear_last_path().endswith("_canonical")
+    # no workspace and no fp16 activations: the scratch-free SPLIT GEMM
+    x, p, s, b = c.device(torch)
+    out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    ql.qlinear_forward_ex(x, p, s, b, 4, c.M, c.N, c.K, out, workspace=None)
+    assert ql.qlinear_last_path().startswith("gemm4_bf16x2"), ql.qlinear_last_path()
     run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
     assert ql.qlinear_last_path().startswith("gemm2")
     c8 = Case(8, 256, 256, 4, wid=411)   # skinny M is always exact
@@ -88,6 +96,8 @@ def test_fast_rows_scaled_into_fp16_range(torch):
     for r in range(M):   # row by row: the rows differ in scale by 10^5
         e = oracle.error_metrics(y[r:r + 1], ref_def[r:r + 1])
         assert e["relF"] <= RELF_DESIGN, (r, e)
+    # and against the plain product, each row at its own scale
+    assert_rows(y, c.reference(), what="vs exact, row by row")
 
 
 def test_fast_one_hot_rows_give_fp16_weights_exactly(torch):
@@ -99,6 +109,10 @@ def test_fast_one_hot_rows_give_fp16_weights_exactly(torch):
     y = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST).cpu().numpy()
     w16 = oracle.fast_weights_f16(c.q, c.s16, c.b16).astype(np.float32)
     assert np.array_equal(y, w16[:, cols].T)
+    # against the format's definition: each returned weight lies within the
+    # fp16 half-ulp (2^-11 relative, or 2^-25 absolute below 2^-14) of W_hat
+    w_hat = oracle.dequantize(c.q, c.s16, c.b16).astype(np.float64)[:, cols].T
+    assert np.all(np.abs(y - w_hat) <= np.maximum(np.abs(w_hat) * 2.0 ** -11, 2.0 ** -25))
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
@@ -156,6 +170,7 @@ def test_fast_prepass_row_widths(torch, K):
     for r in range(M):
         e = oracle.error_metrics(y[r:r + 1], ref_def[r:r + 1])
         assert e["relF"] <= RELF_DESIGN, (r, e)
+    assert_rows(y, c.reference(), what="vs exact, row by row")
 
 
 def test_fast_activations_match_definition_bitwise(torch):
@@ -235,9 +250,7 @@ def test_fast_canonical_equals_tiled(torch, monkeypatch, case, bits):
     if slots:
         monkeypatch.setenv("QLINEAR_GEMM_SLOTS", str(slots))
     c = Case(M, N, K, bits, wid=470 + bits, x_structure="outlier")
-    # from 512 rows on, automatic dispatch runs canonical weights on a tiled
-    # copy: force the GEMM path there to test the kernel on the code rows
-    path = ql.QL_PATH_SPLITK if splits else (ql.QL_PATH_GEMM if M >= 512 else ql.QL_PATH_AUTO)
+    path = ql.QL_PATH_SPLITK if splits else ql.QL_PATH_AUTO
     yt = run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_FAST, path=path, split_k=splits)
     pt = ql.qlinear_last_path()
     yc = run_forward(torch, c, mode=ql.QL_MODE_FAST, path=path, split_k=splits)
@@ -252,5 +265,5 @@ def test_fast_canonical_bf16_and_auto_mode(torch):
     y = run_forward(torch, c, mode=ql.QL_MODE_FAST).cpu().numpy()
     yb = run_forward(torch, c, mode=ql.QL_MODE_FAST, out_dtype="bf16")
     assert np.array_equal(yb.view(torch.int16).cpu().numpy().view(np.uint16), inputs.f32_to_bf16_bits(y))
-    run_forward(torch, c)   # AUTO on canonical weights stays exact
-    assert not ql.qlinear_last_path().startswith("gemm3"), ql.qlinear_last_path()
+    run_forward(torch, c)   # AUTO with a workspace: FAST on canonical weights too
+    assert ql.qlinear_last_path().startswith("gemm3"), ql.qlinear_last_path()

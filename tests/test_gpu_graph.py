@@ -1,12 +1,12 @@
 """GPU test: the forward path inside a captured HIP graph.
 
-A serving loop can capture its projections once and replay them. Every
-launch here takes a caller workspace (no allocation during capture) and the
-library records no memset, so the sequence below (fp16 activations, the FAST
-GEMM plain and with both fused epilogues, the exact-mode GEMM with a K split,
-the skinny kernel) is captured on a side stream and replayed several times,
-with eager work and synchronizations between replays; every replay must give
-the eager results bit for bit."""
+A serving loop can capture its projections once and replay them. The library
+allocates nothing and records no memset, so the sequence below (fp16
+activations, the FAST GEMM plain and with both fused epilogues, the exact-mode
+GEMM with a K split, the skinny kernel, the FAST GEMM on canonical weights and
+the scratch-free SPLIT GEMM of the spec call) is captured on a side
+stream and replayed several times, with eager work and synchronizations
+between replays; every replay must give the eager results bit for bit."""
 import numpy as np
 import pytest
 
@@ -46,7 +46,8 @@ def test_graph_replays_match_eager(torch):
     y_res = torch.empty((M, N), dtype=torch.float32, device="cuda")
     y_exact = torch.empty((M, N), dtype=torch.float32, device="cuda")
     y_skinny = torch.empty((8, N), dtype=torch.float32, device="cuda")
-    y_copy = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    y_canon = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    y_split = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
     def sequence():
         ql.qlinear_fast_activations(x, M, K, x16, rs)
@@ -58,12 +59,15 @@ def test_graph_replays_match_eager(torch):
                               x16=x16, rowscale=rs, epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=y_res,
                               gate=gate, gate_rows=260, workspace=ws[0])
         ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_exact, path=ql.QL_PATH_SPLITK, split_k=3,
-                              workspace=ws[1])
+                              mode=ql.QL_MODE_EXACT, workspace=ws[1])
         ql.qlinear_forward_ex(xs, p, s, b, bits, 8, N, K, y_skinny, workspace=ws[2])
-        # canonical weights at M >= 512: repack into the workspace, then the GEMM on the copy
-        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_copy, workspace=ws[0])
+        # canonical weights with a workspace: fp16 prepass into it, FAST GEMM on the code rows
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_canon, workspace=ws[0])
+        # the spec call's plan (no workspace: SPLIT GEMM) on the capture
+        # stream; qlinear_forward itself launches on the default stream
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_split, workspace=None)
 
-    outs = (y_fast, y_glu, y_res, y_exact, y_skinny, y_copy)
+    outs = (y_fast, y_glu, y_res, y_exact, y_skinny, y_canon, y_split)
     y_res.copy_(res0)
     sequence()
     torch.cuda.synchronize()

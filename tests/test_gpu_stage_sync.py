@@ -31,7 +31,7 @@ def torch():
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("mode", [ql.QL_MODE_FAST, ql.QL_MODE_EXACT])
+@pytest.mark.parametrize("mode", [ql.QL_MODE_FAST, ql.QL_MODE_EXACT, ql.QL_MODE_SPLIT])
 def test_repeated_runs_identical_and_correct(torch, bits, mode):
     M, K, N = 4096, 4608, 4608
     w = inputs.weights(N, K, 70 + bits)
@@ -60,7 +60,7 @@ def test_repeated_runs_identical_and_correct(torch, bits, mode):
             blk = out.index_select(0, ri).index_select(1, ci).cpu().numpy()
             e = oracle.error_metrics(blk, ref)
             assert e["relF"] <= RELF_TOL and e["maxabs_over_rms"] <= MAXABS_RMS_TOL, (ql.qlinear_last_path(), e)
-            if mode == ql.QL_MODE_EXACT:
+            if mode in (ql.QL_MODE_EXACT, ql.QL_MODE_SPLIT):
                 assert e["relF"] <= RELF_DESIGN and e["maxabs_over_rms"] <= MAXABS_RMS_DESIGN, e
         else:
             diff = (out != first).nonzero()

@@ -51,10 +51,11 @@ def test_sizes(lib):
     assert ql.qlinear_packed_words(3, 3, 64) == 3 * 6
     assert ql.qlinear_packed_words(5, 3, 64) == 0
     assert ql.qlinear_tiled_words(3, 40, 128) == 64 * 128 * 3 // 32
-    # skinny path needs no workspace; the GEMM path needs per-group row sums of x
-    assert ql.qlinear_workspace_bytes(4, 1, 27648, 4608) == 0
+    # the skinny path needs no workspace, but the bound also covers the fused
+    # epilogues, which run the FAST GEMM (fp16 x: M*K*2 + M*4 bytes) at any M
+    assert ql.qlinear_workspace_bytes(4, 1, 27648, 4608) == 4608 * 2 + 256
     ws = ql.qlinear_workspace_bytes(4, 4096, 4608, 4608)
-    assert ws >= 72 * 4096 * 4
+    assert ws >= max(72 * 4096 * 4, 4096 * 4608 * 2)
     # long K with few output tiles uses split K partials
     assert ql.qlinear_workspace_bytes(4, 512, 4608, 53248) > 512 * 4608 * 4
     assert ql.qlinear_workspace_bytes(4, 64, 256, 100) == 0
@@ -195,7 +196,16 @@ def _args(**kw):
     (dict(path=1, M=17), ql.QL_EUNSUPPORTED),
     (dict(path=9), ql.QL_EUNSUPPORTED),
     (dict(path=3, K=64), ql.QL_EUNSUPPORTED),
-    (dict(M=64, N=64, K=128, workspace=0x7000, workspace_bytes=16), ql.QL_EWORKSPACE),
+    (dict(M=64, N=64, K=128, mode=1, workspace=0x7000, workspace_bytes=16), ql.QL_EWORKSPACE),
+    # no workspace: plans that need scratch are refused before any launch
+    (dict(M=64, N=64, K=128, mode=1), ql.QL_EWORKSPACE),          # EXACT: group sums of x
+    (dict(M=64, N=64, K=128, mode=2), ql.QL_EWORKSPACE),          # FAST: fp16 activations
+    (dict(M=64, N=64, K=128, mode=3, path=3), ql.QL_EWORKSPACE),  # forced K split: partials
+    (dict(M=64, N=64, K=128, bits=3), ql.QL_EWORKSPACE),          # canonical 3-bit: tiled copy
+    (dict(M=64, N=64, K=128, epilogue=2, residual=0x6000, gate=0x6800, gate_rows=1), ql.QL_EWORKSPACE),
+    (dict(mode=3, path=1), ql.QL_EUNSUPPORTED),                   # SPLIT has no skinny form
+    (dict(mode=4), ql.QL_EINVAL),
+    (dict(M=64, mode=3, epilogue=1, layout=1, biases=0, N=64), ql.QL_EUNSUPPORTED),
     (dict(tile=99, M=64), ql.QL_EUNSUPPORTED),
 ])
 def test_forward_validation_rejects_before_launch(lib, kw, status):
@@ -264,12 +274,12 @@ def _forward_status(lib, M, N, K, bits, ws_bytes, mode, layout):
                                    (640, 300, 448), (4096, 4608, 4608), (512, 4608, 53248)])
 def test_workspace_bytes_bounds_every_mode_and_layout(lib, shape):
     """qlinear_workspace_bytes is enough for every mode and layout under
-    automatic dispatch (canonical weights from 512 rows on and 3-bit weights
-    add their tiled copy), and one byte less than a call's need is refused."""
+    automatic dispatch (canonical 3-bit weights add their tiled copy), and one
+    byte less than a call's need is refused."""
     M, N, K = shape
     for bits in (2, 3, 4, 8):
         wb = lib.qlinear_workspace_bytes(bits, M, N, K)
-        for mode in (ql.QL_MODE_AUTO, ql.QL_MODE_EXACT, ql.QL_MODE_FAST):
+        for mode in (ql.QL_MODE_AUTO, ql.QL_MODE_EXACT, ql.QL_MODE_FAST, ql.QL_MODE_SPLIT):
             for layout in (ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED):
                 lo, hi = 0, wb + 1
                 while lo < hi:   # smallest size not refused for lack of workspace
@@ -279,6 +289,37 @@ def test_workspace_bytes_bounds_every_mode_and_layout(lib, shape):
                     else:
                         hi = mid
                 assert lo <= wb, (bits, mode, layout, lo, wb)
-                if layout == ql.QL_LAYOUT_CANONICAL and M >= 512 and mode == ql.QL_MODE_AUTO:
+                if layout == ql.QL_LAYOUT_CANONICAL and bits == 3 and M > 16:
                     copy = ql.qlinear_tiled_words(bits, N, K) * 4 + ql.qlinear_tiled_sb_words(N, K) * 4
                     assert lo >= copy, (bits, lo, copy)
+
+
+def _north_star_status(lib, M, N, K, bits):
+    return lib.qlinear_forward(0x100000, 0x200000, 0x300000, 0x400000, bits, 64, M, N, K, 0x500000)
+
+
+@pytest.mark.skipif(_gpu_present(), reason="passes placeholder device addresses: runs only where no GPU is visible")
+@pytest.mark.parametrize("shape", [(1, 27648, 4608), (16, 64, 64), (17, 40, 64), (300, 2304, 448),
+                                   (4096, 4608, 4608), (512, 4608, 53248), (4608, 13824, 4608)])
+def test_north_star_call_needs_no_scratch(lib, shape):
+    """qlinear_forward takes no workspace and plans nothing that needs one: every
+    call reaches its launch (which fails here, with no device, as QL_EHIP);
+    only canonical 3-bit GEMMs, which need a tiled copy, are refused up front.
+    With a NULL workspace the full form keeps to the same plans."""
+    M, N, K = shape
+    for bits in (2, 3, 4, 8):
+        st = _north_star_status(lib, M, N, K, bits)
+        if bits == 3 and M > 16:
+            assert st == ql.QL_EWORKSPACE, (bits, st)
+        else:
+            assert st == ql.QL_EHIP, (bits, st)
+        for layout in (ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED):
+            st = _forward_status_nows(lib, M, N, K, bits, ql.QL_MODE_AUTO, layout)
+            assert st != ql.QL_EWORKSPACE or (bits == 3 and M > 16 and layout == ql.QL_LAYOUT_CANONICAL)
+
+
+def _forward_status_nows(lib, M, N, K, bits, mode, layout):
+    a = ql.ql_forward_args()
+    a.x, a.packed_q, a.scales, a.biases, a.out = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    a.bits, a.group, a.M, a.N, a.K, a.mode, a.layout = bits, 64, M, N, K, mode, layout
+    return lib.qlinear_forward_ex(ctypes.byref(a), None)
