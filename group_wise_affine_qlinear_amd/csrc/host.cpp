@@ -80,6 +80,33 @@ float f16_to_f32(uint16_t h) {
   return f;
 }
 
+// ---- scratch of qlinear_forward_noalloc: a fixed device array in this
+// library's code object (each device that loads the library holds its own
+// copy until the process ends). Host code never passes the array's name to a
+// kernel: its device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and kept per device.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+struct ScratchAddress {
+  std::once_flag once;
+  void *ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddress g_scratch_address[kMaxDevices];
+
+int noalloc_scratch(void **out) {
+  *out = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QL_EHIP;
+  ScratchAddress &s = g_scratch_address[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess || s.ptr == nullptr) return QL_EHIP;
+  *out = s.ptr;
+  return QL_OK;
+}
+
 // ---- dispatch
 struct Plan {
   int path = QL_PATH_AUTO;
@@ -554,6 +581,25 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   }
   return QL_OK;
 }
+
+QL_API int qlinear_forward_noalloc(const ql_forward_args *a, void *stream) {
+  if (!a) return QL_EINVAL;
+  if (a->workspace || a->workspace_bytes) return QL_EINVAL;
+  // argument errors first, then the scratch need against the array's size,
+  // both before the scratch address is looked up or anything launched
+  int st = validate_forward(a);
+  if (st != QL_OK) return st;
+  if (qlinear_forward_workspace_bytes(a) > kNoallocScratchBytes) return QL_EWORKSPACE;
+  void *ptr = nullptr;
+  st = noalloc_scratch(&ptr);
+  if (st != QL_OK) return st;
+  ql_forward_args b = *a;
+  b.workspace = ptr;
+  b.workspace_bytes = kNoallocScratchBytes;
+  return qlinear_forward_ex(&b, stream);
+}
+
+QL_API size_t qlinear_forward_noalloc_max_scratch(void) { return kNoallocScratchBytes; }
 
 QL_API int64_t qlinear_group_sums_ld(int64_t M) { return M <= 0 ? 0 : round_up(M, 256); }
 

@@ -31,6 +31,7 @@ EXPORTED = (
     "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
     "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations", "qlinear_repack_glu",
     "qlinear_unrepack_glu", "qlinear_quantize_imatrix", "qlinear_forward_workspace_bytes",
+    "qlinear_forward_noalloc", "qlinear_forward_noalloc_max_scratch",
 )
 
 
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_forward_ex": ([ctypes.POINTER(ql_forward_args), vp], i32),
         "qlinear_workspace_bytes": ([i32, i64, i64, i64], sz),
         "qlinear_forward_workspace_bytes": ([ctypes.POINTER(ql_forward_args)], sz),
+        "qlinear_forward_noalloc": ([ctypes.POINTER(ql_forward_args), vp], i32),
+        "qlinear_forward_noalloc_max_scratch": ([], sz),
         "qlinear_packed_words": ([i32, i64, i64], sz),
         "qlinear_pack_host": ([vp, i32, i64, i64, vp], i32),
         "qlinear_unpack_host": ([vp, i32, i64, i64, vp], i32),

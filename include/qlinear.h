@@ -227,6 +227,28 @@ int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales,
 int qlinear_forward_ex(const ql_forward_args *args, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as qlinear_forward_ex, but its scratch is a fixed 64 MiB array inside
+ * the library (qlinear_forward_noalloc_max_scratch() bytes, held on every
+ * device that loads the library until the process ends) instead of a caller
+ * workspace. args->workspace and args->workspace_bytes must be 0 (QL_EINVAL
+ * otherwise). The plan is the one qlinear_forward_ex picks with a workspace;
+ * a call whose plan needs more than the array (qlinear_forward_workspace_bytes
+ * > the maximum, e.g. fp16 activations of more than 64 MiB) returns
+ * QL_EWORKSPACE before anything is launched. Allocates nothing and never
+ * synchronizes. Every call on one device uses that device's one array, which
+ * keeps the last call's contents: calls that overlap in time on one device
+ * (other streams, other threads) race on it and must be serialized by the
+ * caller. Whatever must start at zero is cleared by a kernel on the call's
+ * stream, so the call can be captured in a HIP graph.
+ */
+int qlinear_forward_noalloc(const ql_forward_args *args, void *stream);
+
+/* Bytes of the fixed scratch array of qlinear_forward_noalloc (64 MiB). */
+size_t qlinear_forward_noalloc_max_scratch(void);
+
+/*
  * Per-group row sums of the activations, xsum[g, m] = sum_{k=64g}^{64g+63}
  * x[m, k] in fp32, written to xsum with row pitch ld_xsum (layout
  * [K/64, ld_xsum]). The fused kernels fold each group's bias in as
