@@ -6,26 +6,33 @@ M=4096 tokens, K=N=4608, 4-bit codes, group 64 (square projection of the
 4608-wide DiT at 1024x1024): the activation prepass (qlinear_fast_activations:
 bf16 x to fp16 with per-row power-of-two scales) followed by the fused
 dequant-GEMM on tiled weights (qlinear_forward_ex, FAST mode), i.e. exactly the
-kernels qlinear_forward_ex launches for this layer. Weights are quantized by the
-library's device RTN quantizer and repacked to the tiled layout during setup, as
-a loader does once per checkpoint; inputs are seeded synthetic tensors already
-resident in HBM when the timed region starts.
+kernels qlinear_forward_ex launches for this layer with a workspace. Weights are
+quantized by the library's device RTN quantizer and repacked to the tiled
+layout during setup, as a loader does once per checkpoint; inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
 
 Printed: one JSON line with the whole-job throughput (TFLOP/s), the roofline of
 the dominant kernel (fused GEMM, timed live with HIP events on its stream), the
-exact-mode, skinny-M and text-conditioning rows as secondary measurements, and
-the CPU oracle timed on this host as a reported baseline.
+other configured workloads and entry points as secondary rows (each with its
+roofline fraction), and the CPU oracle timed on this host as a reported
+baseline (the headline workload in full, the other workloads on row samples).
 """
 from __future__ import annotations
 
-import argparse
-import hashlib
-import json
 import os
-import subprocess
 import sys
-import threading
-import time
+
+# the oracle's BLAS uses every core this process may run on; fixed before
+# numpy (imported by torch) starts its thread pool
+_CORES = len(os.sched_getaffinity(0))
+os.environ.setdefault("OPENBLAS_NUM_THREADS", str(_CORES))
+
+import argparse  # noqa: E402
+import hashlib  # noqa: E402
+import json  # noqa: E402
+import subprocess  # noqa: E402
+import threading  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -36,6 +43,8 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 WORKLOAD = dict(name="dit_square_proj_M4096_K4608_N4608_q4_g64", M=4096, K=4608, N=4608, bits=4, wid=6)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm3_fast_q4_M4096_K4608_N4608_traffic.txt")
+GEMM_SOURCES = ("gemm3.hip", "gemm3_core.h", "ql_device.h")
+SETTLE_S = 0.3                # setup: steps run before the warm-up while the engine clock settles
 
 
 def log(msg):
@@ -45,19 +54,20 @@ def log(msg):
 
 def gemm_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm3.hip", "ql_device.h"):
+    for f in GEMM_SOURCES:
         with open(os.path.join(ROOT, "group_wise_affine_qlinear_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(M, N, K, bits):
+    """Codes + scale/bias + bf16 x + fp32 y, each read or written once."""
     return N * K * bits / 8 + 4 * N * K / 64 + 2 * M * K + 4 * M * N
 
 
-def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1, tiled=False):
+def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1, tiled=False, glu=False):
     """Device-quantized weight sets; tiled=True repacks each set for the GEMM kernels
-    (then a set is (tiled_q, tiled_sb, None))."""
+    (then a set is (tiled_q, tiled_sb, None)); glu=True repacks in GLU order."""
     w = torch.from_numpy(inputs.weights(N, K, wid)).cuda()
     sets = []
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -67,7 +77,7 @@ def make_weights(torch, ql, inputs, N, K, bits, wid, copies=1, tiled=False):
         b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
         ql.qlinear_quantize_rtn(w, bits, 64, N, K, p, s, b, status)
         if tiled:
-            tq, tsb = ql.qlinear_repack(p, s, b, bits, 64, N, K)
+            tq, tsb = (ql.qlinear_repack_glu if glu else ql.qlinear_repack)(p, s, b, bits, 64, N, K)
             sets.append((tq, tsb, None))
             del p, s, b
         else:
@@ -113,158 +123,249 @@ def time_calls(torch, fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
-def secondary_rows(torch, ql, inputs, exact_sets, x_main):
-    rows = {}
-    M, K, N, bits = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"], WORKLOAD["bits"]
+# ------------------------------------------------------------------ secondary cases
+#
+# Each case sets up its tensors once and returns (call, meta): call() runs the
+# measured launch(es) once; meta holds the figures a row reports. GEMM rows
+# report TFLOP/s as a fraction of the dense 16-bit MFMA peak (both fp16 and bf16
+# are 2.5 PFLOP/s on MI355X); skinny rows report GB/s as a fraction of HBM.
+# A call with a workspace runs what automatic dispatch picks there (FAST for
+# M > 16: the fp16 prepass and the GEMM, both inside the timed call); the
+# spec call qlinear_forward runs with no workspace (SPLIT for M > 16).
+
+def _ws(torch, ql, bits, M, N, K):
+    return torch.empty(max(ql.qlinear_workspace_bytes(bits, M, N, K), 16), dtype=torch.uint8, device="cuda")
+
+
+def case_gemm(torch, ql, inputs, M, N, K, bits, wid, xs="normal", entry="auto_tiled", copies=1, mode=None):
+    """entry: auto_tiled / auto_canonical (qlinear_forward_ex with a workspace),
+    the benchmark spec (qlinear_forward, canonical, no workspace), split_tiled (SPLIT,
+    no workspace), exact_tiled / exact_canonical (EXACT with a workspace)."""
+    tiled = entry in ("auto_tiled", "split_tiled", "exact_tiled")
+    sets = make_weights(torch, ql, inputs, N, K, bits, wid, copies, tiled=tiled)
+    x = torch.from_numpy(inputs.activations_bf16(M, K, wid, xs).view("int16")).cuda()
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    p, s, _ = exact_sets
+    ws = _ws(torch, ql, bits, M, N, K)
+    layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
+    kw = {}
+    if entry.startswith("exact"):
+        kw["mode"] = ql.QL_MODE_EXACT
+    if entry == "split_tiled":
+        kw["mode"] = ql.QL_MODE_SPLIT
+    if mode is not None:
+        kw["mode"] = mode
+    i = [0]
 
-    def fe():
-        ql.qlinear_forward_ex(x_main, p, s, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
-                              mode=ql.QL_MODE_EXACT)
+    def call():
+        p, s, b = sets[i[0] % copies]
+        i[0] += 1
+        if entry == "north_star":
+            ql.qlinear_forward(x, p, s, b, bits, 64, M, N, K, out)
+        else:
+            ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=layout,
+                                  workspace=None if entry == "split_tiled" else ws, **kw)
 
-    ms = time_calls(torch, fe, 20, 5)
-    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-    rows[f"exact_mode_M{M}_K{K}_N{N}_q{bits}"] = {
-        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-        "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)}
-    log(f"exact mode: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
+    return call, {"flop": 2.0 * M * N * K, "weight_copies_rotated": copies}
 
-    # the plain entry point on canonical weights (EXACT numerics, library-owned workspace)
-    (pc, sc, bc), = make_weights(torch, ql, inputs, N, K, bits, WORKLOAD["wid"])
 
-    def fc():
-        ql.qlinear_forward(x_main, pc, sc, bc, bits, 64, M, N, K, out)
+def case_skinny(torch, ql, inputs, M, N, K, bits, wid, tiled, copies):
+    sets = make_weights(torch, ql, inputs, N, K, bits, wid, copies, tiled=tiled)
+    x = torch.from_numpy(inputs.activations_bf16(M, K, wid).view("int16")).cuda()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
+    i = [0]
 
-    ms = time_calls(torch, fc, 20, 5)
-    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-    rows[f"canonical_entry_M{M}_K{K}_N{N}_q{bits}"] = {
-        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-        "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4),
-        "note": "qlinear_forward, canonical layout (automatic dispatch: tiled copy in the workspace, exact GEMM)"}
-    log(f"canonical qlinear_forward: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
+    def call():
+        p, s, b = sets[i[0] % copies]
+        i[0] += 1
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=layout, workspace=None)
 
-    # the same weights with the kernels forced onto the canonical code rows, and FAST numerics
-    variants = (
-        ("canonical_exact_direct", {"path": ql.QL_PATH_GEMM}, PEAK_BF16_TFLOPS,
-         "exact GEMM reading the canonical code rows (forced GEMM path, no copy)"),
-        ("canonical_fast", {"mode": ql.QL_MODE_FAST}, PEAK_F16_TFLOPS,
-         "prepass + FAST GEMM, automatic dispatch (tiled copy in the workspace)"),
-        ("canonical_fast_direct", {"mode": ql.QL_MODE_FAST, "path": ql.QL_PATH_GEMM}, PEAK_F16_TFLOPS,
-         "prepass + FAST GEMM reading the canonical code rows (forced GEMM path, no copy)"),
-    )
-    for name, kw, peak, note in variants:
-        def fv(kw=kw):
-            ql.qlinear_forward_ex(x_main, pc, sc, bc, bits, M, N, K, out, **kw)
+    return call, {"bytes": algorithmic_bytes(M, N, K, bits), "weight_copies_rotated": copies}
 
-        ms = time_calls(torch, fv, 20, 5)
-        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-        rows[f"{name}_M{M}_K{K}_N{N}_q{bits}"] = {
-            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-            "frac_mfma": round(tf / peak, 4), "note": note}
-        log(f"{name}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s ({ql.qlinear_last_path()})")
-    del out, pc, sc, bc
 
-    K, N = 4608, 27648
-    for M, bits, tiled in ((1, 4, False), (1, 4, True), (8, 4, False), (8, 4, True), (1, 8, True), (1, 3, True)):
-        copies = 8  # 8 x >= 56 MB of distinct weights > 256 MB Infinity Cache
-        sets = make_weights(torch, ql, inputs, N, K, bits, 40 + (M > 1), copies, tiled=tiled)
-        x = torch.from_numpy(inputs.activations_bf16(M, K, 40 + (M > 1)).view("int16")).cuda()
-        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
-        i = [0]
+SKINNY_COPIES = 8     # 8 x >= 56 MB of distinct weights > the 256 MB Infinity Cache
+COND_COPIES = 4       # 4 x 138 MB of llm_cond_proj weights
 
-        def fn():
-            p, s, b = sets[i[0] % copies]
-            i[0] += 1
-            ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=layout)
+# name -> (builder, kwargs, note)
+CASES = {
+    # the headline shape through the other entry points and numerics
+    "north_star_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6, entry="north_star"),
+                                        "qlinear_forward: canonical weights, no workspace (SPLIT GEMM)"),
+    "split_tiled_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6, entry="split_tiled"),
+                                         "SPLIT GEMM on tiled weights, no workspace"),
+    "fast_canonical_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6,
+                                                             entry="auto_canonical"),
+                                            "canonical weights with a workspace: prepass + FAST GEMM on the code rows"),
+    "exact_tiled_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6, entry="exact_tiled"),
+                                         "EXACT: group sums + exact-integer bf16 MFMA GEMM"),
+    "exact_canonical_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6,
+                                                              entry="exact_canonical"),
+                                             "EXACT on the canonical code rows"),
+    # QKV projection at 1024^2 (outlier channels)
+    "qkv_M4608_K4608_N13824_q4": (case_gemm, dict(M=4608, N=13824, K=4608, bits=4, wid=2, xs="outlier"),
+                                  "prepass + FAST GEMM, tiled"),
+    "qkv_north_star_M4608_K4608_N13824_q4": (case_gemm, dict(M=4608, N=13824, K=4608, bits=4, wid=2, xs="outlier",
+                                                              entry="north_star"),
+                                             "qlinear_forward (SPLIT)"),
+    # SwiGLU MLP at 1024^2: gate/up (8-bit and 4-bit) and down (4- and 8-bit)
+    "mlp_gateup_M4608_K4608_N24576_q8": (case_gemm, dict(M=4608, N=24576, K=4608, bits=8, wid=3),
+                                         "prepass + FAST GEMM, tiled"),
+    "mlp_gateup_M4608_K4608_N24576_q4": (case_gemm, dict(M=4608, N=24576, K=4608, bits=4, wid=3),
+                                         "prepass + FAST GEMM, tiled"),
+    "mlp_down_M4608_K12288_N4608_q4": (case_gemm, dict(M=4608, N=4608, K=12288, bits=4, wid=30),
+                                       "prepass + FAST GEMM, tiled"),
+    "mlp_down_M4608_K12288_N4608_q8": (case_gemm, dict(M=4608, N=4608, K=12288, bits=8, wid=30),
+                                       "prepass + FAST GEMM, tiled"),
+    # text conditioning: long K, few tiles
+    "llm_cond_proj_M512_K53248_N4608_q4_canonical": (
+        case_gemm, dict(M=512, N=4608, K=53248, bits=4, wid=4, xs="slices", entry="auto_canonical", copies=COND_COPIES),
+        "canonical weights with a workspace: prepass + FAST GEMM split along K + ordered reduce"),
+    "llm_cond_proj_M512_K53248_N4608_q4_tiled": (
+        case_gemm, dict(M=512, N=4608, K=53248, bits=4, wid=4, xs="slices", copies=COND_COPIES),
+        "tiled, prepass + FAST GEMM split along K + ordered reduce"),
+    "llm_cond_proj_M512_K53248_N4608_q4_canonical_exact": (
+        case_gemm, dict(M=512, N=4608, K=53248, bits=4, wid=4, xs="slices", entry="exact_canonical",
+                        copies=COND_COPIES),
+        "EXACT on the canonical code rows, split along K"),
+    "llm_cond_proj_M512_K53248_N4608_q4_north_star": (
+        case_gemm, dict(M=512, N=4608, K=53248, bits=4, wid=4, xs="slices", entry="north_star", copies=COND_COPIES),
+        "qlinear_forward: no workspace, so no K split (SPLIT GEMM in row pieces)"),
+    # AdaLN / timestep projections (skinny path, HBM-bound)
+    "adaln_skinny_M1_K4608_N27648_q4_tiled": (case_skinny, dict(M=1, N=27648, K=4608, bits=4, wid=40, tiled=True,
+                                                                copies=SKINNY_COPIES), ""),
+    "adaln_skinny_M1_K4608_N27648_q4_canonical": (case_skinny, dict(M=1, N=27648, K=4608, bits=4, wid=40, tiled=False,
+                                                                    copies=SKINNY_COPIES), ""),
+    "adaln_skinny_M8_K4608_N27648_q4_tiled": (case_skinny, dict(M=8, N=27648, K=4608, bits=4, wid=41, tiled=True,
+                                                                copies=SKINNY_COPIES), ""),
+    "adaln_skinny_M8_K4608_N27648_q4_canonical": (case_skinny, dict(M=8, N=27648, K=4608, bits=4, wid=41, tiled=False,
+                                                                    copies=SKINNY_COPIES), ""),
+    "adaln_skinny_M1_K4608_N27648_q8_tiled": (case_skinny, dict(M=1, N=27648, K=4608, bits=8, wid=40, tiled=True,
+                                                                copies=SKINNY_COPIES), ""),
+    "adaln_skinny_M1_K512_N27648_q4_tiled": (case_skinny, dict(M=1, N=27648, K=512, bits=4, wid=42, tiled=True,
+                                                               copies=40),
+                                             "the pages' AdaLN width (512) as input: informational"),
+    "adaln_skinny_M1_K512_N27648_q8_tiled": (case_skinny, dict(M=1, N=27648, K=512, bits=8, wid=42, tiled=True,
+                                                               copies=24),
+                                             "8-bit modulation (the mixed plans' width) at the pages' AdaLN width"),
+}
 
-        ms = time_calls(torch, fn, 64, 16)
-        by = algorithmic_bytes(M, N, K, bits)
-        gbs = by / (ms * 1e-3) / 1e9
-        lname = "tiled" if tiled else "canonical"
-        rows[f"adaln_skinny_M{M}_K{K}_N{N}_q{bits}_{lname}"] = {
-            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies_rotated": copies}
-        del sets
-        log(f"skinny M={M} q{bits} {lname}: {ms*1e3:.1f} us, {gbs:.0f} GB/s")
 
-    # SwiGLU MLP gate/up projection at 1024x1024: plain FAST GEMM (fp32 y, [M, 2F])
-    # against the fused epilogue (bf16 silu(gate) * up, [M, F])
+def run_case(torch, ql, inputs, name, iters=20, warmup=5):
+    builder, kw, note = CASES[name]
+    call, meta = builder(torch, ql, inputs, **kw)
+    ms = time_calls(torch, call, iters, warmup)
+    row = {"path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2)}
+    if "flop" in meta:
+        tf = meta["flop"] / (ms * 1e-3) / 1e12
+        row.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4)})
+    else:
+        gbs = meta["bytes"] / (ms * 1e-3) / 1e9
+        row.update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    if meta.get("weight_copies_rotated", 1) > 1:
+        row["weight_copies_rotated"] = meta["weight_copies_rotated"]
+    if note:
+        row["note"] = note
+    return row
+
+
+def fused_epilogue_rows(torch, ql, inputs, rows):
+    # SwiGLU MLP gate/up at 1024x1024: plain FAST GEMM (fp32 y, [M, 2F]) against
+    # the fused epilogue (bf16 silu(gate) * up, [M, F])
     M, K, N = 4608, 4608, 2 * 12288
-    w = torch.from_numpy(inputs.weights(N, K, 3)).cuda()
-    p = torch.empty((N, K // 8), dtype=torch.int32, device="cuda")
-    s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-    b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-    ql.qlinear_quantize_rtn(w, 4, 64, N, K, p, s, b)
-    del w
-    tq, tsb = ql.qlinear_repack(p, s, b, 4, 64, N, K)
-    gq, gsb = ql.qlinear_repack_glu(p, s, b, 4, 64, N, K)
-    del p, s, b
+    (tq, tsb, _), = make_weights(torch, ql, inputs, N, K, 4, 3, tiled=True, glu=True)
     x = torch.from_numpy(inputs.activations_bf16(M, K, 3).view("int16")).cuda()
-    x16, rs = ql.qlinear_fast_activations(x, M, K)
-    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = _ws(torch, ql, 4, M, N, K)
     yg = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
-    ms_plain = time_calls(torch, lambda: ql.qlinear_forward_ex(
-        x, tq, tsb, None, 4, M, N, K, y, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs), 10, 3)
-    path_plain = ql.qlinear_last_path()
-    ms_glu = time_calls(torch, lambda: ql.qlinear_forward_ex(
-        x, gq, gsb, None, 4, M, N, K, yg, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs,
-        epilogue=ql.QL_EPI_SWIGLU), 10, 3)
-    tf = 2 * M * N * K / 1e12
-    rows["mlp_gateup_M4608_K4608_N24576_q4_fast"] = {
-        "path": path_plain, "us": round(ms_plain * 1e3, 1), "TFLOP/s": round(tf / (ms_plain * 1e-3), 1),
-        "out_bytes": M * N * 4}
+    ms = time_calls(torch, lambda: ql.qlinear_forward_ex(
+        x, tq, tsb, None, 4, M, N, K, yg, layout=ql.QL_LAYOUT_TILED, epilogue=ql.QL_EPI_SWIGLU, workspace=ws), 10, 3)
+    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
     rows["mlp_gateup_M4608_K4608_N24576_q4_swiglu_fused"] = {
-        "path": ql.qlinear_last_path(), "us": round(ms_glu * 1e3, 1), "TFLOP/s": round(tf / (ms_glu * 1e-3), 1),
-        "out_bytes": M * (N // 2) * 2}
-    log(f"gate/up plain {ms_plain*1e3:.1f} us, fused SwiGLU {ms_glu*1e3:.1f} us")
-    del tq, tsb, gq, gsb, x, x16, rs, y, yg
+        "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+        "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4), "out_bytes": M * (N // 2) * 2,
+        "note": "prepass + FAST GEMM with silu(gate) * up in the store, bf16 [M, F]"}
+    del tq, tsb, x, ws, yg
 
     # attention-out projection at 1024x1024 (2 samples of 2304 tokens) with the
-    # AdaLN gated residual update: plain FAST GEMM, GEMM + a separate torch
-    # update of the residual stream, and the update fused into the GEMM store
+    # AdaLN gated residual update: GEMM + a separate torch update of the
+    # residual stream, against the update fused into the GEMM store
     M, K, N, L = 4608, 4608, 4608, 2304
-    w = torch.from_numpy(inputs.weights(N, K, 7)).cuda()
-    p = torch.empty((N, K // 8), dtype=torch.int32, device="cuda")
-    s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-    b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-    ql.qlinear_quantize_rtn(w, 4, 64, N, K, p, s, b)
-    del w
-    tq, tsb = ql.qlinear_repack(p, s, b, 4, 64, N, K)
-    del p, s, b
+    (tq, tsb, _), = make_weights(torch, ql, inputs, N, K, 4, 7, tiled=True)
     x = torch.from_numpy(inputs.activations_bf16(M, K, 7).view("int16")).cuda()
-    x16, rs = ql.qlinear_fast_activations(x, M, K)
+    ws = _ws(torch, ql, 4, M, N, K)
     res = torch.from_numpy(inputs.residual_stream(M, N, 7)).cuda()
     gate = torch.from_numpy(inputs.adaln_gate(M // L, N, 7)).cuda()
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
-    def plain():
-        ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, y, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs)
-
     def unfused():
-        plain()
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, y, layout=ql.QL_LAYOUT_TILED, workspace=ws)
         res.view(M // L, L, N).addcmul_(gate[:, None, :], y.view(M // L, L, N))
 
     def fused():
-        ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, res, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs,
+        ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, res, layout=ql.QL_LAYOUT_TILED, workspace=ws,
                               epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=gate, gate_rows=L)
 
-    ms_plain = time_calls(torch, plain, 20, 5)
     ms_unf = time_calls(torch, unfused, 20, 5)
     ms_fused = time_calls(torch, fused, 20, 5)
-    tf = 2 * M * N * K / 1e12
-    rows["attn_out_M4608_K4608_N4608_q4_fast"] = {
-        "path": "gemm3 (plain y)", "us": round(ms_plain * 1e3, 1), "TFLOP/s": round(tf / (ms_plain * 1e-3), 1)}
+    flop = 2 * M * N * K
     rows["attn_out_M4608_K4608_N4608_q4_gate_unfused"] = {
-        "path": "gemm3 + torch addcmul_ on the residual", "us": round(ms_unf * 1e3, 1),
-        "TFLOP/s": round(tf / (ms_unf * 1e-3), 1)}
+        "path": "prepass + FAST GEMM + torch addcmul_ on the residual", "us": round(ms_unf * 1e3, 1),
+        "TFLOP/s": round(flop / (ms_unf * 1e-3) / 1e12, 1)}
     rows["attn_out_M4608_K4608_N4608_q4_gate_fused"] = {
-        "path": ql.qlinear_last_path(), "us": round(ms_fused * 1e3, 1), "TFLOP/s": round(tf / (ms_fused * 1e-3), 1),
+        "path": ql.qlinear_last_path(), "us": round(ms_fused * 1e3, 1),
+        "TFLOP/s": round(flop / (ms_fused * 1e-3) / 1e12, 1),
+        "frac_mfma": round(flop / (ms_fused * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
         "note": "residual updated in place: out = residual + gate[sample] * y"}
-    log(f"attn-out plain {ms_plain*1e3:.1f} us, unfused gate {ms_unf*1e3:.1f} us, fused gate {ms_fused*1e3:.1f} us")
-    del tq, tsb, x, x16, rs, res, gate, y
+    log(f"gate/up + SwiGLU {rows['mlp_gateup_M4608_K4608_N24576_q4_swiglu_fused']['us']} us; "
+        f"attn-out + gate: unfused {ms_unf*1e3:.1f} us, fused {ms_fused*1e3:.1f} us")
 
+
+def sweep_rows(torch, ql, inputs, rows):
+    # 2048x2048 canvas: per-bit layer sweep, and one pass over the 34 blocks'
+    # attention projections (QKV N=13824 then out N=4608) with 34 distinct
+    # weight sets per width (every launch streams its weights); fp16
+    # activations made once per pass and shared by its 68 projections
+    M, K = 16896, 4608
+    x = torch.from_numpy(inputs.activations_bf16(M, K, 5).view("int16")).cuda()
+    x16, rs = ql.qlinear_fast_activations(x, M, K)
+    ws = _ws(torch, ql, 8, M, 13824, K)
+    for bits in (2, 3, 4, 8):
+        layers = []
+        for N in (13824, 4608):
+            (p, s, b), = make_weights(torch, ql, inputs, N, K, bits, 5 if N == 4608 else 50)
+            sets = [ql.qlinear_repack(p, s, b, bits, 64, N, K) for _ in range(34)]
+            del p, s, b
+            out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            layers.append((N, sets, out))
+            tq, tsb = sets[0]
+            ms = time_calls(torch, lambda: ql.qlinear_forward_ex(
+                x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs,
+                workspace=ws), 10, 3)
+            tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+            rows[f"sweep_2048_M{M}_K{K}_N{N}_q{bits}"] = {
+                "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+                "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4), "note": "FAST GEMM on shared fp16 activations"}
+
+        def one_pass():
+            ql.qlinear_fast_activations(x, M, K, x16, rs)
+            for i in range(34):
+                for N, sets, out in layers:
+                    tq, tsb = sets[i]
+                    ql.qlinear_forward_ex(x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
+                                          x16=x16, rowscale=rs, workspace=ws)
+
+        ms = time_calls(torch, one_pass, 3, 1)
+        flop = 34 * sum(2 * M * N * K for N, _, _ in layers)
+        tf = flop / (ms * 1e-3) / 1e12
+        rows[f"sweep_2048_34_layer_qkv_out_pass_q{bits}"] = {
+            "ms": round(ms, 2), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4),
+            "weight_sets": 34,
+            "note": "one prepass + 34 x (QKV 16896x4608->13824 + out 16896x4608->4608)"}
+        log(f"2048 sweep q{bits}: 34-layer pass {ms:.2f} ms")
+        del layers
+    del x, x16, rs, ws
+
+
+def dit_block_rows(torch, ql, inputs, rows):
     # one DiT block at 1024x1024 (4608 tokens) under the mixed-precision plans:
     # modulation (skinny, M=1, 8-bit), QKV, attention-out + gated residual,
     # gate/up + fused SwiGLU (bf16), down (fed by the SwiGLU output) + gated
@@ -282,6 +383,7 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
     qkv = torch.empty((M, 3 * 4608), dtype=torch.bfloat16, device="cuda")
     hmid = torch.empty((M, 12288), dtype=torch.bfloat16, device="cuda")
     mod = torch.empty((1, 6 * 4608), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(ql.qlinear_workspace_bytes(8, M, 2 * 12288, 12288), 16), dtype=torch.uint8, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     for policy in ("mixed_3_8", "mixed_4_8"):
         wts = {}
@@ -303,7 +405,7 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
         def proj(role, xin, out, **kw):
             tq, tsb, p = wts[role]
             ql.qlinear_forward_ex(xin, tq, tsb, None, p.bits, xin.shape[0], p.N, p.K, out,
-                                  layout=ql.QL_LAYOUT_TILED, **kw)
+                                  layout=ql.QL_LAYOUT_TILED, workspace=ws, **kw)
 
         def block():
             proj("adaln_modulation", temb, mod)
@@ -315,114 +417,48 @@ def secondary_rows(torch, ql, inputs, exact_sets, x_main):
         ms = time_calls(torch, block, 10, 3)
         blk = qplan.block_projections(policy)
         flops = sum(2 * (1 if p.role == "adaln_modulation" else M) * p.N * p.K for p in blk)
+        tf = flops / (ms * 1e-3) / 1e12
         rows[f"dit_block_1024_{policy}"] = {
-            "us": round(ms * 1e3, 1), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+            "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4),
             "weight_MB": round(sum(p.storage_bytes for p in blk) / 1e6, 1),
             "bits_per_weight_model": round(qplan.bits_per_weight(qplan.model_plan(policy)), 3),
             "note": "modulation M=1 8-bit skinny; QKV, out+gate, gate/up+SwiGLU, down+gate at the bulk width"}
         log(f"DiT block {policy}: {ms*1e3:.1f} us")
         del wts
-    del wf, x, att, temb, res, gates, qkv, hmid, mod
+    del wf, x, att, temb, res, gates, qkv, hmid, mod, ws
 
-    # 2048x2048 canvas: per-bit layer sweep, and one pass over the 34 blocks'
-    # attention projections (QKV N=13824 then out N=4608) with 34 distinct
-    # weight sets per width (every launch streams its weights)
-    M, K = 16896, 4608
-    x = torch.from_numpy(inputs.activations_bf16(M, K, 5).view("int16")).cuda()
-    x16, rs = ql.qlinear_fast_activations(x, M, K)
-    for bits in (2, 3, 4, 8):
-        layers = []
-        for N in (13824, 4608):
-            w = torch.from_numpy(inputs.weights(N, K, 5 if N == 4608 else 50)).cuda()
-            p = torch.empty((N, K * bits // 32), dtype=torch.int32, device="cuda")
-            s = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-            b = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
-            ql.qlinear_quantize_rtn(w, bits, 64, N, K, p, s, b)
-            del w
-            sets = [ql.qlinear_repack(p, s, b, bits, 64, N, K) for _ in range(34)]
-            del p, s, b
-            out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-            layers.append((N, sets, out))
-            tq, tsb = sets[0]
-            ms = time_calls(torch, lambda: ql.qlinear_forward_ex(
-                x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs), 10, 3)
-            rows[f"sweep_2048_M{M}_K{K}_N{N}_q{bits}"] = {
-                "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1),
-                "TFLOP/s": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
 
-        def one_pass():
-            for i in range(34):
-                for N, sets, out in layers:
-                    tq, tsb = sets[i]
-                    ql.qlinear_forward_ex(x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
-                                          x16=x16, rowscale=rs)
-
-        ms = time_calls(torch, one_pass, 3, 1)
-        flop = 34 * sum(2 * M * N * K for N, _, _ in layers)
-        rows[f"sweep_2048_34_layer_qkv_out_pass_q{bits}"] = {
-            "ms": round(ms, 2), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1), "weight_sets": 34,
-            "note": "34 x (QKV 16896x4608->13824 + out 16896x4608->4608), shared fp16 activations"}
-        log(f"2048 sweep q{bits}: 34-layer pass {ms:.2f} ms")
-        del layers
-    del x, x16, rs
-
-    M, K, N = 512, 53248, 4608
-    copies = 4
-    x = torch.from_numpy(inputs.activations_bf16(M, K, 4, "slices").view("int16")).cuda()
-    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    for tiled in (False, True):
-        sets = make_weights(torch, ql, inputs, N, K, 4, 4, copies, tiled=tiled)
-        layout = ql.QL_LAYOUT_TILED if tiled else ql.QL_LAYOUT_CANONICAL
-        i = [0]
-
-        def fn2():
-            p, s, b = sets[i[0] % copies]
-            i[0] += 1
-            ql.qlinear_forward_ex(x, p, s, b, 4, M, N, K, out, layout=layout)
-
-        ms = time_calls(torch, fn2, 20, 5)
-        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-        lname = "tiled" if tiled else "canonical"
-        rows[f"llm_cond_proj_M512_K53248_N4608_q4_{lname}"] = {
-            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-            "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "weight_copies_rotated": copies}
-        log(f"llm_cond_proj {lname}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
-        del sets
-    del x, out
-
-    # one GPU's share under two-way tensor parallelism at 1024x1024 (M = 4608):
-    # column shards (QKV, gate/up: N halved, no exchange) and row shards
-    # (attention-out, down: K halved, fp32 partial y for an all-reduce that is
-    # not run here)
-    M = 4608
-    for name, K, N in (("qkv_col_shard", 4608, 6912), ("gateup_col_shard", 4608, 12288),
-                       ("attn_out_row_shard", 2304, 4608), ("down_row_shard", 6144, 4608)):
-        (p, s, _), = make_weights(torch, ql, inputs, N, K, 4, 8, tiled=True)
-        x = torch.from_numpy(inputs.activations_bf16(M, K, 8).view("int16")).cuda()
-        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-
-        def fs():
-            ql.qlinear_forward_ex(x, p, s, None, 4, M, N, K, out, layout=ql.QL_LAYOUT_TILED)
-
-        ms = time_calls(torch, fs, 20, 5)
-        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
-        rows[f"tp2_{name}_M{M}_K{K}_N{N}_q4"] = {
-            "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
-            "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4), "note": "prepass + FAST GEMM on one GPU's shard"}
-        log(f"tp2 {name}: {ms*1e3:.1f} us, {tf:.0f} TFLOP/s")
-        del p, s, x, out
+def secondary_rows(torch, ql, inputs):
+    rows = {}
+    for name in CASES:
+        rows[name] = run_case(torch, ql, inputs, name)
+        r = rows[name]
+        rate = f"{r['TFLOP/s']} TFLOP/s ({100 * r['frac_mfma']:.1f}%)" if "TFLOP/s" in r else \
+            f"{r['GB/s']} GB/s ({100 * r['frac_hbm']:.1f}%)"
+        log(f"{name}: {r['us']} us, {rate}, {r['path']}")
+        torch.cuda.empty_cache()
+    fused_epilogue_rows(torch, ql, inputs, rows)
+    torch.cuda.empty_cache()
+    dit_block_rows(torch, ql, inputs, rows)
+    torch.cuda.empty_cache()
+    sweep_rows(torch, ql, inputs, rows)
+    torch.cuda.empty_cache()
     return rows
+
+
+# ------------------------------------------------------------------ the oracle on this host
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [0])
+    except Exception:
+        return 0
 
 
 def cpu_baseline(inputs, M, N, K, bits, wid):
     """The oracle as it stands, timed on this host over the full headline workload."""
-    import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     w = inputs.weights(N, K, wid)
     q, s16, b16 = oracle.quantize_rtn(w, bits)
     packed = oracle.pack(q, bits)
@@ -430,9 +466,39 @@ def cpu_baseline(inputs, M, N, K, bits, wid):
     del w, q
     _, t = oracle.timed_forward(x, packed, s16, b16, bits, K)
     tf = 2 * M * N * K / t["total_s"] / 1e12
-    return {"value": round(tf, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(tf, 4), "unit": "TFLOP/s", "cores": _CORES, "kind": "oracle",
+            "blas_threads": _blas_threads(), "openblas_num_threads": os.environ.get("OPENBLAS_NUM_THREADS"),
             "sample": f"full workload M={M} K={K} N={N} q{bits}, one run: unpack+dequantize "
                       f"{t['dequant_s']:.2f} s + fp64 GEMM {t['gemm_s']:.2f} s"}
+
+
+def cpu_oracle_per_config(inputs):
+    """The oracle on every configured workload: the whole weight (unpack +
+    dequantize) and the fp64 product on a sample of at most 512 rows of x,
+    one run each (median of 3 for the tiny and skinny ones); throughput of
+    the sample and the full workload's time extrapolated linearly in M."""
+    import oracle
+    out = {}
+    for name, wl in inputs.WORKLOADS.items():
+        M, K, N = wl["M"], wl["K"], wl["N"]
+        bits = wl["bits"][0]
+        m = min(M, 512)
+        w = inputs.weights(N, K, wl["id"])
+        q, s16, b16 = oracle.quantize_rtn(w, bits)
+        packed = oracle.pack(q, bits)
+        x = inputs.activations_bf16(m, K, wl["id"], wl["x"])
+        del w, q
+        reps = 3 if M <= 64 else 1
+        runs = sorted((oracle.timed_forward(x, packed, s16, b16, bits, K)[1] for _ in range(reps)),
+                      key=lambda t: t["total_s"])
+        t = runs[len(runs) // 2]
+        full_s = t["dequant_s"] + t["gemm_s"] * M / m
+        out[name] = {"bits": bits, "rows_timed": m, "M": M, "dequant_s": round(t["dequant_s"], 3),
+                     "gemm_s": round(t["gemm_s"], 3),
+                     "sample_TFLOP/s": round(2 * m * N * K / t["total_s"] / 1e12, 4),
+                     "full_workload_s_extrapolated": round(full_s, 3)}
+        log(f"oracle {name}: {out[name]}")
+    return {"cores": _CORES, "blas_threads": _blas_threads(), "workloads": out}
 
 
 def load_traffic(src_hash):
@@ -445,6 +511,9 @@ def load_traffic(src_hash):
     return rec.get("traffic_bytes_per_launch")
 
 
+PROFILE_CHOICES = ["none", "step", "copy"] + sorted(CASES)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,8 +521,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--profile", choices=["none", "step", "copy", "skinny"], default="none",
-                    help="short run for rocprofv3: 'step' = the timed step only, 'copy' = a plain copy of known size, 'skinny' = the AdaLN skinny kernel")
+    ap.add_argument("--profile", choices=PROFILE_CHOICES, default="none",
+                    help="short run for rocprofv3: 'step' = the timed step only, 'copy' = a plain copy of known "
+                         "size, a secondary case name = that case's launches only")
+    ap.add_argument("--profile-calls", type=int, default=40)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -471,19 +542,6 @@ def main():
         sys.exit(1)
     ql.load_library()
 
-    if args.profile == "skinny":
-        # the skinny path at the AdaLN shape, M=1, tiled 4-bit weights, 8
-        # distinct weight copies rotated so every launch streams from HBM
-        M, K, N, copies = 1, 4608, 27648, 8
-        sets = make_weights(torch, ql, inputs, N, K, 4, 40, copies, tiled=True)
-        x = torch.from_numpy(inputs.activations_bf16(M, K, 40).view("int16")).cuda()
-        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        for i in range(16 + 64):
-            p, s, _ = sets[i % copies]
-            ql.qlinear_forward_ex(x, p, s, None, 4, M, N, K, out, layout=ql.QL_LAYOUT_TILED)
-        torch.cuda.synchronize()
-        log(f"skinny M=1 K=4608 N=27648 q4 tiled: 80 launches ({ql.qlinear_last_path()})")
-        return
     if args.profile == "copy":
         n = 256 * 1024 * 1024 // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -492,6 +550,14 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy kernel: {n * 4} bytes read and written per launch, 5 launches")
+        return
+    if args.profile in CASES:
+        builder, kw, _ = CASES[args.profile]
+        call, _ = builder(torch, ql, inputs, **kw)
+        for _ in range(args.profile_calls):
+            call()
+        torch.cuda.synchronize()
+        log(f"{args.profile}: {args.profile_calls} calls ({ql.qlinear_last_path()})")
         return
 
     M, K, N, bits = WORKLOAD["M"], WORKLOAD["K"], WORKLOAD["N"], WORKLOAD["bits"]
@@ -519,10 +585,19 @@ def main():
         if evs:
             evs[0].record(stream)
         ql.qlinear_forward_ex(x, p, s, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED,
-                              mode=ql.QL_MODE_FAST, x16=x16, rowscale=rowscale, stream=stream)
+                              mode=ql.QL_MODE_FAST, x16=x16, rowscale=rowscale, stream=stream, workspace=None)
         if evs:
             evs[1].record(stream)
 
+    # setup ends with SETTLE_S seconds of steps while the engine clock settles
+    # under load (the first tens of steps after setup run up to 15 % slower);
+    # then the W untimed warm-up steps and the K timed steps
+    if args.profile == "none":
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < SETTLE_S:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -547,7 +622,8 @@ def main():
     # distribution of the per-step event times, and a sustained ~1 s loop for
     # clock-throttling context (both after the timed region)
     per_step = sorted(a[1].elapsed_time(b[1]) * 1e3 for a, b in zip(ev[:-1], ev[1:]))   # GEMM end to GEMM end
-    q = lambda f: round(per_step[min(len(per_step) - 1, int(f * len(per_step)))], 1)
+    gemm_each = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+    q = lambda v, f: round(v[min(len(v) - 1, int(f * len(v)))], 1) if v else None
     torch.cuda.synchronize()
     # amd-smi sampled from a side thread while the sustained loop runs; the
     # loop lasts at least 1 s and until the sample has returned
@@ -561,13 +637,18 @@ def main():
         torch.cuda.synchronize()
     sus_ms = (time.perf_counter() - ts0) * 1e3 / n_sus
     sampler.join()
-    timing = {"step_us_p10": q(0.1), "step_us_median": q(0.5), "step_us_p90": q(0.9),
+    timing = {"step_us_p10": q(per_step, 0.1), "step_us_median": q(per_step, 0.5), "step_us_p90": q(per_step, 0.9),
+              "gemm_us_p10": q(gemm_each, 0.1), "gemm_us_median": q(gemm_each, 0.5),
+              "gemm_us_p90": q(gemm_each, 0.9),
               "sustained_1s_step_us": round(sus_ms * 1e3, 1),
-              "sustained_1s_TFLOP/s": round(flop / (sus_ms * 1e-3) / 1e12, 1), "sustained_steps": n_sus}
+              "sustained_1s_TFLOP/s": round(flop / (sus_ms * 1e-3) / 1e12, 1), "sustained_steps": n_sus,
+              "settle_s_before_warmup": SETTLE_S}
     log(f"per-step p10/median/p90 {timing['step_us_p10']}/{timing['step_us_median']}/{timing['step_us_p90']} us; "
-        f"sustained 1 s: {timing['sustained_1s_step_us']} us per step")
+        f"GEMM median {timing['gemm_us_median']} us; sustained 1 s: {timing['sustained_1s_step_us']} us per step")
+    del x16, rowscale, out
+    torch.cuda.empty_cache()
 
-    secondary = {} if args.no_secondary else secondary_rows(torch, ql, inputs, (p, s, None), x)
+    secondary = {} if args.no_secondary else secondary_rows(torch, ql, inputs)
     src_hash = gemm_source_hash()
     traffic = load_traffic(src_hash)
 
@@ -597,6 +678,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(inputs, M, N, K, bits, WORKLOAD["wid"])
+        rec["cpu_oracle_per_config"] = cpu_oracle_per_config(inputs)
     print(json.dumps(rec), flush=True)
 
 

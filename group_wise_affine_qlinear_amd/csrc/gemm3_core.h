@@ -63,6 +63,11 @@ constexpr int kBM = 256, kBN = 256, kNW = 8, kNT = 64 * kNW;
 constexpr int kWN = 32, kMI = kBM / 16, kNI = kWN / 16;  // a wave: all rows x 32 columns
 constexpr int kXStage = kBM * 128;               // bytes of one x stage
 constexpr int kStages = 3;                       // x stages in the LDS ring
+// canonical scale/bias staging in LDS: chunks of 8 groups of the tile's 256
+// columns, [buffer][s, b][column][group], one f16 per dword (a 2-byte copy to
+// LDS writes its value zero-extended to 4 bytes); loads run 2 chunks ahead
+constexpr int kSbChunk = 8, kSbBufs = 3;
+constexpr int kSbBufWords = 2 * kBN * kSbChunk;  // dwords per buffer
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne3(float f) {
   uint32_t u = __float_as_uint(f);
@@ -213,6 +218,10 @@ struct TileIO {
   const Gemm3Args &a;
   int lane, wave, r16, h, G;
   bool x_issuer;
+  // canonical scale/bias staging (see stage_issue)
+  uint32_t *sbl = nullptr;
+  int g_first = 0;        // first group of the tile's K range
+  uint32_t st_voff = 0;   // the lane's staging offset: its row and its group within a chunk
   __amdgpu_buffer_rsrc_t xr, wr, sr, br;
   uint32_t xo[XPW];
   uint32_t wo = 0, so = 0, who = 0;  // who: 3-bit, the lane's high-bit word
@@ -221,7 +230,8 @@ struct TileIO {
   int a_off[2][4];
   int a_base;
 
-  __device__ TileIO(const Gemm3Args &args, int64_t m0, int64_t n0) : a(args) {
+  __device__ TileIO(const Gemm3Args &args, int64_t m0, int64_t n0, uint32_t *sb_lds = nullptr, int g_begin = 0)
+      : a(args) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,6 +268,9 @@ struct TileIO {
         rowo[ni] = (uint32_t)(n * (a.K * BITS / 8)) + (uint32_t)(h * 2 * BITS);
         srow[ni] = (uint32_t)(n * G * 2);
       }
+      sbl = sb_lds;
+      g_first = g_begin;
+      st_voff = (uint32_t)(((n0 + (wave & 3) * 64 + (lane >> 3)) * G + (lane & 7)) * 2);
     } else {
       wr = make_rsrc(a.w, strip * G * BB, (int64_t)G * BB);
       sr = make_rsrc(a.sb, strip * G * 128, (int64_t)G * 128);
@@ -278,7 +291,8 @@ struct TileIO {
   }
 
   // Codes and scale/bias of group gv for this lane's two column blocks.
-  // Tiled: sb = s | b << 16, bb unused; canonical: sb = s, bb = b.
+  // Tiled: sb = s | b << 16, bb unused; canonical: codes only (scale and
+  // bias come from the staged chunks through read_sb).
   __device__ __forceinline__ void load_codes(uint32_t (&w)[kNI][LC::kWords], uint32_t (&sb)[kNI], uint32_t (&bb)[kNI],
                                              int gv) const {
     const int g = __builtin_amdgcn_readfirstlane(gv);
@@ -297,8 +311,6 @@ struct TileIO {
         } else {
           w[ni][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, rowo[ni], go, 0);
         }
-        sb[ni] = __builtin_amdgcn_raw_buffer_load_b16(sr, srow[ni], (uint32_t)g * 2u, 0);
-        bb[ni] = __builtin_amdgcn_raw_buffer_load_b16(br, srow[ni], (uint32_t)g * 2u, 0);
         continue;
       }
       if constexpr (BITS == 4) {
@@ -320,11 +332,62 @@ struct TileIO {
     }
   }
 
+  // Canonical: scale | bias << 16 of group gv for this lane's two column
+  // blocks, from the staged chunk (see stage_issue).
+  __device__ __forceinline__ void read_sb(int gv, uint32_t (&sb)[kNI]) const {
+    const int rel = __builtin_amdgcn_readfirstlane(gv) - g_first;
+    const uint32_t *buf = sbl + ((rel / kSbChunk) % kSbBufs) * kSbBufWords + (rel % kSbChunk);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int col = wave * kWN + ni * 16 + r16;
+      sb[ni] = buf[col * kSbChunk] | (buf[(kBN + col) * kSbChunk] << 16);
+    }
+  }
+
   __device__ __forceinline__ void issue_x(unsigned char *X, int gv) const {
     const int g = __builtin_amdgcn_readfirstlane(gv);
     if (x_issuer) {
 #pragma unroll
       for (int i = 0; i < XPW; ++i) dma16(xr, xo[i], (uint32_t)g * 128u, X + (wave * XPW + i) * 1024);
+    }
+  }
+
+  // Canonical scale/bias staging. Per-group loads of a lane's own column
+  // touch 16 rows for 2 bytes each; a staging load instead covers 8 groups
+  // of 8 columns (16 bytes of each row's line) and copies them straight to
+  // LDS. Chunk c holds groups [g_first + 8c, +8) of the tile's 256 columns
+  // in buffer c % 3: scale at [col][group], bias kBN*kSbChunk dwords further.
+  // Wave w copies array w / 4 (scale, bias), columns (w % 4)*64 + 8j + L/8
+  // for its load j, lane L taking group L % 8: the lanes of one load fill 64
+  // consecutive dwords. The row step and the chunk's first group go in the
+  // uniform offset, which the buffer range check includes: rows past N and
+  // groups past the array's end read zero; groups past G of other rows read
+  // the next row's values. Neither is ever used.
+  // Before the K loop chunks 0-1 are copied (a wait and a barrier publish
+  // them); then each group g of the loop copies load (g - g_first) % 8 of
+  // chunk (g - g_first)/8 + 2. A chunk's last copy is requested six groups
+  // before its first group is read (codes are read at most two groups
+  // ahead), and a buffer is refilled after two barriers past the last read
+  // of the chunk it held.
+  __device__ __forceinline__ void stage_issue(int chunk, int j) const {
+    const __amdgpu_buffer_rsrc_t r = (wave >> 2) ? br : sr;
+    const uint32_t soff = (uint32_t)(8 * j * G + g_first + chunk * kSbChunk) * 2u;
+    uint32_t *dst = sbl + (chunk % kSbBufs) * kSbBufWords + ((wave >> 2) * kBN + (wave & 3) * 64 + 8 * j) * kSbChunk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 2, (int)st_voff, (int)soff, 0, 0);
+  }
+  __device__ void stage_prologue() const {
+    if constexpr (CANON) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) stage_issue(c, j);
+    }
+  }
+  // once per group of the K loop, after the group's barrier
+  __device__ __forceinline__ void stage_step(int gv) const {
+    if constexpr (CANON) {
+      const int rel = __builtin_amdgcn_readfirstlane(gv) - g_first;
+      stage_issue(rel / 8 + 2, rel % 8);
     }
   }
 
@@ -381,9 +444,9 @@ struct TileIO {
 // (m0, n0) over groups [g_begin, g_end) on fp16 MFMA; cs[ni] receives the
 // power-of-two output scale 2^c of the lane's column blocks.
 template <int BITS, int MI, bool CANON>
-__device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages], int64_t m0,
-                                                 int64_t n0, int g_begin, int g_end, f32x4 (&acc)[MI][kNI],
-                                                 float (&cs)[kNI]) {
+__device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages],
+                                                 uint32_t *sbl, int64_t m0, int64_t n0, int g_begin, int g_end,
+                                                 f32x4 (&acc)[MI][kNI], float (&cs)[kNI]) {
   constexpr int S = kStages;
   using IO = TileIO<BITS, MI, CANON>;
   using LC = typename IO::LC;
@@ -400,7 +463,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // work sits between MFMAs instead of in bursts
   constexpr int kPieces = 8 * kNI;
   constexpr int kPerStep = (kPieces + kHalf - 1) / kHalf;
-  const IO io(a, m0, n0);
+  const IO io(a, m0, n0, sbl, g_begin);
   const int h = io.h;
 
   // per-column fp16 range: weights of a column whose bound reaches 65504 are
@@ -427,12 +490,13 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // group g.
   u32x4 bf[kNI][2];
   uint32_t cq[S - 1][kNI][LC::kWords];
-  uint32_t sq[S - 1][kNI];   // tiled: s | b << 16; canonical: s
-  uint32_t bq[S - 1][kNI];   // canonical: b (unused when tiled)
-  // piece i of the B fragments from cq[0]/sq[0]: fragment (ni, c) = i / 4, word i % 4
+  uint32_t sq[S - 1][kNI];   // tiled: s | b << 16
+  uint32_t bq[S - 1][kNI];   // unused
+  uint32_t sbc[kNI];         // canonical: s | b << 16 of the group being dequantized
+  // piece i of the B fragments from cq[0] and its scale/bias: fragment (ni, c) = i / 4, word i % 4
   auto dequant_piece = [&](u32x4 (&dst)[kNI][2], bool valid, int i) {
     const int f = i >> 2, p = i & 3, ni = f >> 1, c = f & 1;
-    const uint32_t v = valid ? (CANON ? (sq[0][ni] & 0xFFFFu) | (bq[0][ni] << 16) : sq[0][ni]) : 0u;
+    const uint32_t v = valid ? (CANON ? sbc[ni] : sq[0][ni]) : 0u;
     const h2 s2 = __builtin_bit_cast(h2, (v & 0xFFFFu) * 0x10001u) * wsc[ni];
     const h2 b2 = __builtin_bit_cast(h2, (v >> 16) * 0x10001u) * wsc[ni];
     if constexpr (BITS == 3 && !CANON) {
@@ -462,8 +526,10 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
         // the second half runs at raised wave priority (back to normal at the
         // end of the group): 1-1.5 % faster on the large shapes, measured
         __builtin_amdgcn_s_setprio(1);
+        io.stage_step(g);
         io.issue_x(XD, min(g + S - 1, g_end - 1));
         io.load_codes(cq[S - 2], sq[S - 2], bq[S - 2], min(g + S - 1, g_end - 1));
+        if constexpr (CANON) io.read_sb(min(g + 1, g_end - 1), sbc);
       }
       if (t + kAhead < kSteps) af[(t + kAhead) % (kAhead + 1)] = io.read_a(X, t + kAhead);
       else af[(t + kAhead) % (kAhead + 1)] = io.read_a(XN, t + kAhead - kSteps);
@@ -504,6 +570,10 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // Groups run S at a time (one per x stage) in straight-line code: loads
   // for a group past the end are clamped to the last group and its weights
   // dequantize to zero, so the accumulators never pass through a branch.
+  if constexpr (CANON) {
+    io.stage_prologue();
+    dma_barrier();  // the first staged chunks are read below
+  }
   if (g_begin < g_end) {
     io.load_codes(cq[0], sq[0], bq[0], g_begin);
     io.issue_x(xs[0], g_begin);
@@ -511,6 +581,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   }
   dma_barrier();  // first two stages and the first codes have arrived
   if (g_begin < g_end) {
+    if constexpr (CANON) io.read_sb(g_begin, sbc);
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
     io.load_codes(cq[0], sq[0], bq[0], min(g_begin + 1, g_end - 1));
@@ -541,7 +612,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
 // MFMAs, so it is read one step ahead.
 template <int BITS, int MI, bool CANON>
 __device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsigned char *const (&xs)[kStages],
-                                                      int64_t m0, int64_t n0, int g_begin, int g_end,
+                                                      uint32_t *sbl, int64_t m0, int64_t n0, int g_begin, int g_end,
                                                       f32x4 (&acc)[MI][kNI]) {
   constexpr int S = kStages;
   using IO = TileIO<BITS, MI, CANON>;
@@ -555,7 +626,7 @@ __device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsign
   constexpr int kStride = kHalf >= kPieces ? kHalf / kPieces : 1;
   constexpr int kPerStep = kHalf >= kPieces ? 1 : kPieces / kHalf;
   static_assert(kHalf >= kPieces ? kHalf % kPieces == 0 : kPieces % kHalf == 0, "pieces spread evenly");
-  const IO io(a, m0, n0);
+  const IO io(a, m0, n0, sbl, g_begin);
   const int h = io.h;
 
   h8 af[kAhead + 1];
@@ -565,10 +636,14 @@ __device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsign
   uint32_t bq[2][kNI];
   float sf[kNI], bfl[kNI];  // fp32 scale and bias of the slot being dequantized
 
-  auto prep_slot = [&](int slot, bool valid) {
+  // fp32 scale and bias of group gv (code slot `slot`); canonical: read from
+  // the staged chunk here
+  auto prep_slot = [&](int slot, int gv, bool valid) {
+    uint32_t sbc[kNI];
+    if constexpr (CANON) io.read_sb(min(gv, g_end - 1), sbc);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
-      const uint32_t v = valid ? (CANON ? (sq[slot][ni] & 0xFFFFu) | (bq[slot][ni] << 16) : sq[slot][ni]) : 0u;
+      const uint32_t v = valid ? (CANON ? sbc[ni] : sq[slot][ni]) : 0u;
       sf[ni] = f16_to_f32((uint16_t)(v & 0xFFFFu));
       bfl[ni] = f16_to_f32((uint16_t)(v >> 16));
     }
@@ -593,13 +668,14 @@ __device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsign
       const int tt = t % kHalf;
       if (t == 0) {
         io.load_codes(cq[1], sq[1], bq[1], min(g + 1, g_end - 1));
-        prep_slot(0, g < g_end);
+        prep_slot(0, g, g < g_end);
       }
       if (t == kHalf) {
         dma_barrier();  // stage g+1 and the codes of g+1 have landed, stage g-1 is free
         __builtin_amdgcn_s_setprio(1);
+        io.stage_step(g);
         io.issue_x(XD, min(g + S - 1, g_end - 1));
-        prep_slot(1, g + 1 < g_end);
+        prep_slot(1, g + 1, g + 1 < g_end);
       }
       if (t + kAhead < kSteps) af[(t + kAhead) % (kAhead + 1)] = io.read_a(X, t + kAhead);
       else af[(t + kAhead) % (kAhead + 1)] = io.read_a(XN, t + kAhead - kSteps);
@@ -639,6 +715,10 @@ __device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsign
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (CANON) {
+    io.stage_prologue();
+    dma_barrier();  // the first staged chunks are read below
+  }
   if (g_begin < g_end) {
     io.load_codes(cq[0], sq[0], bq[0], g_begin);
     io.issue_x(xs[0], g_begin);
@@ -646,7 +726,7 @@ __device__ __forceinline__ void tile_accumulate_split(const Gemm3Args &a, unsign
   }
   dma_barrier();  // first two stages and the codes of the first group have arrived
   if (g_begin < g_end) {
-    prep_slot(0, true);
+    prep_slot(0, g_begin, true);
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) dequant_piece(0, 0, i);  // k-block 0 of the first group
 #pragma unroll
@@ -785,6 +865,8 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x2[kXStage];
   __shared__ __attribute__((aligned(16))) float rs_lds[kBM];
+  // canonical scale/bias staging (unused with tiled weights)
+  __shared__ __attribute__((aligned(16))) uint32_t sbl[CANON ? kSbBufs * kSbBufWords : 4];
   unsigned char *const xs[kStages] = {x0, x1, x2};
   // FAST: the row scales of a tile's rows, requested at the tile's start (one
   // value per thread), written to LDS once the K loop has ended (its last
@@ -802,11 +884,11 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   auto accumulate = [&](auto &acc_, int64_t m0, int64_t n0, int gb, int ge, float (&cs)[kNI]) {
     constexpr int MI = sizeof(acc_) / sizeof(acc_[0]);
     if constexpr (SPLIT) {
-      tile_accumulate_split<BITS, MI, CANON>(a, xs, m0, n0, gb, ge, acc_);
+      tile_accumulate_split<BITS, MI, CANON>(a, xs, sbl, m0, n0, gb, ge, acc_);
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni) cs[ni] = 1.f;
     } else {
-      tile_accumulate3<BITS, MI, CANON>(a, xs, m0, n0, gb, ge, acc_, cs);
+      tile_accumulate3<BITS, MI, CANON>(a, xs, sbl, m0, n0, gb, ge, acc_, cs);
     }
   };
   const int tiles_n = (int)((a.N + kBN - 1) / kBN);
