@@ -16,10 +16,48 @@ __device__ __forceinline__ int row_exponent(float mx) {
   return ex > 134 ? 120 : min(max(ex - 14, -126), 120);
 }
 
+// Optional AdaLN scale modulation of the activations: value k of row m
+// becomes x * (1 + scale[m / mod_rows, k]), in fp32 (1 + scale rounded once,
+// the product rounded once), before the row maximum and the fp16 rounding.
+struct Modulation {
+  const float *scale;  // fp32 [ceil(M / rows), K]; null: none
+  int64_t rows;        // activation rows per scale row (>= 1)
+};
+
+// The 8 (possibly modulated) fp32 values of 16-byte vector i of row m.
+template <bool MOD>
+__device__ __forceinline__ void load8(const u32x4 &v, const Modulation &md, int64_t m, int64_t K, int i, float (&f)[8]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f[2 * t] = bf16_lo(v[t]);
+    f[2 * t + 1] = bf16_hi(v[t]);
+  }
+  if constexpr (MOD) {
+    const float4 *sp = reinterpret_cast<const float4 *>(md.scale + (int64_t)((uint64_t)m / (uint64_t)md.rows) * K) + 2 * i;
+    const float4 s0 = sp[0], s1 = sp[1];
+    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = f[j] * (1.0f + sc[j]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8_f16(const float (&f)[8], float inv) {
+  u32x4 o;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const _Float16 lo = (_Float16)(f[2 * t] * inv);
+    const _Float16 hi = (_Float16)(f[2 * t + 1] * inv);
+    o[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return o;
+}
+
 // x (bf16) -> x16 (fp16) with a power-of-two scale per row. One block per
 // row: the row's max magnitude picks e (row_exponent); every value is
 // multiplied by 2^-e (exact) and rounded to fp16.
-__global__ __launch_bounds__(256) void x16_kernel(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t K) {
+template <bool MOD>
+__global__ __launch_bounds__(256) void x16_kernel(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t K,
+                                                  Modulation md) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(x + m * K);
@@ -27,12 +65,10 @@ __global__ __launch_bounds__(256) void x16_kernel(const uint16_t *x, uint16_t *x
   const int nv = (int)(K / 8);
   float mx = 0.f;
   for (int i = threadIdx.x; i < nv; i += 256) {
-    const u32x4 v = src[i];
+    float f[8];
+    load8<MOD>(src[i], md, m, K, i, f);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      mx = fmaxf(mx, fabsf(bf16_lo(v[t])));
-      mx = fmaxf(mx, fabsf(bf16_hi(v[t])));
-    }
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(f[j]));
   }
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -42,37 +78,36 @@ __global__ __launch_bounds__(256) void x16_kernel(const uint16_t *x, uint16_t *x
   const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
   if (threadIdx.x == 0) rowscale[m] = __uint_as_float((uint32_t)(127 + e) << 23);
   for (int i = threadIdx.x; i < nv; i += 256) {
-    const u32x4 v = src[i];
-    u32x4 o;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const _Float16 lo = (_Float16)(bf16_lo(v[t]) * inv);
-      const _Float16 hi = (_Float16)(bf16_hi(v[t]) * inv);
-      o[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    dst[i] = o;
+    float f[8];
+    load8<MOD>(src[i], md, m, K, i, f);
+    dst[i] = pack8_f16(f, inv);
   }
 }
 
 // Same conversion with one wave per row and the row held in registers (K up
 // to 64*8*V): one read of x instead of two.
-template <int V>
+template <int V, bool MOD>
 __global__ __launch_bounds__(256) void x16_row_kernel(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M,
-                                                      int64_t K) {
+                                                      int64_t K, Modulation md) {
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (m >= M) return;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(x + m * K);
   u32x4 *dst = reinterpret_cast<u32x4 *>(x16 + m * K);
   const int nv = (int)(K / 8);
-  u32x4 v[V];
+  float f[V][8];
   float mx = 0.f;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int i = lane + 64 * j;
-    v[j] = i < nv ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    if (i < nv) {
+      load8<MOD>(src[i], md, m, K, i, f[j]);
+    } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(v[j][t])), fabsf(bf16_hi(v[j][t]))));
+      for (int t = 0; t < 8; ++t) f[j][t] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf(f[j][t]));
   }
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   const int e = row_exponent(mx);
@@ -82,14 +117,7 @@ __global__ __launch_bounds__(256) void x16_row_kernel(const uint16_t *x, uint16_
   for (int j = 0; j < V; ++j) {
     const int i = lane + 64 * j;
     if (i >= nv) break;
-    u32x4 o;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const _Float16 lo = (_Float16)(bf16_lo(v[j][t]) * inv);
-      const _Float16 hi = (_Float16)(bf16_hi(v[j][t]) * inv);
-      o[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    dst[i] = o;
+    dst[i] = pack8_f16(f[j], inv);
   }
 }
 
@@ -151,13 +179,23 @@ Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits, b
   return p;
 }
 
-hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream) {
+namespace {
+template <bool MOD>
+void launch_x16_mod(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, Modulation md,
+                    hipStream_t stream) {
   const int64_t vecs = (K / 8 + 63) / 64;  // 16-byte vectors per lane for one wave per row
   const dim3 grid4((unsigned)((M + 3) / 4));
-  if (vecs <= 4) hipLaunchKernelGGL(x16_row_kernel<4>, grid4, dim3(256), 0, stream, x, x16, rowscale, M, K);
-  else if (vecs <= 9) hipLaunchKernelGGL(x16_row_kernel<9>, grid4, dim3(256), 0, stream, x, x16, rowscale, M, K);
-  else if (vecs <= 16) hipLaunchKernelGGL(x16_row_kernel<16>, grid4, dim3(256), 0, stream, x, x16, rowscale, M, K);
-  else hipLaunchKernelGGL(x16_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, x16, rowscale, K);
+  if (vecs <= 4) hipLaunchKernelGGL((x16_row_kernel<4, MOD>), grid4, dim3(256), 0, stream, x, x16, rowscale, M, K, md);
+  else if (vecs <= 9) hipLaunchKernelGGL((x16_row_kernel<9, MOD>), grid4, dim3(256), 0, stream, x, x16, rowscale, M, K, md);
+  else if (vecs <= 16) hipLaunchKernelGGL((x16_row_kernel<16, MOD>), grid4, dim3(256), 0, stream, x, x16, rowscale, M, K, md);
+  else hipLaunchKernelGGL((x16_kernel<MOD>), dim3((unsigned)M), dim3(256), 0, stream, x, x16, rowscale, K, md);
+}
+}  // namespace
+
+hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream,
+                      const float *mod_scale, int64_t mod_rows) {
+  if (mod_scale) launch_x16_mod<true>(x, x16, rowscale, M, K, Modulation{mod_scale, mod_rows}, stream);
+  else launch_x16_mod<false>(x, x16, rowscale, M, K, Modulation{nullptr, 1}, stream);
   return hipGetLastError();
 }
 

@@ -616,6 +616,19 @@ QL_API int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x
              : QL_EHIP;
 }
 
+QL_API int qlinear_fast_activations_adaln(const void *x, const float *scale, int64_t scale_rows, int64_t M, int64_t K,
+                                          void *x16, float *rowscale, void *stream) {
+  if (M < 0 || K < 0 || K % kGroup || scale_rows < 1) return QL_EINVAL;
+  if (M == 0 || K == 0) return QL_OK;
+  if (!x || !x16 || !rowscale || !scale) return QL_EINVAL;
+  if (!aligned16(x) || !aligned16(x16) || !aligned16(scale)) return QL_EALIGN;
+  set_last_path("fast_activations_adaln");
+  return ql::launch_x16(static_cast<const uint16_t *>(x), static_cast<uint16_t *>(x16), rowscale, M, K,
+                        reinterpret_cast<hipStream_t>(stream), scale, scale_rows) == hipSuccess
+             ? QL_OK
+             : QL_EHIP;
+}
+
 QL_API int qlinear_group_sums(const void *x, int64_t M, int64_t K, float *xsum, int64_t ld_xsum, void *stream) {
   if (M < 0 || K < 0 || K % kGroup) return QL_EINVAL;
   if (M == 0 || K == 0) return QL_OK;

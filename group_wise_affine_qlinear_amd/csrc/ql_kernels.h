@@ -90,7 +90,10 @@ struct Gemm3Plan {
 // cut every tile along M into row pieces so the grid covers the CUs (needs no
 // scratch, unlike a K split).
 Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits, bool fill_by_pieces = false);
-hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream);
+// mod_scale (fp32 [ceil(M / mod_rows), K], or null): AdaLN scale, value k of
+// row m taken as x * (1 + mod_scale[m / mod_rows, k]) before the conversion
+hipError_t launch_x16(const uint16_t *x, uint16_t *x16, float *rowscale, int64_t M, int64_t K, hipStream_t stream,
+                      const float *mod_scale = nullptr, int64_t mod_rows = 1);
 hipError_t launch_gemm3(int bits, const Gemm3Args &a, hipStream_t stream);
 // SPLIT numerics (gemm4.hip): same arguments, x16 holds the caller's bf16 x,
 // rowscale is unused, glu and gate must be off.

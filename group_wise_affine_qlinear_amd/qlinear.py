@@ -29,7 +29,8 @@ EXPORTED = (
     "qlinear_pack_host", "qlinear_unpack_host", "qlinear_quantize_rtn_host", "qlinear_quantize_rtn",
     "qlinear_dequantize", "qlinear_status_string", "qlinear_last_path", "qlinear_version",
     "qlinear_group_sums", "qlinear_group_sums_ld", "qlinear_tiled_words", "qlinear_tiled_sb_words",
-    "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations", "qlinear_repack_glu",
+    "qlinear_repack", "qlinear_unrepack", "qlinear_fast_activations", "qlinear_fast_activations_adaln",
+    "qlinear_repack_glu",
     "qlinear_unrepack_glu", "qlinear_quantize_imatrix", "qlinear_forward_workspace_bytes",
     "qlinear_forward_noalloc", "qlinear_forward_noalloc_max_scratch",
 )
@@ -113,6 +114,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qlinear_group_sums": ([vp, i64, i64, vp, i64, vp], i32),
         "qlinear_group_sums_ld": ([i64], i64),
         "qlinear_fast_activations": ([vp, i64, i64, vp, vp, vp], i32),
+        "qlinear_fast_activations_adaln": ([vp, vp, i64, i64, i64, vp, vp, vp], i32),
         "qlinear_tiled_words": ([i32, i64, i64], sz),
         "qlinear_tiled_sb_words": ([i64, i64], sz),
         "qlinear_repack": ([vp, vp, vp, i32, i32, i64, i64, vp, vp, vp], i32),
@@ -305,6 +307,25 @@ def qlinear_fast_activations(x, M, K, x16=None, rowscale=None, stream=None):
                                       _dev_ptr(rowscale, "rowscale", (torch.float32,), (M,)),
                                       _stream_handle(stream))
     _check(st, "qlinear_fast_activations")
+    return x16, rowscale
+
+
+def qlinear_fast_activations_adaln(x, scale, scale_rows, M, K, x16=None, rowscale=None, stream=None):
+    """C ``qlinear_fast_activations_adaln``: FAST-mode activations of x * (1 + scale[m // scale_rows])."""
+    torch = _torch()
+    lib = load_library()
+    if x16 is None:
+        x16 = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    if rowscale is None:
+        rowscale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    samples = -(-M // scale_rows) if scale_rows > 0 else 0
+    st = lib.qlinear_fast_activations_adaln(_dev_ptr(x, "x", _u16(torch), (M, K)),
+                                            _dev_ptr(scale, "scale", (torch.float32,), (samples, K)),
+                                            scale_rows, M, K,
+                                            _dev_ptr(x16, "x16", (torch.float16, torch.int16), (M, K)),
+                                            _dev_ptr(rowscale, "rowscale", (torch.float32,), (M,)),
+                                            _stream_handle(stream))
+    _check(st, "qlinear_fast_activations_adaln")
     return x16, rowscale
 
 

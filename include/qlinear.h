@@ -277,6 +277,25 @@ int64_t qlinear_group_sums_ld(int64_t M);
  */
 int qlinear_fast_activations(const void *x, int64_t M, int64_t K, void *x16, float *rowscale, void *stream);
 
+/*
+ * FAST-mode activations of an AdaLN-modulated input (Ideogram 4 paper notes,
+ * section 2.1 pipeline: each DiT block takes an AdaLN scale, with its gate,
+ * from the timestep embedding; Ideogram-4-IQ4_M card, Conversion section:
+ * the modulation projection emits a per-layer scale and a tanh gate). The
+ * pages give no formula; the reading taken is the zero-centred one, value
+ * k of row m becomes x[m, k] * (1 + scale[m / scale_rows, k]) (integer
+ * division: the rows of one sample share its scale row; no shift term).
+ * This call applies it on the way into fp16: in fp32, t = 1 + scale (one
+ * rounding) and v = x * t (one rounding), then the row maximum, exponent e
+ * and x16 = fp16(v * 2^-e) exactly as qlinear_fast_activations does for v.
+ * The gate half of the modulation is the QL_EPI_GATE_RESIDUAL epilogue.
+ * scale is fp32 [ceil(M / scale_rows), K], 16-byte aligned; scale_rows >= 1.
+ * Returns QL_EINVAL for bad sizes or null pointers, QL_EALIGN for misaligned
+ * x, x16 or scale.
+ */
+int qlinear_fast_activations_adaln(const void *x, const float *scale, int64_t scale_rows, int64_t M, int64_t K,
+                                   void *x16, float *rowscale, void *stream);
+
 /* Bytes of device workspace that serve every qlinear_forward_ex call of this
  * shape with automatic path, tile and split, under any numerics mode, layout
  * or epilogue (an upper bound over the plans; for 3-bit codes it includes the

@@ -57,6 +57,14 @@ the gate (already through tanh) multiplies a branch's output projection
 feature-wise, per sample, before it is added to the residual stream:
 out[m, n] = residual[m, n] + gate[m // rows_per_sample, n] * y[m, n].
 ``gate_residual`` writes that out in float64.
+
+AdaLN scale (the same two passages: the block's input is modulated by a
+per-layer scale emitted from the timestep embedding; the pages name a scale
+and a gate, no shift, and print no formula). Reading taken: the zero-centred
+form, each input channel k of the rows of one sample multiplied by one plus
+that sample's scale: x_mod[m, k] = x[m, k] * (1 + scale[m // rows_per_sample, k]).
+``adaln_modulate`` writes it out in float64 and ``forward_modulated`` takes
+the plain product of the modulated input with the dequantized weights.
 """
 from __future__ import annotations
 
@@ -72,7 +80,7 @@ __all__ = [
     "quantize_rtn", "pack", "unpack", "dequantize", "gemm_f64", "forward",
     "forward_rows", "error_metrics", "timed_forward",
     "fast_weights_f16", "fast_activations_f16", "forward_fast", "forward_fast_rows", "silu", "swiglu",
-    "gate_residual",
+    "gate_residual", "adaln_modulate", "forward_modulated",
     "IMATRIX_DELTAS", "quantize_imatrix", "weighted_error",
 ]
 
@@ -486,6 +494,25 @@ def gate_residual(y: np.ndarray, residual: np.ndarray, gate: np.ndarray, gate_ro
     sample = np.arange(y.shape[0]) // gate_rows
     assert gate.shape[0] > (sample[-1] if len(sample) else -1)
     return residual + gate[sample] * y
+
+
+def adaln_modulate(x_bf16, scale, rows_per_sample: int) -> np.ndarray:
+    """AdaLN scale applied to a bf16 input: row m belongs to sample
+    m // rows_per_sample, and x_mod[m, k] = x[m, k] * (1 + scale[sample, k]),
+    float64 [M, K]."""
+    x = bf16_bits_to_f64(x_bf16)
+    scale = np.asarray(scale, dtype=np.float64)
+    assert rows_per_sample >= 1 and scale.ndim == 2 and scale.shape[1] == x.shape[1]
+    sample = np.arange(x.shape[0]) // rows_per_sample
+    assert scale.shape[0] > (sample[-1] if len(sample) else -1)
+    return x * (1.0 + scale[sample])
+
+
+def forward_modulated(x_bf16, scale, rows_per_sample, packed, s16, b16, bits, k, group: int = GROUP):
+    """Plain product of the AdaLN-modulated input with the dequantized weights:
+    adaln_modulate(x) @ W_hat^T, float64 [M, N]."""
+    w_hat = dequantize(unpack(packed, bits, k), s16, b16, group)
+    return adaln_modulate(x_bf16, scale, rows_per_sample) @ np.asarray(w_hat, dtype=np.float64).T
 
 
 def error_metrics(y: np.ndarray, y_ref: np.ndarray) -> dict:

@@ -230,6 +230,17 @@ def test_device_entry_points_validate_before_launch(lib):
     assert lib.qlinear_quantize_rtn(0, 4, 64, 4, 64, 0x2000, 0x3000, 0x4000, None, None) == ql.QL_EINVAL
 
 
+def test_adaln_prepass_validates_before_launch(lib):
+    f = lib.qlinear_fast_activations_adaln
+    # empty shapes are no-ops; bad sizes, nulls and misaligned pointers are
+    # refused before anything touches a device
+    assert f(None, None, 1, 0, 64, None, None, None) == ql.QL_OK
+    assert f(0x1000, 0x2000, 0, 4, 64, 0x3000, 0x4000, None) == ql.QL_EINVAL   # scale_rows < 1
+    assert f(0x1000, 0x2000, 1, 4, 65, 0x3000, 0x4000, None) == ql.QL_EINVAL   # K not a multiple of 64
+    assert f(0x1000, None, 1, 4, 64, 0x3000, 0x4000, None) == ql.QL_EINVAL     # no scale
+    assert f(0x1000, 0x2004, 1, 4, 64, 0x3000, 0x4000, None) == ql.QL_EALIGN   # scale not 16-byte aligned
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ql, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):

@@ -623,6 +623,64 @@ def test_gate_residual_special_cases():
     np.testing.assert_allclose(oracle.gate_residual(y, res, g7, 1), res + g7 * y, rtol=1e-15)
 
 
+# ---- AdaLN scale application ----------------------------------------------
+
+def _bf16(vals):
+    return inputs.f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def test_adaln_modulate_hand_worked():
+    # 3 rows of K = 2 (exact in bf16), 2 rows per sample: rows 0, 1 take scale row 0
+    x = _bf16([[1.0, 2.0], [-3.0, 0.5], [4.0, -8.0]])
+    scale = np.array([[0.5, -0.25], [1.0, -1.5]])
+    got = oracle.adaln_modulate(x, scale, 2)
+    assert np.array_equal(got, np.array([[1.5, 1.5], [-4.5, 0.375], [8.0, 4.0]]))
+
+
+def test_adaln_modulate_special_cases():
+    x = inputs.activations_bf16(6, 64, 71)
+    xf = oracle.bf16_bits_to_f64(x)
+    # zero scale is the identity, scale -1 annihilates, scale 1 doubles (exact)
+    assert np.array_equal(oracle.adaln_modulate(x, np.zeros((2, 64)), 3), xf)
+    assert np.array_equal(oracle.adaln_modulate(x, -np.ones((1, 64)), 6), np.zeros_like(xf))
+    assert np.array_equal(oracle.adaln_modulate(x, np.ones((6, 64)), 1), 2.0 * xf)
+
+
+def test_adaln_forward_brute_force():
+    # y[m, n] = sum_k x[m, k] (1 + s[m // r, k]) W[n, k], one term at a time
+    rng = np.random.default_rng(72)
+    M, N, K, r = 5, 3, 64, 2
+    w = inputs.weights(N, K, 73)
+    q, s16, b16 = oracle.quantize_rtn(w, 4)
+    packed = oracle.pack(q, 4)
+    x = inputs.activations_bf16(M, K, 74)
+    scale = rng.uniform(-0.9, 0.9, size=(3, K))
+    got = oracle.forward_modulated(x, scale, r, packed, s16, b16, 4, K)
+    xf = oracle.bf16_bits_to_f64(x)
+    wf = oracle.dequantize(q, s16, b16).astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            ref = math.fsum(xf[m, k] * (1.0 + scale[m // r, k]) * wf[n, k] for k in range(K))
+            assert abs(got[m, n] - ref) <= 1e-12 * math.fsum(abs(xf[m, k] * wf[n, k]) * 2 for k in range(K))
+
+
+def test_adaln_scale_acts_on_input_channels():
+    # for one sample, scaling input channel k equals scaling column k of the
+    # weights: x_mod @ W^T == x @ (W * (1 + s))^T (N != K, so a scale indexed
+    # by output channel would not even broadcast)
+    rng = np.random.default_rng(75)
+    M, N, K = 4, 5, 128
+    w = inputs.weights(N, K, 76)
+    q, s16, b16 = oracle.quantize_rtn(w, 8)
+    packed = oracle.pack(q, 8)
+    x = inputs.activations_bf16(M, K, 77)
+    scale = rng.uniform(-1.0, 1.0, size=(1, K))
+    got = oracle.forward_modulated(x, scale, M, packed, s16, b16, 8, K)
+    wf = oracle.dequantize(q, s16, b16).astype(np.float64)
+    ref = oracle.bf16_bits_to_f64(x) @ (wf * (1.0 + scale[0])[None, :]).T
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 # ---- importance-weighted fit (the pages' imatrix objective) ---------------
 
 def _outlier_importance(k, wid):
