@@ -457,6 +457,14 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                      tiled_in ? nullptr : static_cast<const uint16_t *>(a->biases),
                      tiled_in ? static_cast<const uint32_t *>(a->scales) : nullptr,
                      a->out, a->M, a->N, a->K, G, out_bf16, tiled_in ? 1 : 0};
+    // one or two rows on canonical weights: the lane-along-K GEMV (its
+    // loads read whole lines of a row); QLINEAR_NO_GEMV=1 keeps the skinny
+    // kernel, for comparisons
+    if (ql::gemv_chunks_per_lane(a->bits, a->M, a->K, tiled_in ? 1 : 0) > 0 && !env_int("QLINEAR_NO_GEMV", 0)) {
+      std::snprintf(buf, sizeof(buf), "gemv_b%d_m%lld_canonical", a->bits, (long long)a->M);
+      set_last_path(buf);
+      return ql::launch_gemv(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;
+    }
     std::snprintf(buf, sizeof(buf), "skinny_b%d_m%lld_%s", a->bits, (long long)a->M, tiled_in ? "tiled" : "canonical");
     set_last_path(buf);
     return ql::launch_skinny(a->bits, s, stream) == hipSuccess ? QL_OK : QL_EHIP;

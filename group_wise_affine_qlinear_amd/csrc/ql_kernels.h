@@ -117,6 +117,10 @@ struct SkinnyArgs {
 };
 // M <= 16 only.
 hipError_t launch_skinny(int bits, const SkinnyArgs &a, hipStream_t stream);
+// Canonical rows, one or two rows of x (gemv.hip): chunks of 16 bytes per
+// lane and row for the shape, 0 when the GEMV does not serve it.
+int gemv_chunks_per_lane(int bits, int64_t M, int64_t K, int tiled);
+hipError_t launch_gemv(int bits, const SkinnyArgs &a, hipStream_t stream);
 
 // Tiled layout (see layout.hip): codes [N32][G][32 * 2*bits words], scale|bias [N32][G][32].
 // glu_f > 0: GLU row order for a [gate (glu_f); up (glu_f)] weight (see layout.hip).

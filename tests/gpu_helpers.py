@@ -16,6 +16,18 @@ RELF_DESIGN = 2e-5
 MAXABS_RMS_DESIGN = 2e-4
 
 
+def gemv_serves(bits, M, K):
+    """Whether a canonical-layout call of M rows goes to the lane-along-K GEMV:
+    one or two rows, 2/4/8-bit codes, at least 64 16-byte chunks per weight
+    row, at most 5 per lane, the lane's slice of x within 96 registers and x
+    within 32 KB of LDS."""
+    if M < 1 or M > 2 or bits not in (2, 4, 8):
+        return False
+    chunks = K * bits // 128
+    per_lane = -(-chunks // 64)
+    return chunks >= 64 and per_lane <= 5 and M * per_lane * (64 // bits) <= 96 and M * K * 2 <= 32768
+
+
 def torch_or_skip():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
