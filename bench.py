@@ -591,8 +591,9 @@ def main():
 
     # setup ends with SETTLE_S seconds of steps while the engine clock settles
     # under load (the first tens of steps after setup run up to 15 % slower);
-    # then the W untimed warm-up steps and the K timed steps
-    if args.profile == "none":
+    # then the W untimed warm-up steps and the K timed steps (a profiled run
+    # does the same, so the last K dispatches of its trace are the timed ones)
+    if args.profile in ("none", "step"):
         t_settle = time.perf_counter()
         while time.perf_counter() - t_settle < SETTLE_S:
             for _ in range(10):
