@@ -131,7 +131,8 @@ def time_calls(torch, fn, iters, warmup):
 # are 2.5 PFLOP/s on MI355X); skinny rows report GB/s as a fraction of HBM.
 # A call with a workspace runs what automatic dispatch picks there (FAST for
 # M > 16: the fp16 prepass and the GEMM, both inside the timed call); the
-# spec call qlinear_forward runs with no workspace (SPLIT for M > 16).
+# spec call qlinear_forward runs with no workspace (for M > 16 the FAST
+# GEMM converting x itself, plus its recomputation launch).
 
 def _ws(torch, ql, bits, M, N, K):
     return torch.empty(max(ql.qlinear_workspace_bytes(bits, M, N, K), 16), dtype=torch.uint8, device="cuda")
@@ -139,8 +140,9 @@ def _ws(torch, ql, bits, M, N, K):
 
 def case_gemm(torch, ql, inputs, M, N, K, bits, wid, xs="normal", entry="auto_tiled", copies=1, mode=None):
     """entry: auto_tiled / auto_canonical (qlinear_forward_ex with a workspace),
-    the benchmark spec (qlinear_forward, canonical, no workspace), split_tiled (SPLIT,
-    no workspace), exact_tiled / exact_canonical (EXACT with a workspace)."""
+    the benchmark spec (qlinear_forward, canonical, no workspace), split_tiled /
+    split_canonical (SPLIT, no workspace), exact_tiled / exact_canonical (EXACT
+    with a workspace)."""
     tiled = entry in ("auto_tiled", "split_tiled", "exact_tiled")
     sets = make_weights(torch, ql, inputs, N, K, bits, wid, copies, tiled=tiled)
     x = torch.from_numpy(inputs.activations_bf16(M, K, wid, xs).view("int16")).cuda()
@@ -150,7 +152,7 @@ def case_gemm(torch, ql, inputs, M, N, K, bits, wid, xs="normal", entry="auto_ti
     kw = {}
     if entry.startswith("exact"):
         kw["mode"] = ql.QL_MODE_EXACT
-    if entry == "split_tiled":
+    if entry.startswith("split"):
         kw["mode"] = ql.QL_MODE_SPLIT
     if mode is not None:
         kw["mode"] = mode
@@ -163,7 +165,7 @@ def case_gemm(torch, ql, inputs, M, N, K, bits, wid, xs="normal", entry="auto_ti
             ql.qlinear_forward(x, p, s, b, bits, 64, M, N, K, out)
         else:
             ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=layout,
-                                  workspace=None if entry == "split_tiled" else ws, **kw)
+                                  workspace=None if entry.startswith("split") else ws, **kw)
 
     return call, {"flop": 2.0 * M * N * K, "weight_copies_rotated": copies}
 
@@ -190,7 +192,10 @@ COND_COPIES = 4       # 4 x 138 MB of llm_cond_proj weights
 CASES = {
     # the headline shape through the other entry points and numerics
     "north_star_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6, entry="north_star"),
-                                        "qlinear_forward: canonical weights, no workspace (SPLIT GEMM)"),
+                                        "qlinear_forward: canonical weights, no workspace (FAST GEMM converting x)"),
+    "split_canonical_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6,
+                                                              entry="split_canonical"),
+                                             "SPLIT GEMM on canonical weights, no workspace"),
     "split_tiled_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6, entry="split_tiled"),
                                          "SPLIT GEMM on tiled weights, no workspace"),
     "fast_canonical_M4096_K4608_N4608_q4": (case_gemm, dict(M=4096, N=4608, K=4608, bits=4, wid=6,
@@ -206,7 +211,7 @@ CASES = {
                                   "prepass + FAST GEMM, tiled"),
     "qkv_north_star_M4608_K4608_N13824_q4": (case_gemm, dict(M=4608, N=13824, K=4608, bits=4, wid=2, xs="outlier",
                                                               entry="north_star"),
-                                             "qlinear_forward (SPLIT)"),
+                                             "qlinear_forward (FAST GEMM converting x)"),
     # SwiGLU MLP at 1024^2: gate/up (8-bit and 4-bit) and down (4- and 8-bit)
     "mlp_gateup_M4608_K4608_N24576_q8": (case_gemm, dict(M=4608, N=24576, K=4608, bits=8, wid=3),
                                          "prepass + FAST GEMM, tiled"),
@@ -229,7 +234,7 @@ CASES = {
         "EXACT on the canonical code rows, split along K"),
     "llm_cond_proj_M512_K53248_N4608_q4_north_star": (
         case_gemm, dict(M=512, N=4608, K=53248, bits=4, wid=4, xs="slices", entry="north_star", copies=COND_COPIES),
-        "qlinear_forward: no workspace, so no K split (SPLIT GEMM in row pieces)"),
+        "qlinear_forward: no workspace, so no K split (FAST GEMM converting x, in row pieces)"),
     # AdaLN / timestep projections (skinny path, HBM-bound)
     "adaln_skinny_M1_K4608_N27648_q4_tiled": (case_skinny, dict(M=1, N=27648, K=4608, bits=4, wid=40, tiled=True,
                                                                 copies=SKINNY_COPIES), ""),

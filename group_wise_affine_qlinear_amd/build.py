@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlinear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["gemm3.hip", "gemm4.hip", "gemm2.hip", "host.cpp", "gemm.hip", "skinny.hip", "gemv.hip", "misc.hip",
+SOURCES = ["gemm3.hip", "gemm3o.hip", "gemm4.hip", "gemm2.hip", "host.cpp", "gemm.hip", "skinny.hip", "gemv.hip", "misc.hip",
            "layout.hip"]
 
 COMMON_FLAGS = [

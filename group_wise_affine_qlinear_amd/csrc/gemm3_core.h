@@ -58,6 +58,7 @@ namespace g3 {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf2;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256, kBN = 256, kNW = 8, kNT = 64 * kNW;
 constexpr int kWN = 32, kMI = kBM / 16, kNI = kWN / 16;  // a wave: all rows x 32 columns
@@ -352,6 +353,70 @@ struct TileIO {
     }
   }
 
+  // Vector-memory loads load_codes issues (they follow a group's x copies).
+  static constexpr int kCodeLoads = CANON ? kNI : (BITS == 3 ? 3 : 2) * kNI;
+
+  // In-kernel fp16 activations (FAST without a prepass). Copy i of stage X
+  // (the 16 bytes this lane brought in: 8 bf16 values of one row) becomes 8
+  // fp16 values in place, fp16 = RTZ(x): exact for 2^-17 <= |x| <= 65504
+  // (bf16 carries 8 significant bits), off by less than 2^-24 below. Only the
+  // lane that copied the bytes touches them, once its own copy has landed.
+  // The largest magnitude of the row seen so far is kept as a bf16 bit
+  // pattern (sign cleared; integer order is value order, a NaN counts as
+  // largest) in 16-bit slot i % 2 of mx[i / 2].
+  static constexpr int kMxRegs = (XPW + 1) / 2;
+  __device__ __forceinline__ void convert_copy(unsigned char *X, int i, uint32_t (&mx)[kMxRegs]) const {
+    if (x_issuer) {
+      u32x4 *p = reinterpret_cast<u32x4 *>(X + (wave * XPW + i) * 1024 + lane * 16);
+      const u32x4 v = *p;
+      u32x4 o;
+      u16x2 m = {0, 0};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t w = v[t];
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+        o[t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                       __uint_as_float(w & 0xFFFF0000u)));
+      }
+      *p = o;
+      // both halves -> the copy's largest, then into its slot
+      m = __builtin_elementwise_max(m, __builtin_shufflevector(m, m, 1, 0));
+      const uint32_t mw = __builtin_bit_cast(uint32_t, m) & ((i & 1) ? 0xFFFF0000u : 0x0000FFFFu);
+      mx[i / 2] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx[i / 2]),
+                                                                         __builtin_bit_cast(u16x2, mw)));
+    }
+  }
+
+  // Whether a row this block copied lies outside the range where the
+  // unscaled fp16 activations keep FAST's accuracy: a largest magnitude above
+  // 2^15 (or a non-finite value), or a nonzero largest magnitude below 2^-6
+  // (values below 2^-17 round with an absolute error up to 2^-24, which must
+  // stay small against the row). A row's maximum combines the 8 lanes that
+  // copy it (lanes 8r .. 8r+7 of a copy) with DPP moves; the block's answer
+  // comes back from a barrier.
+  __device__ __forceinline__ bool rows_out_of_range(const uint32_t (&mx)[kMxRegs]) const {
+    int bad = 0;
+    if (x_issuer) {
+#pragma unroll
+      for (int r = 0; r < kMxRegs; ++r) {
+        u16x2 v = __builtin_bit_cast(u16x2, mx[r]);
+        v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2, __builtin_amdgcn_update_dpp(
+                                                               0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+        v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2, __builtin_amdgcn_update_dpp(
+                                                               0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+        v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2, __builtin_amdgcn_update_dpp(
+                                                               0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (2 * r + hh >= XPW) continue;
+          const uint32_t h16 = v[hh];
+          bad |= (h16 > 0x4700u) || (h16 != 0u && h16 < 0x3C80u);
+        }
+      }
+    }
+    return __syncthreads_or(bad) != 0;
+  }
+
   // Canonical scale/bias staging. Per-group loads of a lane's own column
   // touch 16 rows for 2 bytes each; a staging load instead covers 8 groups
   // of 8 columns (16 bytes of each row's line) and copies them straight to
@@ -443,8 +508,13 @@ struct TileIO {
 // FAST numerics: accumulates rows m0 .. m0 + 16*MI of the block tile at
 // (m0, n0) over groups [g_begin, g_end) on fp16 MFMA; cs[ni] receives the
 // power-of-two output scale 2^c of the lane's column blocks.
-template <int BITS, int MI, bool CANON>
-__device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages],
+// ONLINE: x arrives as the caller's bf16 and each wave converts the rows it
+// copied to fp16 in LDS (convert_copy) in the first half of the group before
+// their first read, one copy every third MFMA step (converting them all at
+// one step pushes the loop past the register file); the return value says
+// whether a row fell outside the range where that keeps FAST's accuracy.
+template <int BITS, int MI, bool CANON, bool ONLINE = false>
+__device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned char *const (&xs)[kStages],
                                                  uint32_t *sbl, int64_t m0, int64_t n0, int g_begin, int g_end,
                                                  f32x4 (&acc)[MI][kNI], float (&cs)[kNI]) {
   constexpr int S = kStages;
@@ -463,6 +533,8 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // work sits between MFMAs instead of in bursts
   constexpr int kPieces = 8 * kNI;
   constexpr int kPerStep = (kPieces + kHalf - 1) / kHalf;
+  // ONLINE: the step of the first half at which copy i of the next stage is converted
+  constexpr auto conv_step = [](int i) { return 2 + 3 * i < kHalf - 1 ? 2 + 3 * i : kHalf - 1; };
   const IO io(a, m0, n0, sbl, g_begin);
   const int h = io.h;
 
@@ -489,6 +561,7 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // g+1 .. g+S-2 are held (cq[0] = g+1); those of g+S-1 are requested in
   // group g.
   u32x4 bf[kNI][2];
+  uint32_t xmx[IO::kMxRegs] = {};  // ONLINE: largest magnitudes of the rows this lane converts
   uint32_t cq[S - 1][kNI][LC::kWords];
   uint32_t sq[S - 1][kNI];   // tiled: s | b << 16
   uint32_t bq[S - 1][kNI];   // unused
@@ -516,11 +589,23 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
   // into XD and their codes are requested. Second half: MFMAs, with the next
   // group's B fragments dequantized in between and the first A fragments of
   // XN read ahead, so the next group starts without a stall.
-  auto step = [&](const unsigned char *X, const unsigned char *XN, unsigned char *XD, int g) {
+  auto step = [&](const unsigned char *X, unsigned char *XN, unsigned char *XD, int g) {
     u32x4 bn[kNI][2];
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
       const int c = t / MI, mi = t % MI;
+      if constexpr (ONLINE) {
+        // stage g+1 was copied in the middle of group g-1, and only the
+        // codes of g+1 were requested after it: once at most that many
+        // vector loads are in flight, this wave's copies have landed
+        if (t == conv_step(0)) {
+          constexpr int n = IO::kCodeLoads;
+          __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | 0xF70);
+        }
+#pragma unroll
+        for (int i = 0; i < IO::XPW; ++i)
+          if (t == conv_step(i)) io.convert_copy(XN, i, xmx);
+      }
       if (t == kHalf) {
         dma_barrier();  // stage g+1 has landed everywhere, stage g-1 is free
         // the second half runs at raised wave priority (back to normal at the
@@ -528,6 +613,8 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
         __builtin_amdgcn_s_setprio(1);
         io.stage_step(g);
         io.issue_x(XD, min(g + S - 1, g_end - 1));
+        // ONLINE counts the code loads issued after the copies (see above)
+        if constexpr (ONLINE) __builtin_amdgcn_sched_barrier(0);
         io.load_codes(cq[S - 2], sq[S - 2], bq[S - 2], min(g + S - 1, g_end - 1));
         if constexpr (CANON) io.read_sb(min(g + 1, g_end - 1), sbc);
       }
@@ -580,6 +667,12 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
     io.issue_x(xs[1], min(g_begin + 1, g_end - 1));
   }
   dma_barrier();  // first two stages and the first codes have arrived
+  if constexpr (ONLINE) {
+    // the first group's stage; the second one's is converted during the first group
+#pragma unroll
+    for (int i = 0; i < IO::XPW; ++i) io.convert_copy(xs[0], i, xmx);
+    __syncthreads();
+  }
   if (g_begin < g_end) {
     if constexpr (CANON) io.read_sb(g_begin, sbc);
 #pragma unroll
@@ -600,6 +693,8 @@ __device__ __forceinline__ void tile_accumulate3(const Gemm3Args &a, unsigned ch
     for (int k = 0; k < S; ++k) step(xs[k], xs[(k + 1) % S], xs[(k + S - 1) % S], g + k);
   }
   dma_barrier();  // the copies requested past the last group have landed; every stage is free
+  if constexpr (ONLINE) return io.rows_out_of_range(xmx);
+  return false;
 }
 
 // SPLIT numerics: same tile walk on bf16 MFMA with hi and lo weight
@@ -852,6 +947,31 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
     }
 }
 
+// The output slice of this block's K range (fp32 partials [splits, M, N]
+// when K is split).
+__device__ __forceinline__ void *out_of_split(const Gemm3Args &a) {
+  return a.splits > 1 ? static_cast<void *>(static_cast<float *>(a.out) + (int64_t)blockIdx.y * a.M * a.N) : a.out;
+}
+
+// ONLINE: the mark of a tile left to the fixup kernel, a NaN in its first
+// output element (m0, n0), and the fixup kernel's test for it (every thread
+// reads the same element: the answer is uniform).
+template <bool OUT_BF16>
+__device__ __forceinline__ void mark_tile(void *out, int64_t N, int64_t m0, int64_t n0) {
+  if constexpr (OUT_BF16) reinterpret_cast<uint16_t *>(out)[m0 * N + n0] = 0x7FC1u;
+  else reinterpret_cast<uint32_t *>(out)[m0 * N + n0] = 0x7FC00001u;
+}
+template <bool OUT_BF16>
+__device__ __forceinline__ bool tile_marked(const void *out, int64_t N, int64_t m0, int64_t n0) {
+  if constexpr (OUT_BF16) {
+    const uint32_t v = reinterpret_cast<const uint16_t *>(out)[m0 * N + n0];
+    return __builtin_amdgcn_readfirstlane((v & 0x7FFFu) > 0x7F80u) != 0;
+  } else {
+    const uint32_t v = reinterpret_cast<const uint32_t *>(out)[m0 * N + n0];
+    return __builtin_amdgcn_readfirstlane((v & 0x7FFFFFFFu) > 0x7F800000u) != 0;
+  }
+}
+
 // blockIdx.y = K range (a.splits of them; each writes its own fp32 slice of
 // out, [splits, M, N], for an ordered reduction afterwards). Blocks
 // [0, tail_tiles * 16/PMI) first run the row pieces of the last tail_tiles
@@ -859,7 +979,14 @@ __device__ __forceinline__ void tile_store3(const Gemm3Args &a, void *out, int64
 // block takes whole tiles t = blockIdx.x, + gridDim.x, ... below dp_tiles.
 // Power-of-two row and column scales commute exactly with the summation, so
 // partials carry them already.
-template <int BITS, bool OUT_BF16, int PMI, bool CANON, bool SPLIT>
+// ONLINE (FAST only): x16 holds the caller's bf16 x, converted to fp16 in
+// LDS by the kernel (no row scales). A tile with a row outside that
+// conversion's range is not stored: its first output element gets a NaN
+// mark and gemm3_fixup_kernel, launched next on the same grid, recomputes
+// it with SPLIT numerics. Other tiles have finite outputs (finite fp16
+// operands, |x| <= 2^15), so a NaN there means a marked tile, or a NaN
+// weight, whose SPLIT recomputation is NaN as well.
+template <int BITS, bool OUT_BF16, int PMI, bool CANON, bool SPLIT, bool ONLINE = false>
 __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char x0[kXStage];
   __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
@@ -872,7 +999,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
   // value per thread), written to LDS once the K loop has ended (its last
   // barrier also ends every wave's reads of the previous tile's scales)
   auto tile_rs = [&](int64_t m0, int rows) -> float {
-    if constexpr (SPLIT) return 1.f;
+    if constexpr (SPLIT || ONLINE) return 1.f;
     const int64_t m = m0 + threadIdx.x;
     return (int)threadIdx.x < rows && m < a.M ? a.rowscale[m] : 0.f;
   };
@@ -887,15 +1014,21 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
       tile_accumulate_split<BITS, MI, CANON>(a, xs, sbl, m0, n0, gb, ge, acc_);
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni) cs[ni] = 1.f;
+      return false;
     } else {
-      tile_accumulate3<BITS, MI, CANON>(a, xs, sbl, m0, n0, gb, ge, acc_, cs);
+      return tile_accumulate3<BITS, MI, CANON, ONLINE>(a, xs, sbl, m0, n0, gb, ge, acc_, cs);
     }
+  };
+  // ONLINE: a tile left to the fixup kernel (the flag is uniform per block)
+  auto store = [&](bool redo, auto &acc_, int64_t m0, int64_t n0, const float (&cs)[kNI]) {
+    constexpr int MI = sizeof(acc_) / sizeof(acc_[0]);
+    if (!redo) tile_store3<OUT_BF16, MI, !SPLIT>(a, out_of_split(a), m0, n0, acc_, rs_lds, cs);
+    else if (threadIdx.x == 0) mark_tile<OUT_BF16>(out_of_split(a), a.N, m0, n0);
   };
   const int tiles_n = (int)((a.N + kBN - 1) / kBN);
   const int split = blockIdx.y;
   const int gps = (a.G + a.splits - 1) / a.splits;
   const int gb = split * gps, ge = min(a.G, gb + gps);
-  void *out = a.splits > 1 ? static_cast<void *>(static_cast<float *>(a.out) + (int64_t)split * a.M * a.N) : a.out;
 
   if constexpr (PMI > 0) {
     constexpr int kPieces = 16 / PMI;
@@ -908,9 +1041,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
         f32x4 pacc[PMI][kNI];
         float cs[kNI];
         const float rs = tile_rs(m0, 16 * PMI);
-        accumulate(pacc, m0, n0, gb, ge, cs);
+        const bool redo = accumulate(pacc, m0, n0, gb, ge, cs);
         stage_rs(rs, 16 * PMI);
-        tile_store3<OUT_BF16, PMI, !SPLIT>(a, out, m0, n0, pacc, rs_lds, cs);
+        store(redo, pacc, m0, n0, cs);
       }
     }
   }
@@ -920,39 +1053,95 @@ __global__ __launch_bounds__(kNT, 1) void gemm3_kernel(Gemm3Args a) {
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
     float cs[kNI];
     const float rs = tile_rs(m0, kBM);
-    accumulate(acc, m0, n0, gb, ge, cs);
+    const bool redo = accumulate(acc, m0, n0, gb, ge, cs);
     stage_rs(rs, kBM);
-    tile_store3<OUT_BF16, kMI, !SPLIT>(a, out, m0, n0, acc, rs_lds, cs);
+    store(redo, acc, m0, n0, cs);
   }
 }
 
-template <int BITS, bool OUT_BF16, bool CANON, bool SPLIT>
+// The tiles of an ONLINE launch that gemm3_kernel left marked, recomputed
+// with SPLIT numerics: same grid, same tile and row-piece walk; every other
+// tile costs one load of its mark.
+template <int BITS, bool OUT_BF16, int PMI, bool CANON>
+__global__ __launch_bounds__(kNT, 1) void gemm3_fixup_kernel(Gemm3Args a) {
+  __shared__ __attribute__((aligned(16))) unsigned char x0[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char x1[kXStage];
+  __shared__ __attribute__((aligned(16))) unsigned char x2[kXStage];
+  __shared__ __attribute__((aligned(16))) uint32_t sbl[CANON ? kSbBufs * kSbBufWords : 4];
+  unsigned char *const xs[kStages] = {x0, x1, x2};
+  const int tiles_n = (int)((a.N + kBN - 1) / kBN);
+  const int split = blockIdx.y;
+  const int gps = (a.G + a.splits - 1) / a.splits;
+  const int gb = split * gps, ge = min(a.G, gb + gps);
+  void *out = out_of_split(a);
+  const float one[kNI] = {1.f, 1.f};
+  if constexpr (PMI > 0) {
+    constexpr int kPieces = 16 / PMI;
+    if ((int)blockIdx.x < a.tail_tiles * kPieces) {
+      const int tail = blockIdx.x % a.tail_tiles, piece = blockIdx.x / a.tail_tiles;
+      const int tile = a.dp_tiles + tail;
+      const int64_t m0 = (int64_t)(tile / tiles_n) * kBM + piece * 16 * PMI;
+      const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
+      if (m0 < a.M && tile_marked<OUT_BF16>(out, a.N, m0, n0)) {
+        f32x4 pacc[PMI][kNI];
+        tile_accumulate_split<BITS, PMI, CANON>(a, xs, sbl, m0, n0, gb, ge, pacc);
+        tile_store3<OUT_BF16, PMI, false>(a, out, m0, n0, pacc, nullptr, one);
+      }
+    }
+  }
+  for (int t = blockIdx.x; t < a.dp_tiles; t += gridDim.x) {
+    const int tile = xcd_remap(t, a.dp_tiles);
+    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM, n0 = (int64_t)(tile % tiles_n) * kBN;
+    if (!tile_marked<OUT_BF16>(out, a.N, m0, n0)) continue;
+    f32x4 acc[kMI][kNI];
+    tile_accumulate_split<BITS, kMI, CANON>(a, xs, sbl, m0, n0, gb, ge, acc);
+    tile_store3<OUT_BF16, kMI, false>(a, out, m0, n0, acc, nullptr, one);
+  }
+}
+
+template <int BITS, bool OUT_BF16, bool CANON, bool SPLIT, bool ONLINE>
 void launch3_out(const Gemm3Args &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.grid_x, (unsigned)a.splits);
   switch (a.tail_tiles > 0 ? a.tail_mi : 0) {
-    case 2: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 2, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 4, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 8, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
-    default: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 0, CANON, SPLIT>), grid, dim3(kNT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 2, CANON, SPLIT, ONLINE>), grid, dim3(kNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 4, CANON, SPLIT, ONLINE>), grid, dim3(kNT), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 8, CANON, SPLIT, ONLINE>), grid, dim3(kNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm3_kernel<BITS, OUT_BF16, 0, CANON, SPLIT, ONLINE>), grid, dim3(kNT), 0, stream, a); break;
   }
 }
 
-template <int BITS, bool CANON, bool SPLIT>
-void launch3_layout(const Gemm3Args &a, hipStream_t stream) {
-  if (a.out_bf16 && a.splits == 1) launch3_out<BITS, true, CANON, SPLIT>(a, stream);
-  else launch3_out<BITS, false, CANON, SPLIT>(a, stream);
+template <int BITS, bool OUT_BF16, bool CANON>
+void launch3_fixup_out(const Gemm3Args &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.grid_x, (unsigned)a.splits);
+  switch (a.tail_tiles > 0 ? a.tail_mi : 0) {
+    case 2: hipLaunchKernelGGL((gemm3_fixup_kernel<BITS, OUT_BF16, 2, CANON>), grid, dim3(kNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemm3_fixup_kernel<BITS, OUT_BF16, 4, CANON>), grid, dim3(kNT), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemm3_fixup_kernel<BITS, OUT_BF16, 8, CANON>), grid, dim3(kNT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm3_fixup_kernel<BITS, OUT_BF16, 0, CANON>), grid, dim3(kNT), 0, stream, a); break;
+  }
 }
 
-template <int BITS, bool SPLIT>
+template <int BITS, bool CANON, bool SPLIT, bool ONLINE>
+void launch3_layout(const Gemm3Args &a, hipStream_t stream) {
+  const bool bf = a.out_bf16 && a.splits == 1;
+  if (bf) launch3_out<BITS, true, CANON, SPLIT, ONLINE>(a, stream);
+  else launch3_out<BITS, false, CANON, SPLIT, ONLINE>(a, stream);
+  if constexpr (ONLINE) {
+    if (bf) launch3_fixup_out<BITS, true, CANON>(a, stream);
+    else launch3_fixup_out<BITS, false, CANON>(a, stream);
+  }
+}
+
+template <int BITS, bool SPLIT, bool ONLINE = false>
 hipError_t launch3_bits(const Gemm3Args &a, hipStream_t stream) {
   if (a.tail_tiles > 0 && a.tail_mi != 2 && a.tail_mi != 4 && a.tail_mi != 8) return hipErrorInvalidValue;
   if (a.splits < 1 || (a.splits > 1 && a.tail_tiles > 0)) return hipErrorInvalidValue;
   if constexpr (BITS == 3) {
     if (a.canon) return hipErrorInvalidValue;  // 3-bit codes run on tiled weights only
-    launch3_layout<BITS, false, SPLIT>(a, stream);
+    launch3_layout<BITS, false, SPLIT, ONLINE>(a, stream);
   } else {
-    if (a.canon) launch3_layout<BITS, true, SPLIT>(a, stream);
-    else launch3_layout<BITS, false, SPLIT>(a, stream);
+    if (a.canon) launch3_layout<BITS, true, SPLIT, ONLINE>(a, stream);
+    else launch3_layout<BITS, false, SPLIT, ONLINE>(a, stream);
   }
   return hipGetLastError();
 }

@@ -116,6 +116,7 @@ struct Plan {
   int groups_per_split = 0;
   size_t ws_xsum = 0, ws_partial = 0;
   size_t ws_x16 = 0;  // fast mode: fp16 x and per-row scales
+  bool online = false;  // fast mode without them: the GEMM converts x itself
   bool copy = false;  // canonical 3-bit codes: the GEMM runs on a tiled copy in the workspace
   ql::Gemm2Plan g2{};
   ql::Gemm3Plan g3{};
@@ -126,6 +127,7 @@ struct Plan {
 // x16, xsum: the caller's FAST activations / EXACT group sums.
 struct Caller {
   bool scratch = false, x16 = false, xsum = false;
+  bool epilogue = false;  // a fused epilogue (its FAST GEMM takes prepared fp16 activations)
 };
 
 size_t ti_sizes(int tile) {
@@ -183,12 +185,12 @@ size_t repack_ws_bytes(int bits, int64_t N, int64_t K) {
   return (size_t)round_up(n32 * K * bits / 32 * 4, 256) + (size_t)round_up(n32 * (K / kGroup) * 4, 256);
 }
 
-// Plans a forward call. Automatic numerics for the large-M path: FAST when
-// the call may use scratch (or brings its fp16 activations), SPLIT otherwise:
-// SPLIT needs no scratch unless K is split, and K is split only with a
-// workspace; a grid of fewer tiles than CUs that is not split along K is cut
-// into row pieces instead. Canonical 3-bit codes run every GEMM on a tiled copy in the
-// workspace.
+// Plans a forward call. Automatic numerics for the large-M path: FAST, with
+// its activations from the caller, from a prepass into the workspace, or
+// (no workspace) converted inside the GEMM, which needs no scratch; K is
+// split only with a workspace, and a grid of fewer tiles than CUs that is not
+// split along K is cut into row pieces instead. Canonical 3-bit codes run
+// every GEMM on a tiled copy in the workspace.
 int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int force_split,
               int force_tile, bool tiled, int mode, Caller c, Plan *p) {
   *p = Plan{};  // a re-plan into the same Plan keeps no field of the previous one
@@ -214,7 +216,7 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
   if (mode == QL_MODE_AUTO) {
     if (forced) mode = forced->gen == 3 ? QL_MODE_FAST : forced->gen == 4 ? QL_MODE_SPLIT : QL_MODE_EXACT;
     else if (canon_big) mode = QL_MODE_EXACT;
-    else mode = (c.scratch || c.x16) ? QL_MODE_FAST : QL_MODE_SPLIT;
+    else mode = QL_MODE_FAST;  // with no workspace and no fp16 activations the GEMM converts x itself
   }
   if (mode != QL_MODE_EXACT && mode != QL_MODE_FAST && mode != QL_MODE_SPLIT) return QL_EINVAL;
   p->mode = mode;
@@ -238,7 +240,12 @@ int make_plan(int bits, int64_t M, int64_t N, int64_t K, int force_path, int for
     p->tile = gen == 3 ? kFastTile : kSplitTile;
     p->splits = p->g3.splits;
     p->groups_per_split = G > 0 ? (G + p->splits - 1) / p->splits : 0;
-    if (mode == QL_MODE_FAST && !c.x16) p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
+    // FAST activations: the caller's, else a prepass into the workspace, else
+    // (no workspace) converted inside the GEMM
+    if (mode == QL_MODE_FAST && !c.x16) {
+      if (c.scratch || c.epilogue) p->ws_x16 = (size_t)round_up(M * K * 2, 256) + (size_t)round_up(M * 4, 256);
+      else p->online = true;
+    }
     p->ws_partial = p->g3.partial_bytes;
     return QL_OK;
   }
@@ -441,6 +448,7 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   c.scratch = a->workspace != nullptr;
   c.x16 = a->x16 != nullptr;
   c.xsum = a->xsum != nullptr;
+  c.epilogue = glu || gated;
   const bool tiled_in = a->layout == QL_LAYOUT_TILED;
   // the fused epilogues run on the FAST GEMM without a K split (they need
   // finished sums), at any M
@@ -500,10 +508,13 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
   const char *lay = canon ? "canonical" : (copy ? "tiled_copy" : "tiled");
   if (p.mode == QL_MODE_FAST || p.mode == QL_MODE_SPLIT) {
     const bool fast = p.mode == QL_MODE_FAST;
-    const uint16_t *x16 = static_cast<const uint16_t *>(fast ? a->x16 : a->x);
-    const float *rowscale = fast ? a->rowscale : nullptr;
+    // the GEMM reads x16: the caller's fp16 activations, the prepass output
+    // below, or the bf16 x itself (SPLIT, and FAST converting in the GEMM)
+    const uint16_t *x16 = static_cast<const uint16_t *>(fast && !p.online ? a->x16 : a->x);
+    const float *rowscale = fast && !p.online ? a->rowscale : nullptr;
     char *after = static_cast<char *>(ws) + round_up((int64_t)p.ws_x16, 256);
-    if (fast && !x16) {
+    if (fast && !p.online && !x16) {
+      if (!ws) return QL_EWORKSPACE;  // the plan asked for it: checked above, kept as a guard
       uint16_t *x16w = static_cast<uint16_t *>(ws);
       float *rsw = reinterpret_cast<float *>(static_cast<char *>(ws) + round_up(a->M * a->K * 2, 256));
       if (ql::launch_x16(static_cast<const uint16_t *>(a->x), x16w, rsw, a->M, a->K, stream) != hipSuccess)
@@ -521,7 +532,7 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
                      gated ? (int)std::min<int64_t>(a->gate_rows, a->M) : 0,
                      canon ? 1 : 0, canon ? static_cast<const uint16_t *>(a->scales) : nullptr,
                      canon ? static_cast<const uint16_t *>(a->biases) : nullptr};
-    const char *kname = fast ? "gemm3_f16" : "gemm4_bf16x2";
+    const char *kname = p.online ? "gemm3_f16online" : fast ? "gemm3_f16" : "gemm4_bf16x2";
     if (gated)
       std::snprintf(buf, sizeof(buf), "%s_256x256_b%d%s_gate_%s", kname, a->bits, p.g3.tail_tiles > 0 ? "_tail" : "",
                     lay);
@@ -536,7 +547,9 @@ QL_API int qlinear_forward_ex(const ql_forward_args *a, void *stream_v) {
     else
       std::snprintf(buf, sizeof(buf), "%s_256x256_b%d_%s", kname, a->bits, lay);
     set_last_path(buf);
-    const hipError_t le = fast ? ql::launch_gemm3(a->bits, g3, stream) : ql::launch_gemm4(a->bits, g3, stream);
+    const hipError_t le = p.online ? ql::launch_gemm3_online(a->bits, g3, stream)
+                          : fast     ? ql::launch_gemm3(a->bits, g3, stream)
+                                     : ql::launch_gemm4(a->bits, g3, stream);
     if (le != hipSuccess) return QL_EHIP;
     if (split && ql::launch_splitk_reduce(partial, p.g3.splits, a->M, a->N, a->out, out_bf16, stream) != hipSuccess)
       return QL_EHIP;

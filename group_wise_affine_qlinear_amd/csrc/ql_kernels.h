@@ -98,6 +98,11 @@ hipError_t launch_gemm3(int bits, const Gemm3Args &a, hipStream_t stream);
 // SPLIT numerics (gemm4.hip): same arguments, x16 holds the caller's bf16 x,
 // rowscale is unused, glu and gate must be off.
 hipError_t launch_gemm4(int bits, const Gemm3Args &a, hipStream_t stream);
+// FAST numerics without a prepass (gemm3o.hip): x16 holds the caller's bf16
+// x, converted to fp16 inside the GEMM; rowscale is unused, glu and gate must
+// be off. Two launches: the GEMM, then the recomputation (SPLIT numerics) of
+// any tile with a row outside the in-kernel conversion's range.
+hipError_t launch_gemm3_online(int bits, const Gemm3Args &a, hipStream_t stream);
 
 hipError_t launch_splitk_reduce(const float *partial, int splits, int64_t M, int64_t N,
                                 void *out, int out_bf16, hipStream_t stream);

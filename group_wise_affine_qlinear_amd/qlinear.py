@@ -203,8 +203,8 @@ def qlinear_forward_ex(x, packed_q, scales, biases, bits, M, N, K, out, *, group
 
     With ``layout=QL_LAYOUT_TILED``, ``packed_q`` and ``scales`` are the outputs of
     ``qlinear_repack`` (tiled codes, tiled scale|bias words) and ``biases`` is ignored.
-    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path on tiled weights when a
-    workspace is passed, SPLIT otherwise). ``workspace`` is a device tensor the library may use
+    ``mode`` is a ``ql_mode`` (AUTO: FAST for the large-M path; with no workspace and no
+    ``x16`` the GEMM converts x to fp16 itself). ``workspace`` is a device tensor the library may use
     as scratch, ``None`` (the call keeps to plans that need none, as the C call with a NULL
     workspace), or by default a tensor of ``qlinear_workspace_bytes`` bytes that torch's caching
     allocator provides on the call's stream (the library itself never allocates);

@@ -107,13 +107,20 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  *   bias are served (such a column's weights are then exact to one rounding
  *   relative to its largest magnitude). Runs on either layout (canonical
  *   2/4/8-bit codes of fewer than 2^31 code bytes; slower than tiled: strided
- *   code loads). Uses M*K*2 + M*4 workspace bytes for the fp16 x unless the
- *   caller passes it (qlinear_fast_activations, x16/rowscale).
+ *   code loads). The fp16 x comes from the caller (qlinear_fast_activations,
+ *   x16/rowscale), else from a prepass into M*K*2 + M*4 workspace bytes, else
+ *   (no workspace, no fused epilogue) from the GEMM itself: each block
+ *   converts the bf16 x it stages in LDS to fp16 by truncation, with no row
+ *   scale (exact for 2^-17 <= |x| <= 2^15; below 2^-17 the error is under
+ *   2^-24 per value), and every block tile or row piece holding a row whose
+ *   largest magnitude is above 2^15 (or not finite), or nonzero and below
+ *   2^-6, is recomputed by a second launch with SPLIT numerics. Outputs of
+ *   this form equal the prepass form's bit for bit wherever every nonzero
+ *   |x| is at least 2^-17 and no tile is recomputed.
  * A K split (few output tiles, long K) adds splits*M*N*4 bytes of fp32
  *   partials to any mode's workspace.
- * AUTO: FAST when the call has a workspace (or its own fp16 activations),
- *   SPLIT otherwise (EXACT for canonical codes of 2^31 bytes or more). The
- *   skinny (M <= 16) path is always EXACT and needs no workspace. Without a
+ * AUTO: FAST (EXACT for canonical codes of 2^31 bytes or more). The skinny
+ *   (M <= 16) path is always EXACT and needs no workspace. Without a
  *   workspace K is never split. A grid of fewer 256 x 256 tiles than CUs that
  *   is not split along K is cut into row pieces of 128, 64 or 32 rows instead
  *   (long-K, few-row shapes run slower than with a workspace's K split).
@@ -203,8 +210,9 @@ typedef struct ql_forward_args {
  * group, M, N, K, out) on canonical weights.
  * M, N >= 0 (0 is a no-op), K >= 0 and a multiple of 64 (K == 0 writes zeros),
  * group must be 64. The call allocates no memory and uses no scratch: M <= 16
- * runs the skinny kernel, larger M the SPLIT GEMM without a K split (see
- * ql_mode; few-tile shapes run as row pieces). The library holds no buffers or other state between calls, so
+ * runs the skinny kernel (or the GEMV), larger M the FAST GEMM converting x
+ * itself, without a K split (see ql_mode; few-tile shapes run as row
+ * pieces). The library holds no buffers or other state between calls, so
  * concurrent calls on different streams are independent. The one case that
  * needs scratch, canonical 3-bit codes with M > 16 (tiled copy, see
  * ql_layout), returns QL_EWORKSPACE: use qlinear_forward_ex with a workspace,
@@ -219,10 +227,10 @@ int qlinear_forward(const void *x, const uint32_t *packed_q, const void *scales,
  * args->workspace, which the caller owns and sizes with
  * qlinear_workspace_bytes; the library never allocates device memory and
  * never synchronizes. With a NULL workspace automatic selection keeps to
- * plans that need none (no K split, SPLIT numerics on the large-M path
- * unless FAST activations are passed); a request that still needs scratch
- * (EXACT without xsum, FAST or an epilogue without x16, a forced K split,
- * canonical 3-bit GEMMs) returns QL_EWORKSPACE before anything is launched.
+ * plans that need none (no K split; FAST converts x inside the GEMM unless
+ * FAST activations are passed); a request that still needs scratch (EXACT
+ * without xsum, an epilogue without x16, a forced K split, canonical 3-bit
+ * GEMMs) returns QL_EWORKSPACE before anything is launched.
  * Calls that share one workspace must not overlap in time. */
 int qlinear_forward_ex(const ql_forward_args *args, void *stream);
 

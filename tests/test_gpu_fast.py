@@ -63,11 +63,11 @@ def test_fast_is_auto_choice_with_a_workspace(torch):
     assert ql.qlinear_last_path().startswith("gemm3")
     run_forward(torch, c)
     assert ql.qlinear_last_path().startswith("gemm3") and ql.qlinear_last_path().endswith("_canonical")
-    # no workspace and no fp16 activations: the scratch-free SPLIT GEMM
+    # no workspace and no fp16 activations: FAST converting x inside the GEMM
     x, p, s, b = c.device(torch)
     out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
     ql.qlinear_forward_ex(x, p, s, b, 4, c.M, c.N, c.K, out, workspace=None)
-    assert ql.qlinear_last_path().startswith("gemm4_bf16x2"), ql.qlinear_last_path()
+    assert ql.qlinear_last_path().startswith("gemm3_f16online"), ql.qlinear_last_path()
     run_forward(torch, c, layout=ql.QL_LAYOUT_TILED, mode=ql.QL_MODE_EXACT)
     assert ql.qlinear_last_path().startswith("gemm2")
     c8 = Case(8, 256, 256, 4, wid=411)   # skinny M is always exact

@@ -2,9 +2,11 @@
 
 Every workload of ``inputs.WORKLOADS`` runs at its full shape through the
 launches the benchmark times and the spec call:
-  * ``qlinear_forward`` on canonical weights, no workspace (SPLIT GEMM for
-    M > 16, the skinny kernel below): against the oracle at the design bound
-    of the exact modes;
+  * ``qlinear_forward`` on canonical weights, no workspace (for M > 16 the
+    FAST GEMM converting x itself, against the oracle at the acceptance bar
+    row by row and within the FAST budget; below, the skinny kernel or the
+    GEMV at the design bound of the exact modes);
+  * SPLIT numerics on canonical weights, no workspace, at the design bound;
   * the tiled layout under automatic dispatch with a workspace (FAST GEMM for
     M > 16, the skinny kernel below): against the oracle at the acceptance
     bar, on the whole output and row by row, and within the FAST budget;
@@ -70,10 +72,21 @@ def test_full_size_full_output(torch, name, bits):
     ql.qlinear_forward(xd, pd, sd, bd, bits, 64, M, N, K, out)
     torch.cuda.synchronize()
     path = ql.qlinear_last_path()
-    assert path.startswith(("skinny", "gemv") if M <= 16 else "gemm4_bf16x2"), path
+    assert path.startswith(("skinny", "gemv") if M <= 16 else "gemm3_f16online"), path
     y = host(out)
-    check(y, ref, RELF_DESIGN, MAXABS_RMS_DESIGN, ("qlinear_forward", path))
+    if M > 16:
+        check(y, ref, RELF_FAST, MAXABS_RMS_FAST, ("qlinear_forward, FAST budget", path))
+    else:
+        check(y, ref, RELF_DESIGN, MAXABS_RMS_DESIGN, ("qlinear_forward", path))
     assert_rows(y, ref, what=("qlinear_forward rows", path))
+    if M > 16:
+        # SPLIT numerics, no workspace: the exact-mode bound
+        out.fill_(float("nan"))
+        ql.qlinear_forward_ex(xd, pd, sd, bd, bits, M, N, K, out, mode=ql.QL_MODE_SPLIT, workspace=None)
+        torch.cuda.synchronize()
+        path = ql.qlinear_last_path()
+        assert path.startswith("gemm4_bf16x2"), path
+        check(host(out), ref, RELF_DESIGN, MAXABS_RMS_DESIGN, ("split, no workspace", path))
 
     # tiled layout, automatic dispatch with a workspace
     tq, tsb = ql.qlinear_repack(pd, sd, bd, bits, 64, N, K)

@@ -48,6 +48,7 @@ def test_graph_replays_match_eager(torch):
     y_skinny = torch.empty((8, N), dtype=torch.float32, device="cuda")
     y_canon = torch.empty((M, N), dtype=torch.float32, device="cuda")
     y_split = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    y_online = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
     def sequence():
         ql.qlinear_fast_activations(x, M, K, x16, rs)
@@ -63,11 +64,13 @@ def test_graph_replays_match_eager(torch):
         ql.qlinear_forward_ex(xs, p, s, b, bits, 8, N, K, y_skinny, workspace=ws[2])
         # canonical weights with a workspace: fp16 prepass into it, FAST GEMM on the code rows
         ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_canon, workspace=ws[0])
-        # the spec call's plan (no workspace: SPLIT GEMM) on the capture
-        # stream; qlinear_forward itself launches on the default stream
-        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_split, workspace=None)
+        # the spec call's plan (no workspace: FAST converting x in the
+        # GEMM, then the recomputation launch) on the capture stream;
+        # qlinear_forward itself launches on the default stream
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_online, workspace=None)
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, y_split, mode=ql.QL_MODE_SPLIT, workspace=None)
 
-    outs = (y_fast, y_glu, y_res, y_exact, y_skinny, y_canon, y_split)
+    outs = (y_fast, y_glu, y_res, y_exact, y_skinny, y_canon, y_online, y_split)
     y_res.copy_(res0)
     sequence()
     torch.cuda.synchronize()

@@ -95,8 +95,8 @@ def test_tiny_config_all_paths(torch):
     w, x = inputs.workload_inputs("tiny")
     c = Case(wl["M"], wl["N"], wl["K"], 4, wid=wl["id"], w=w, x=x)
     ref = c.reference()
-    y = run_forward(torch, c, via_ex=False)
-    assert_parity(y.cpu().numpy(), ref, what="qlinear_forward")
+    y = run_forward(torch, c, via_ex=False)   # FAST converting x in the GEMM: the acceptance bar
+    assert_rows(y.cpu().numpy(), ref, what="qlinear_forward")
     for mode in EXACT_MODES:
         for path in (ql.QL_PATH_GEMM, ql.QL_PATH_SPLITK):
             y = run_forward(torch, c, path=path, mode=mode)

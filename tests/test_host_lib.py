@@ -199,7 +199,6 @@ def _args(**kw):
     (dict(M=64, N=64, K=128, mode=1, workspace=0x7000, workspace_bytes=16), ql.QL_EWORKSPACE),
     # no workspace: plans that need scratch are refused before any launch
     (dict(M=64, N=64, K=128, mode=1), ql.QL_EWORKSPACE),          # EXACT: group sums of x
-    (dict(M=64, N=64, K=128, mode=2), ql.QL_EWORKSPACE),          # FAST: fp16 activations
     (dict(M=64, N=64, K=128, mode=3, path=3), ql.QL_EWORKSPACE),  # forced K split: partials
     (dict(M=64, N=64, K=128, bits=3), ql.QL_EWORKSPACE),          # canonical 3-bit: tiled copy
     (dict(M=64, N=64, K=128, epilogue=2, residual=0x6000, gate=0x6800, gate_rows=1), ql.QL_EWORKSPACE),
@@ -327,6 +326,24 @@ def test_north_star_call_needs_no_scratch(lib, shape):
         for layout in (ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED):
             st = _forward_status_nows(lib, M, N, K, bits, ql.QL_MODE_AUTO, layout)
             assert st != ql.QL_EWORKSPACE or (bits == 3 and M > 16 and layout == ql.QL_LAYOUT_CANONICAL)
+
+
+@pytest.mark.skipif(_gpu_present(), reason="passes placeholder device addresses: runs only where no GPU is visible")
+@pytest.mark.parametrize("layout", [ql.QL_LAYOUT_CANONICAL, ql.QL_LAYOUT_TILED])
+def test_fast_without_workspace_converts_in_the_gemm(lib, layout):
+    """FAST with neither a workspace nor the caller's fp16 activations plans
+    the GEMM that converts x itself: nothing is launched before it (no
+    prepass into a missing workspace), so the path is set and the GEMM's own
+    launch is what fails here. With a fused epilogue the prepass is needed
+    and the call is refused up front."""
+    for bits in (2, 4, 8) if layout == ql.QL_LAYOUT_CANONICAL else (2, 3, 4, 8):
+        st = _forward_status_nows(lib, 4096, 4608, 4608, bits, ql.QL_MODE_FAST, layout)
+        assert st == ql.QL_EHIP, (bits, st)
+        path = ql.qlinear_last_path()
+        assert path.startswith("gemm3_f16online_") and path.endswith(
+            "canonical" if layout == ql.QL_LAYOUT_CANONICAL else "tiled"), path
+    a = _args(M=64, N=64, K=128, mode=ql.QL_MODE_FAST, epilogue=2, residual=0x6000, gate=0x6800, gate_rows=1)
+    assert lib.qlinear_forward_ex(ctypes.byref(a), None) == ql.QL_EWORKSPACE
 
 
 def _forward_status_nows(lib, M, N, K, bits, mode, layout):
