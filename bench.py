@@ -107,10 +107,19 @@ def smi_snapshot():
         return None
 
 
-def time_calls(torch, fn, iters, warmup):
-    """Average per-call time (ms) with HIP events on the current stream."""
+def time_calls(torch, fn, iters, warmup, settle_s=0.0):
+    """Average per-call time (ms) with HIP events on the current stream, after
+    `warmup` calls and then calls for at least `settle_s` seconds while the
+    engine clock settles under the load."""
     for _ in range(warmup):
         fn()
+    if settle_s > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -255,10 +264,13 @@ CASES = {
 }
 
 
+CASE_SETTLE_S = 0.2   # calls per case before its timed calls, while the clock settles
+
+
 def run_case(torch, ql, inputs, name, iters=20, warmup=5):
     builder, kw, note = CASES[name]
     call, meta = builder(torch, ql, inputs, **kw)
-    ms = time_calls(torch, call, iters, warmup)
+    ms = time_calls(torch, call, iters, warmup, CASE_SETTLE_S)
     row = {"path": ql.qlinear_last_path(), "us": round(ms * 1e3, 2)}
     if "flop" in meta:
         tf = meta["flop"] / (ms * 1e-3) / 1e12
@@ -282,7 +294,8 @@ def fused_epilogue_rows(torch, ql, inputs, rows):
     ws = _ws(torch, ql, 4, M, N, K)
     yg = torch.empty((M, N // 2), dtype=torch.bfloat16, device="cuda")
     ms = time_calls(torch, lambda: ql.qlinear_forward_ex(
-        x, tq, tsb, None, 4, M, N, K, yg, layout=ql.QL_LAYOUT_TILED, epilogue=ql.QL_EPI_SWIGLU, workspace=ws), 10, 3)
+        x, tq, tsb, None, 4, M, N, K, yg, layout=ql.QL_LAYOUT_TILED, epilogue=ql.QL_EPI_SWIGLU, workspace=ws), 10, 3,
+        CASE_SETTLE_S)
     tf = 2 * M * N * K / (ms * 1e-3) / 1e12
     rows["mlp_gateup_M4608_K4608_N24576_q4_swiglu_fused"] = {
         "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
@@ -309,8 +322,8 @@ def fused_epilogue_rows(torch, ql, inputs, rows):
         ql.qlinear_forward_ex(x, tq, tsb, None, 4, M, N, K, res, layout=ql.QL_LAYOUT_TILED, workspace=ws,
                               epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=gate, gate_rows=L)
 
-    ms_unf = time_calls(torch, unfused, 20, 5)
-    ms_fused = time_calls(torch, fused, 20, 5)
+    ms_unf = time_calls(torch, unfused, 20, 5, CASE_SETTLE_S)
+    ms_fused = time_calls(torch, fused, 20, 5, CASE_SETTLE_S)
     flop = 2 * M * N * K
     rows["attn_out_M4608_K4608_N4608_q4_gate_unfused"] = {
         "path": "prepass + FAST GEMM + torch addcmul_ on the residual", "us": round(ms_unf * 1e3, 1),
@@ -344,7 +357,7 @@ def sweep_rows(torch, ql, inputs, rows):
             tq, tsb = sets[0]
             ms = time_calls(torch, lambda: ql.qlinear_forward_ex(
                 x, tq, tsb, None, bits, M, N, K, out, layout=ql.QL_LAYOUT_TILED, x16=x16, rowscale=rs,
-                workspace=ws), 10, 3)
+                workspace=ws), 10, 3, CASE_SETTLE_S)
             tf = 2 * M * N * K / (ms * 1e-3) / 1e12
             rows[f"sweep_2048_M{M}_K{K}_N{N}_q{bits}"] = {
                 "path": ql.qlinear_last_path(), "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
@@ -419,7 +432,7 @@ def dit_block_rows(torch, ql, inputs, rows):
             proj("mlp_gate_up", x, hmid, epilogue=ql.QL_EPI_SWIGLU)
             proj("mlp_down", hmid, res, epilogue=ql.QL_EPI_GATE_RESIDUAL, residual=res, gate=g_mlp, gate_rows=M)
 
-        ms = time_calls(torch, block, 10, 3)
+        ms = time_calls(torch, block, 10, 3, CASE_SETTLE_S)
         blk = qplan.block_projections(policy)
         flops = sum(2 * (1 if p.role == "adaln_modulation" else M) * p.N * p.K for p in blk)
         tf = flops / (ms * 1e-3) / 1e12
@@ -431,6 +444,24 @@ def dit_block_rows(torch, ql, inputs, rows):
         log(f"DiT block {policy}: {ms*1e3:.1f} us")
         del wts
     del wf, x, att, temb, res, gates, qkv, hmid, mod, ws
+
+
+def dense_library_rows(torch, rows):
+    # context, not this library's path: the vendor's dense GEMM (torch.matmul,
+    # hipBLASLt) on unquantized fp16 and bf16 operands of the same shapes,
+    # y = x @ W^T with fp32 accumulation; it reads 16-bit weights (4x the
+    # 4-bit codes' bytes) and dequantizes nothing
+    for (M, N, K) in ((4096, 4608, 4608), (4608, 13824, 4608)):
+        for name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+            x = torch.randn(M, K, device="cuda", dtype=dt)
+            wt = torch.randn(N, K, device="cuda", dtype=dt).t()
+            ms = time_calls(torch, lambda: x @ wt, 20, 5, CASE_SETTLE_S)
+            tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+            rows[f"context_dense_library_{name}_M{M}_K{K}_N{N}"] = {
+                "us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4),
+                "note": f"context only: torch.matmul (hipBLASLt) on dense {name} operands, not the quantized path"}
+            log(f"dense library {name} {M}x{K}->{N}: {ms*1e3:.1f} us ({100*tf/PEAK_F16_TFLOPS:.1f}%)")
+            del x, wt
 
 
 def secondary_rows(torch, ql, inputs):
@@ -447,6 +478,8 @@ def secondary_rows(torch, ql, inputs):
     dit_block_rows(torch, ql, inputs, rows)
     torch.cuda.empty_cache()
     sweep_rows(torch, ql, inputs, rows)
+    torch.cuda.empty_cache()
+    dense_library_rows(torch, rows)
     torch.cuda.empty_cache()
     return rows
 
