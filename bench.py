@@ -549,6 +549,51 @@ def load_traffic(src_hash):
     return rec.get("traffic_bytes_per_launch")
 
 
+# EXACT-mode GEMM tiles (gemm.hip / gemm2.hip ids) and the shapes the
+# automatic table is chosen on: (label, M, N, K, bits, weight id)
+SWEEP_TILES = (1, 2, 3, 5, 10, 11)
+SWEEP_SHAPES = (
+    ("square_M256_K4608_N4608_q4", 256, 4608, 4608, 4, 6),
+    ("square_M4096_K4608_N4608_q4", 4096, 4608, 4608, 4, 6),
+    ("qkv_M4608_K4608_N13824_q4", 4608, 13824, 4608, 4, 2),
+    ("mlp_gateup_M4608_K4608_N24576_q8", 4608, 24576, 4608, 8, 3),
+    ("mlp_down_M4608_K12288_N4608_q8", 4608, 4608, 12288, 8, 30),
+    ("mlp_down_M4608_K12288_N4608_q4", 4608, 4608, 12288, 4, 30),
+    ("llm_cond_proj_M512_K53248_N4608_q4", 512, 4608, 53248, 4, 4),
+    ("sweep_2048_M16896_K4608_N13824_q2", 16896, 13824, 4608, 2, 50),
+)
+
+
+def sweep_tiles(torch, ql, inputs):
+    """Every EXACT tile on every sweep shape (canonical weights, a workspace,
+    the automatic K split), 10 timed calls after 0.1 s of settling; one JSON
+    line per shape with the times and the fastest tile, which is what the
+    library's EXACT tile table encodes."""
+    for label, M, N, K, bits, wid in SWEEP_SHAPES:
+        (p, s, b), = make_weights(torch, ql, inputs, N, K, bits, wid)
+        x = torch.from_numpy(inputs.activations_bf16(M, K, wid).view("int16")).cuda()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = _ws(torch, ql, bits, M, N, K)
+        times = {}
+        ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=ql.QL_LAYOUT_CANONICAL, workspace=ws,
+                              mode=ql.QL_MODE_EXACT)
+        auto_path = ql.qlinear_last_path()
+        for tile in SWEEP_TILES:
+            def call(tile=tile):
+                ql.qlinear_forward_ex(x, p, s, b, bits, M, N, K, out, layout=ql.QL_LAYOUT_CANONICAL,
+                                      workspace=ws, mode=ql.QL_MODE_EXACT, tile=tile)
+            try:
+                call()
+            except RuntimeError:
+                continue   # the tile cannot serve this shape or width
+            times[tile] = round(time_calls(torch, call, 10, 2, 0.1) * 1e3, 1)
+        best = min(times, key=times.get)
+        print(json.dumps({"sweep": label, "us_by_tile": times, "fastest_tile": best, "auto_path": auto_path}),
+              flush=True)
+        del p, s, b, x, out, ws
+        torch.cuda.empty_cache()
+
+
 PROFILE_CHOICES = ["none", "step", "copy"] + sorted(CASES)
 
 
@@ -563,6 +608,8 @@ def main():
                     help="short run for rocprofv3: 'step' = the timed step only, 'copy' = a plain copy of known "
                          "size, a secondary case name = that case's launches only")
     ap.add_argument("--profile-calls", type=int, default=40)
+    ap.add_argument("--sweep-tiles", action="store_true",
+                    help="time every EXACT-mode tile on the configured shapes (one JSON line per shape) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -580,6 +627,9 @@ def main():
         sys.exit(1)
     ql.load_library()
 
+    if args.sweep_tiles:
+        sweep_tiles(torch, ql, inputs)
+        return
     if args.profile == "copy":
         n = 256 * 1024 * 1024 // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
