@@ -157,10 +157,15 @@ Gemm3Plan gemm3_plan(int64_t M, int64_t N, int G, int slots, int force_splits, b
     return p;
   }
   if (p.tiles < slots && fill_by_pieces && M > 32) {
-    // every tile in row pieces: the fewest pieces per tile (2, 4 or 8) that
-    // give at least one block per slot
-    int pieces = 2;
-    while (pieces < 8 && p.tiles * pieces < slots) pieces *= 2;
+    // every tile in row pieces, all in one round of blocks: the most pieces
+    // per tile (8, 4 or 2) that need no more blocks than slots, whole tiles
+    // when even halves would not fit. A piece dequantizes its tile's whole
+    // width, so its time grows much less than its rows: two rounds of small
+    // pieces take longer than one of larger ones (36 tiles as 288 pieces of
+    // 32 rows on 256 slots gave 32 slots two pieces each)
+    int pieces = 8;
+    while (pieces >= 2 && p.tiles * pieces > slots) pieces /= 2;
+    if (pieces < 2) return p;
     p.dp_tiles = 0;
     p.tail_tiles = (int)p.tiles;
     p.tail_mi = 16 / pieces;
