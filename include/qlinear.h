@@ -122,8 +122,10 @@ typedef enum { QL_LAYOUT_CANONICAL = 0, QL_LAYOUT_TILED = 1 } ql_layout;
  * AUTO: FAST (EXACT for canonical codes of 2^31 bytes or more). The skinny
  *   (M <= 16) path is always EXACT and needs no workspace. Without a
  *   workspace K is never split. A grid of fewer 256 x 256 tiles than CUs that
- *   is not split along K is cut into row pieces of 128, 64 or 32 rows instead
- *   (long-K, few-row shapes run slower than with a workspace's K split).
+ *   is not split along K has every tile cut into the most row pieces (8, 4 or
+ *   2: 32, 64 or 128 rows) that fit one round of blocks, whole tiles when even
+ *   halves would not (long-K, few-row shapes run slower than with a
+ *   workspace's K split).
  */
 typedef enum { QL_MODE_AUTO = 0, QL_MODE_EXACT = 1, QL_MODE_FAST = 2, QL_MODE_SPLIT = 3 } ql_mode;
 
