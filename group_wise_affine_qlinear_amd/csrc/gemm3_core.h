@@ -525,8 +525,23 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
   constexpr int kHalf = kSteps / 2;
   // A fragments are read this many steps ahead of their use; the ring index
   // t % (kAhead + 1) continues across groups, whose reads ahead wrap into
-  // the next stage, which is complete only after the mid-group barrier
-  constexpr int kAhead = (kSteps % 4 == 0 && kHalf >= 3) ? 3 : 1;
+  // the next stage, which is complete only after the mid-group barrier.
+  // ONLINE on tiled codes reads one step ahead: its conversion registers
+  // pushed the loop past the register file, and the spills sat in the K
+  // loop; the shorter ring (8 fewer VGPRs) gave M = 4608, K = 4608,
+  // N = 13824 691 us against 850 and M = 4096, K = N = 4608 220 against 235
+  // (outputs bit-identical). On canonical codes the same change was slower
+  // (759 against 695 us, 256 against 249 us), as was FAST's (1-2 %).
+  constexpr int kAhead = (kSteps % 4 == 0 && kHalf >= 3 && !(ONLINE && !CANON)) ? 3 : 1;
+  // FAST on tiled codes builds each group's k-block 1 fragments during the
+  // group's own first half and the next group's k-block 0 fragments during
+  // its second half, so one fragment set is live instead of two (16 fewer
+  // VGPRs against one more code slot): 157.3 against 160.3 us at M = 4096,
+  // K = N = 4608 and 444.8 against 454.1 at K = 12288 (outputs
+  // bit-identical; ONLINE ran slower with it). Otherwise the next group's
+  // whole fragment set is built during the second half.
+  constexpr bool kHalfRefill = !ONLINE && !CANON;
+  constexpr int kRing = kHalfRefill ? S : S - 1;  // code slots
   static_assert(kSteps % (kAhead + 1) == 0, "A-fragment ring must divide the steps of a group");
   static_assert(kAhead <= kHalf, "reads of the next stage must follow the mid-group barrier");
   // the next group's B fragments are built in 4 * 2 * kNI pieces of one word
@@ -563,14 +578,16 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
   // group g.
   u32x4 bf[kNI][2];
   uint32_t xmx[IO::kMxRegs] = {};  // ONLINE: largest magnitudes of the rows this lane converts
-  uint32_t cq[S - 1][kNI][LC::kWords];
-  uint32_t sq[S - 1][kNI];   // tiled: s | b << 16
-  uint32_t bq[S - 1][kNI];   // unused
+  // code ring: group g+1 .. (and group g itself with half refills) at the
+  // start of group g; the last slot is requested in group g
+  uint32_t cq[kRing][kNI][LC::kWords];
+  uint32_t sq[kRing][kNI];   // tiled: s | b << 16
+  uint32_t bq[kRing][kNI];   // unused
   uint32_t sbc[kNI];         // canonical: s | b << 16 of the group being dequantized
   // piece i of the B fragments from cq[0] and its scale/bias: fragment (ni, c) = i / 4, word i % 4
-  auto dequant_piece = [&](u32x4 (&dst)[kNI][2], bool valid, int i) {
+  auto dequant_piece = [&](u32x4 (&dst)[kNI][2], int slot, bool valid, int i) {
     const int f = i >> 2, p = i & 3, ni = f >> 1, c = f & 1;
-    const uint32_t v = valid ? (CANON ? sbc[ni] : sq[0][ni]) : 0u;
+    const uint32_t v = valid ? (CANON ? sbc[ni] : sq[slot][ni]) : 0u;
     // scale and bias broadcast to both halves inside the packed multiply
     // (its operand select), no separate splat
     const h2 hv = __builtin_bit_cast(h2, v);
@@ -580,12 +597,14 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
       // the first piece of a column block (i = 8 ni) runs before its other
       // pieces: in both placements below pieces run in increasing i within a
       // column block
-      if (c == 0 && p == 0) cq[0][ni][1] = LC::prep(cq[0][ni][1], h);
+      if (c == 0 && p == 0) cq[slot][ni][1] = LC::prep(cq[slot][ni][1], h);
     }
-    uint32_t r = LC::pair(cq[0][ni], c, p, s2, b2);
+    uint32_t r = LC::pair(cq[slot][ni], c, p, s2, b2);
     asm volatile("" : "+v"(r));  // keeps the piece where it is placed, between MFMAs
     dst[ni][c][p] = r;
   };
+  // half refills: piece j of k-block c is word j % 4 of fragment (j / 4, c)
+  auto piece_of = [](int c, int j) { return ((2 * (j >> 2) + c) << 2) | (j & 3); };
 
   // One group on stage X. First half: MFMAs on the fragments in hand. Then
   // the barrier, after which the next stage XN is complete and the stage of
@@ -619,7 +638,7 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
         io.issue_x(XD, min(g + S - 1, g_end - 1));
         // ONLINE counts the code loads issued after the copies (see above)
         if constexpr (ONLINE) __builtin_amdgcn_sched_barrier(0);
-        io.load_codes(cq[S - 2], sq[S - 2], bq[S - 2], min(g + S - 1, g_end - 1));
+        io.load_codes(cq[kRing - 1], sq[kRing - 1], bq[kRing - 1], min(g + S - 1, g_end - 1));
         if constexpr (CANON) io.read_sb(min(g + 1, g_end - 1), sbc);
       }
       if (t + kAhead < kSteps) af[(t + kAhead) % (kAhead + 1)] = io.read_a(X, t + kAhead);
@@ -628,11 +647,31 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
       for (int ni = 0; ni < kNI; ++ni) {
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t % (kAhead + 1)], __builtin_bit_cast(h8, bf[ni][c]),
                                                              acc[mi][ni], 0, 0, 0);
-        if (t >= kHalf) {
+        if constexpr (!kHalfRefill) {
+          if (t >= kHalf) {
 #pragma unroll
-          for (int u = 0; u < kPerStep; ++u) {
-            const int i = (t - kHalf) * kPerStep + u;
-            if ((u % kNI) == ni && i < kPieces) dequant_piece(bn, g + 1 < g_end, i);
+            for (int u = 0; u < kPerStep; ++u) {
+              const int i = (t - kHalf) * kPerStep + u;
+              if ((u % kNI) == ni && i < kPieces) dequant_piece(bn, 0, g + 1 < g_end, i);
+            }
+          }
+        }
+      }
+      if constexpr (kHalfRefill) {
+        // first half: k-block 1 of group g (slot 0), while its k-block 0 is
+        // in use; second half: k-block 0 of group g+1 (slot 1)
+        const int tl = t % kHalf;
+        constexpr int kHP = kPieces / 2;
+        constexpr int kEvery = kHalf >= kHP ? kHalf / kHP : 1;
+        constexpr int kPer = kHalf >= kHP ? 1 : kHP / kHalf;
+        if (tl % kEvery == 0) {
+#pragma unroll
+          for (int u = 0; u < kPer; ++u) {
+            const int j = (tl / kEvery) * kPer + u;
+            if (j < kHP) {
+              if (t < kHalf) dequant_piece(bf, 0, g < g_end, piece_of(1, j));
+              else dequant_piece(bf, 1, g + 1 < g_end, piece_of(0, j));
+            }
           }
         }
       }
@@ -641,10 +680,12 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni) {
-      bf[ni][0] = bn[ni][0];
-      bf[ni][1] = bn[ni][1];
+      if constexpr (!kHalfRefill) {
+        bf[ni][0] = bn[ni][0];
+        bf[ni][1] = bn[ni][1];
+      }
 #pragma unroll
-      for (int j = 0; j + 1 < S - 1; ++j) {
+      for (int j = 0; j + 1 < kRing; ++j) {
         sq[j][ni] = sq[j + 1][ni];
         bq[j][ni] = bq[j + 1][ni];
 #pragma unroll
@@ -679,15 +720,21 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
   }
   if (g_begin < g_end) {
     if constexpr (CANON) io.read_sb(g_begin, sbc);
+    if constexpr (kHalfRefill) {
+      // k-block 0 of the first group; its k-block 1 is built in its first half
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) dequant_piece(bf, true, i);
-    io.load_codes(cq[0], sq[0], bq[0], min(g_begin + 1, g_end - 1));
+      for (int j = 0; j < kPieces / 2; ++j) dequant_piece(bf, 0, true, piece_of(0, j));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) dequant_piece(bf, 0, true, i);
+    }
+    io.load_codes(cq[kRing - 2], sq[kRing - 2], bq[kRing - 2], min(g_begin + 1, g_end - 1));
     // stages and codes up to g_begin + S - 2 are in flight now; each group g
     // requests g + S - 1
 #pragma unroll
     for (int j = 2; j < S - 1; ++j) {
       io.issue_x(xs[j], min(g_begin + j, g_end - 1));
-      io.load_codes(cq[j - 1], sq[j - 1], bq[j - 1], min(g_begin + j, g_end - 1));
+      io.load_codes(cq[kRing - S + j], sq[kRing - S + j], bq[kRing - S + j], min(g_begin + j, g_end - 1));
     }
 #pragma unroll
     for (int t = 0; t < kAhead; ++t) af[t] = io.read_a(xs[0], t);
