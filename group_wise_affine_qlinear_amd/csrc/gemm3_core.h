@@ -538,9 +538,10 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
   // its second half, so one fragment set is live instead of two (16 fewer
   // VGPRs against one more code slot): 157.3 against 160.3 us at M = 4096,
   // K = N = 4608 and 444.8 against 454.1 at K = 12288 (outputs
-  // bit-identical; ONLINE ran slower with it). Otherwise the next group's
-  // whole fragment set is built during the second half.
-  constexpr bool kHalfRefill = !ONLINE && !CANON;
+  // bit-identical). ONLINE ran slower with it, as did the other code widths
+  // (3-bit 40 %, 2-bit 2-3 %, 8-bit up to 1 %, 2048^2 sweep shapes): there
+  // the next group's whole fragment set is built during the second half.
+  constexpr bool kHalfRefill = !ONLINE && !CANON && BITS == 4;
   constexpr int kRing = kHalfRefill ? S : S - 1;  // code slots
   static_assert(kSteps % (kAhead + 1) == 0, "A-fragment ring must divide the steps of a group");
   static_assert(kAhead <= kHalf, "reads of the next stage must follow the mid-group barrier");
