@@ -640,7 +640,16 @@ __device__ __forceinline__ bool tile_accumulate3(const Gemm3Args &a, unsigned ch
         // ONLINE counts the code loads issued after the copies (see above)
         if constexpr (ONLINE) __builtin_amdgcn_sched_barrier(0);
         io.load_codes(cq[kRing - 1], sq[kRing - 1], bq[kRing - 1], min(g + S - 1, g_end - 1));
-        if constexpr (CANON) io.read_sb(min(g + 1, g_end - 1), sbc);
+      }
+      // canonical: the next group's scale|bias words come from LDS early in
+      // the first half, so their latency is spent under MFMAs rather than
+      // in front of the first dequant piece after the barrier (the staged
+      // chunk was published more than six groups before; its buffer is
+      // refilled two barriers after this read at the earliest). 208 -> 194 us FAST and
+      // 245 -> 228 us ONLINE at M = 4096, K = N = 4608; 570 -> 546 and
+      // 673 -> 645 us at M = 4608, K = 4608, N = 13824 (outputs bit-identical).
+      if constexpr (CANON && !kHalfRefill) {
+        if (t == 1) io.read_sb(min(g + 1, g_end - 1), sbc);
       }
       if (t + kAhead < kSteps) af[(t + kAhead) % (kAhead + 1)] = io.read_a(X, t + kAhead);
       else af[(t + kAhead) % (kAhead + 1)] = io.read_a(XN, t + kAhead - kSteps);
